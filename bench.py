@@ -1,0 +1,223 @@
+#!/usr/bin/env python
+"""Benchmark of the PCD hot path on one MI355X.
+
+One step = one whole request through the C ABI: pcd_prefill of the shared
+prefix, then pcd_decide of every field in one batched branch pass + readout.
+Default workload: the Qwen2.5-1.5B-shaped random-init bf16 decoder, a
+512-token prefix and a 28-field schema (10 booleans, 18 four-way enums).
+Prints one JSON line: fields decided per second and p50 request latency,
+the roofline position of the dominant kernel (timed live with hipEvents on
+the library's stream) and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+
+
+def algorithmic_work(sh, P, Tb, R):
+    """Per-launch algorithmic (flops, bytes) of each kernel class: every
+    operand read once and every output written once."""
+    d, F, V, hd = sh.d_model, sh.ffn_dim, sh.vocab_size, sh.head_dim
+    nq, nk = sh.n_heads * hd, sh.n_kv_heads * hd
+    e = 2 if sh.dtype == "bf16" else 4
+    kv_tok = 2 * nk * e  # K and V of one token in one layer
+
+    def gemm(M, N, K, out_b):
+        return 2.0 * M * N * K, float(N * K * e + M * K * e + M * N * out_b)
+
+    w = {}
+    w["prefill_qkv"] = gemm(P, nq + 2 * nk, d, e)
+    w["prefill_o"] = gemm(P, d, nq, 4)
+    w["prefill_gateup"] = gemm(P, 2 * F, d, 0)
+    w["prefill_gateup"] = (w["prefill_gateup"][0], w["prefill_gateup"][1] + P * F * e)
+    w["prefill_down"] = gemm(P, d, F, 4)
+    w["prefill_attn"] = (4.0 * sh.n_heads * hd * P * (P + 1) / 2, float(2 * P * nq * e + P * kv_tok))
+    w["branch_qkv"] = gemm(Tb, nq + 2 * nk, d, e)
+    w["branch_o"] = gemm(Tb, d, nq, 4)
+    w["branch_gateup"] = gemm(Tb, 2 * F, d, 0)
+    w["branch_gateup"] = (w["branch_gateup"][0], w["branch_gateup"][1] + Tb * F * e)
+    w["branch_down"] = gemm(Tb, d, F, 4)
+    # prefix part of the shared-prefix attention: the prefix K/V of a layer read once
+    w["branch_attn"] = (4.0 * sh.n_heads * hd * Tb * P, float(P * kv_tok + Tb * nq * e))
+    w["readout_lmhead"] = gemm(R, V, d, 0)
+    return w
+
+
+BOUND = {"prefill_qkv": "mfma", "prefill_o": "mfma", "prefill_gateup": "mfma", "prefill_down": "mfma",
+         "prefill_attn": "mfma", "branch_qkv": "hbm", "branch_o": "hbm", "branch_gateup": "hbm",
+         "branch_down": "hbm", "branch_attn": "hbm", "readout_lmhead": "hbm"}
+
+
+def roofline_entry(cls, total_ms, launches, work, peak_mfma):
+    flops, nbytes = work[cls]
+    avg_s = total_ms / launches / 1e3
+    if BOUND[cls] == "mfma":
+        a = flops / avg_s / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": round(a / peak_mfma, 4), "traffic": None, "kernel": cls,
+                "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
+                "per_launch": {"flops": flops, "bytes": nbytes}}
+    a = nbytes / avg_s / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": cls,
+            "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
+            "per_launch": {"flops": flops, "bytes": nbytes}}
+
+
+def cpu_baseline(weights, wl, budget_layers):
+    """The fp32 oracle, as it stands, on the first `budget_layers` layers of
+    the same request, with the per-layer part scaled to the full depth."""
+    import numpy as np
+    from oracle import decoder as odec
+    from oracle import pcd as opcd
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    req = wl.requests[0]
+    dec = odec.Decoder(weights, np.float32)
+    k = budget_layers
+    # cast the sampled layers and the head once, outside the timed part
+    for l in range(k):
+        for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+            dec.mat(f"l{l}.{n}")
+    dec.mat(weights.lm_head_name())
+    dec.mat("embed")
+    t0 = time.perf_counter()
+    kv = opcd.prefill(dec, req.prefix, n_layers=k)
+    t1 = time.perf_counter()
+    plan = opcd.build_plan([(len(req.prefix), req.fields)], wl.shape.vocab_size)
+    x = opcd.branch(dec, plan, [kv], n_layers=k)
+    t2 = time.perf_counter()
+    lse, z = opcd.readout(dec, plan, x)
+    opcd.combine(plan, lse, z)
+    t3 = time.perf_counter()
+    L = wl.shape.n_layers
+    est = (t1 - t0) * L / k + (t2 - t1) * L / k + (t3 - t2)
+    nf = len(req.fields)
+    return {"value": round(nf / est, 3), "unit": "fields/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp32 NumPy oracle on the bench request (P={len(req.prefix)}, {nf} fields) through the "
+                       f"first {k} of {L} layers plus the full readout; prefill and branch time scaled by {L}/{k}; "
+                       f"measured {t3 - t0:.1f} s, estimated full request {est:.1f} s"),
+            "est_request_s": round(est, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg1", help="cfg0 (tiny) or cfg1 (1.5B, 512-token prefix, 28 fields)")
+    ap.add_argument("--cpu-layers", type=int, default=2, help="layers of the CPU-oracle sample (0: skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the path is single-GPU by design (requests are independent and "
+              "would shard over GPUs with no communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import constrained_decoding_pcd_amd as cpd
+    import pcd_inputs as pi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = pi.make_workload(args.workload)
+    sh = wl.shape
+    req = wl.requests[0]
+    t = time.time()
+    weights = pi.make_weights(sh, wl.weight_seed)
+    print(f"# weights drawn in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
+    dev = cpd.upload_weights(weights.mats, sh.n_layers, sh.d_model, "cuda:0")
+    lim = cpd.limits_for(sh.vocab_size, sh.max_seq, [len(req.prefix)], [req.fields])
+    model = cpd.PcdModel(cpd.config_of(sh), dev, lim)
+    kv = torch.empty(model.state_bytes(len(req.prefix)), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        st = model.prefill(req.prefix, kv)
+        out = model.decide(st, req.fields)
+        st.close()
+        return out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lat = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s0 = time.perf_counter()
+        out = step()
+        lat.append(time.perf_counter() - s0)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ms_per_step = total / args.steps * 1e3
+    p50 = float(np.percentile(np.array(lat) * 1e3, 50))
+    p90 = float(np.percentile(np.array(lat) * 1e3, 90))
+    nf = len(req.fields)
+    print(f"# {args.steps} steps: {ms_per_step:.3f} ms/step, p50 {p50:.3f} ms, p90 {p90:.3f} ms",
+          file=sys.stderr, flush=True)
+    stats = model.stats()
+
+    # the same steps again with every kernel launch bracketed by hipEvents on the library's stream
+    model.set_kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = model.kernel_times()
+    model.set_kernel_timing(False)
+    plan = cpd.debug_plan(sh.vocab_size, sh.max_seq, [len(req.prefix)], [req.fields])
+    Tb, R = len(plan["tok"]), len(plan["ro_tok"])
+    work = algorithmic_work(sh, len(req.prefix), Tb, R)
+    peak_mfma = BF16_PEAK_TFLOPS if sh.dtype == "bf16" else FP32_PEAK_TFLOPS
+    kernels = {c: roofline_entry(c, ms, n, work, peak_mfma) for c, (ms, n) in kt.items() if n > 0 and c in work}
+    dominant = max(kernels, key=lambda c: kt[c][0])
+    timed_ms_per_step = sum(ms for ms, _ in kt.values()) / args.steps
+    res = {
+        "metric": "schema fields decided/sec + p50 28-field request ms, 1.5B-shaped bf16",
+        "value": round(nf / (ms_per_step / 1e3), 2),
+        "unit": "fields/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "p50_request_ms": round(p50, 4),
+        "p90_request_ms": round(p90, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sh.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {sh.name} random-init {sh.dtype}, {len(req.prefix)}-token "
+                               f"prefix, {nf} fields, {Tb} branch tokens, {R} readouts, batch 1",
+                   "layers": sh.n_layers, "prefix_tokens": len(req.prefix), "fields": nf,
+                   "branch_tokens": Tb, "readouts": R},
+        "phases_ms": {"prefill": round(stats["last_prefill_ms"], 4), "branch": round(stats["last_branch_ms"], 4),
+                      "readout": round(stats["last_readout_ms"], 4)},
+        "passes": {"prefill": 1, "branch": 1,
+                   "token_by_token_equivalent": int(sum(len(f.scaffold) + len(f.candidates[int(a)])
+                                                        for f, a in zip(req.fields, out["argmax"])))},
+        "roofline": kernels[dominant],
+        "kernels": {c: {k: v for k, v in e.items() if k in ("achieved", "unit", "frac", "avg_launch_us",
+                                                            "launches", "bound")} for c, e in kernels.items()},
+        "kernel_timed_ms_per_step": round(timed_ms_per_step, 4),
+    }
+    if args.cpu_layers > 0:
+        print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(weights, wl, min(args.cpu_layers, sh.n_layers))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

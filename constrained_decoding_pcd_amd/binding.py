@@ -1,0 +1,363 @@
+"""ctypes binding of libpcd.so (argument marshalling only).
+
+Every step of the decoding path runs in the library's HIP kernels; this module
+only converts Python/NumPy arguments to the C structs of include/pcd.h and
+hands torch-allocated device memory and torch's current HIP stream to the
+library.  It fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpcd.so")
+
+PCD_OK = 0
+ERROR_NAMES = {-1: "ARG", -2: "TOKEN", -3: "NCAND", -4: "EMPTY", -5: "DUP", -6: "PREFIX", -7: "CAP",
+               -8: "STATE", -9: "DEVICE", -10: "NOMEM"}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_decide",
+           "pcd_decide_many", "pcd_debug_plan", "pcd_get_stats", "pcd_free_state", "pcd_free_model",
+           "pcd_last_error", "pcd_set_kernel_timing", "pcd_get_kernel_times")
+
+KERNEL_CLASSES = ("prefill_qkv", "prefill_attn", "prefill_o", "prefill_gateup", "prefill_down", "branch_qkv",
+                  "branch_attn", "branch_tail", "branch_o", "branch_gateup", "branch_down", "readout_lmhead",
+                  "other")
+
+
+class PcdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        self.code = code
+        self.name = ERROR_NAMES.get(code, str(code))
+        super().__init__(f"PCD_E_{self.name}: {msg}")
+
+
+class pcd_config(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_heads", c_int32), ("n_kv_heads", c_int32),
+                ("head_dim", c_int32), ("ffn_dim", c_int32), ("vocab_size", c_int32), ("max_seq", c_int32),
+                ("rope_theta", c_float), ("rms_eps", c_float), ("tied_lm_head", c_int32), ("dtype", c_int32)]
+
+
+class pcd_weights(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("lm_head", c_void_p), ("final_norm", c_void_p),
+                ("attn_norm", POINTER(c_void_p)), ("mlp_norm", POINTER(c_void_p)),
+                ("wq", POINTER(c_void_p)), ("wk", POINTER(c_void_p)), ("wv", POINTER(c_void_p)),
+                ("wo", POINTER(c_void_p)), ("w_gate", POINTER(c_void_p)), ("w_up", POINTER(c_void_p)),
+                ("w_down", POINTER(c_void_p))]
+
+
+class pcd_limits(ctypes.Structure):
+    _fields_ = [("max_prefill_tokens", c_int32), ("max_branch_tokens", c_int32), ("max_readouts", c_int32),
+                ("max_gathers", c_int32), ("max_fields", c_int32), ("max_candidates", c_int32),
+                ("max_requests", c_int32)]
+
+
+class pcd_candidate(ctypes.Structure):
+    _fields_ = [("tokens", POINTER(c_int32)), ("n_tokens", c_int32)]
+
+
+class pcd_field(ctypes.Structure):
+    _fields_ = [("scaffold", POINTER(c_int32)), ("n_scaffold", c_int32), ("cand_offset", c_int32),
+                ("n_cands", c_int32)]
+
+
+class pcd_request(ctypes.Structure):
+    _fields_ = [("fields", POINTER(pcd_field)), ("n_fields", c_int32), ("candidates", POINTER(pcd_candidate)),
+                ("n_candidates", c_int32)]
+
+
+class pcd_outputs(ctypes.Structure):
+    _fields_ = [("cand_prob", POINTER(c_float)), ("cand_logscore", POINTER(c_float)),
+                ("field_mass", POINTER(c_float)), ("field_margin", POINTER(c_float)),
+                ("field_argmax", POINTER(c_int32)), ("readout_lse", POINTER(c_float)),
+                ("gather_logit", POINTER(c_float))]
+
+
+class pcd_stats(ctypes.Structure):
+    _fields_ = [("prefill_passes", c_int64), ("branch_passes", c_int64), ("last_branch_tokens", c_int32),
+                ("last_readouts", c_int32), ("last_gathers", c_int32), ("last_requests", c_int32),
+                ("last_prefill_ms", c_float), ("last_branch_ms", c_float), ("last_readout_ms", c_float),
+                ("workspace_bytes", c_int64)]
+
+
+_PLAN_ARRAYS = ("tok", "pos", "req", "field", "anc_off", "anc", "ro_tok", "ro_field", "g_off", "g_tok",
+                "f_ro_root", "f_cand_off", "c_path_off", "c_path")
+
+
+class pcd_plan_info(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("n_branch", "n_readouts", "n_gathers", "n_fields", "n_candidates",
+                                        "n_paths", "n_anc")] + [(n, POINTER(c_int32)) for n in _PLAN_ARRAYS]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads the in-tree libpcd.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    P = POINTER
+    sig = {
+        "pcd_workspace_bytes": (c_size_t, [P(pcd_config), P(pcd_limits)]),
+        "pcd_load_weights": (c_int32, [P(pcd_config), P(pcd_limits), P(pcd_weights), c_void_p, c_size_t, c_void_p,
+                                       P(c_void_p)]),
+        "pcd_state_bytes": (c_size_t, [c_void_p, c_int32]),
+        "pcd_prefill": (c_int32, [c_void_p, P(c_int32), c_int32, c_void_p, c_size_t, c_void_p, P(c_void_p)]),
+        "pcd_decide": (c_int32, [c_void_p, P(pcd_field), c_int32, P(pcd_candidate), c_int32, c_float,
+                                 P(pcd_outputs), c_void_p]),
+        "pcd_decide_many": (c_int32, [P(c_void_p), P(pcd_request), c_int32, c_float, P(pcd_outputs), c_void_p]),
+        "pcd_debug_plan": (c_int32, [c_int32, c_int32, c_int32, P(c_int32), P(pcd_request), P(pcd_plan_info)]),
+        "pcd_get_stats": (c_int32, [c_void_p, P(pcd_stats)]),
+        "pcd_free_state": (None, [c_void_p]),
+        "pcd_free_model": (None, [c_void_p]),
+        "pcd_last_error": (ctypes.c_char_p, []),
+        "pcd_set_kernel_timing": (c_int32, [c_void_p, c_int32]),
+        "pcd_get_kernel_times": (c_int32, [c_void_p, P(c_float), P(c_int64)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != PCD_OK:
+        raise PcdError(rc, load_library().pcd_last_error().decode(errors="replace"))
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(POINTER(c_int32))
+
+
+def _f32p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(POINTER(c_float))
+
+
+class _Marshalled:
+    """C view of requests: lists of fields, each with .scaffold and
+    .candidates (token-id sequences).  Keeps the NumPy buffers alive."""
+
+    def __init__(self, requests: Sequence[Sequence]):
+        self.keep = []
+        self.reqs = (pcd_request * len(requests))()
+        self.n_cands, self.n_fields = [], []
+        for r, fields in enumerate(requests):
+            cands = [c for f in fields for c in f.candidates]
+            ca = (pcd_candidate * max(1, len(cands)))()
+            fa = (pcd_field * max(1, len(fields)))()
+            off = 0
+            for i, c in enumerate(cands):
+                a = np.ascontiguousarray(c, dtype=np.int32)
+                self.keep.append(a)
+                ca[i].tokens = _i32p(a)
+                ca[i].n_tokens = a.size
+            for i, f in enumerate(fields):
+                s = np.ascontiguousarray(f.scaffold, dtype=np.int32)
+                self.keep.append(s)
+                fa[i].scaffold = _i32p(s)
+                fa[i].n_scaffold = s.size
+                fa[i].cand_offset = off
+                fa[i].n_cands = len(f.candidates)
+                off += len(f.candidates)
+            self.keep += [ca, fa]
+            self.reqs[r].fields = fa
+            self.reqs[r].n_fields = len(fields)
+            self.reqs[r].candidates = ca
+            self.reqs[r].n_candidates = len(cands)
+            self.n_cands.append(len(cands))
+            self.n_fields.append(len(fields))
+
+
+def debug_plan(vocab_size: int, max_seq: int, prefix_lens: Sequence[int], requests) -> Dict[str, np.ndarray]:
+    """The library's plan for these requests (host only, no device work)."""
+    lib = load_library()
+    mr = _Marshalled(requests)
+    lens = np.ascontiguousarray(prefix_lens, dtype=np.int32)
+    info = pcd_plan_info()
+    _check(lib.pcd_debug_plan(vocab_size, max_seq, len(requests), _i32p(lens), mr.reqs, ctypes.byref(info)))
+    sizes = {"tok": info.n_branch, "pos": info.n_branch, "req": info.n_branch, "field": info.n_branch,
+             "anc_off": info.n_branch + 1, "anc": info.n_anc, "ro_tok": info.n_readouts,
+             "ro_field": info.n_readouts, "g_off": info.n_readouts + 1, "g_tok": info.n_gathers,
+             "f_ro_root": info.n_fields, "f_cand_off": info.n_fields + 1, "c_path_off": info.n_candidates + 1,
+             "c_path": info.n_paths}
+    out = {k: np.zeros(max(1, n), np.int32) for k, n in sizes.items()}
+    for k in _PLAN_ARRAYS:
+        setattr(info, k, _i32p(out[k]))
+    _check(lib.pcd_debug_plan(vocab_size, max_seq, len(requests), _i32p(lens), mr.reqs, ctypes.byref(info)))
+    return {k: out[k][:sizes[k]] for k in _PLAN_ARRAYS}
+
+
+def config_of(shape, max_seq: Optional[int] = None) -> dict:
+    """pcd_config fields of a model-shape record (attributes named as in
+    pcd_config; `tied` and `dtype` in "f32"/"bf16" form)."""
+    return dict(n_layers=shape.n_layers, d_model=shape.d_model, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
+                head_dim=shape.head_dim, ffn_dim=shape.ffn_dim, vocab_size=shape.vocab_size,
+                max_seq=max_seq or shape.max_seq, rope_theta=shape.rope_theta, rms_eps=shape.rms_eps,
+                tied_lm_head=int(shape.tied), dtype=DTYPE_F32 if shape.dtype == "f32" else DTYPE_BF16)
+
+
+def limits_for(vocab_size: int, max_seq: int, prefix_lens: Sequence[int], requests, max_prefill: int = 0) -> dict:
+    """pcd_limits that fit exactly these requests (counts from the plan)."""
+    p = debug_plan(vocab_size, max_seq, prefix_lens, requests)
+    return dict(max_prefill_tokens=max(max_prefill, max(prefix_lens)), max_branch_tokens=len(p["tok"]),
+                max_readouts=len(p["ro_tok"]), max_gathers=len(p["g_tok"]), max_fields=len(p["f_ro_root"]),
+                max_candidates=len(p["c_path_off"]) - 1, max_requests=len(prefix_lens))
+
+
+def _stream_handle(torch):
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def upload_weights(mats: Dict[str, np.ndarray], n_layers: int, d_model: int, device="cuda:0"):
+    """Copies host weight arrays (float32, or uint16 bf16 patterns) to the
+    device and adds all-ones fp32 norm weights.  Returns name -> tensor."""
+    import torch
+    out = {}
+    for k, a in mats.items():
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        out[k] = t.to(device)
+    ones = torch.ones(d_model, dtype=torch.float32, device=device)
+    out["final_norm"] = ones
+    for l in range(n_layers):
+        out[f"l{l}.attn_norm"] = ones
+        out[f"l{l}.mlp_norm"] = ones
+    return out
+
+
+class PcdState:
+    def __init__(self, model: "PcdModel", handle: c_void_p, kv, n_tokens: int):
+        self.model, self.handle, self.kv, self.n_tokens = model, handle, kv, n_tokens
+
+    def close(self):
+        if self.handle:
+            load_library().pcd_free_state(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class PcdModel:
+    """A model over device weights (torch tensors) and a torch-allocated
+    workspace.  `config` holds the pcd_config fields, `limits` the
+    pcd_limits fields."""
+
+    def __init__(self, config: dict, weights: Dict[str, "object"], limits: dict):
+        import torch
+        self.torch = torch
+        self.lib = load_library()
+        self.cfg = pcd_config(**config)
+        self.lim = pcd_limits(**limits)
+        L = self.cfg.n_layers
+        self.weights = weights
+        arr = lambda name: (c_void_p * L)(*[weights[f"l{l}.{name}"].data_ptr() for l in range(L)])
+        self._arrays = {n: arr(n) for n in ("attn_norm", "mlp_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up",
+                                             "w_down")}
+        w = pcd_weights()
+        w.embed = weights["embed"].data_ptr()
+        w.lm_head = weights["lm_head"].data_ptr() if "lm_head" in weights else None
+        w.final_norm = weights["final_norm"].data_ptr()
+        for n, a in self._arrays.items():
+            setattr(w, n, a)
+        nbytes = self.lib.pcd_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(self.lim))
+        if nbytes == 0:
+            raise PcdError(-1, self.lib.pcd_last_error().decode())
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=weights["embed"].device)
+        h = c_void_p()
+        _check(self.lib.pcd_load_weights(ctypes.byref(self.cfg), ctypes.byref(self.lim), ctypes.byref(w),
+                                         c_void_p(self.workspace.data_ptr()), nbytes, _stream_handle(torch),
+                                         ctypes.byref(h)))
+        self.handle = h
+
+    def state_bytes(self, n_tokens: int) -> int:
+        return self.lib.pcd_state_bytes(self.handle, n_tokens)
+
+    def prefill(self, tokens: Sequence[int], kv=None) -> PcdState:
+        torch = self.torch
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        nb = self.state_bytes(t.size)
+        if kv is None:
+            kv = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.workspace.device)
+        h = c_void_p()
+        _check(self.lib.pcd_prefill(self.handle, _i32p(t), t.size, c_void_p(kv.data_ptr()), kv.numel(),
+                                    _stream_handle(torch), ctypes.byref(h)))
+        return PcdState(self, h, kv, t.size)
+
+    def decide(self, state: PcdState, fields, temperature: float = 1.0, debug: bool = False) -> dict:
+        return self.decide_many([state], [fields], temperature, debug)[0]
+
+    def decide_many(self, states: Sequence[PcdState], requests, temperature: float = 1.0,
+                    debug: bool = False) -> List[dict]:
+        mr = _Marshalled(requests)
+        counts = None
+        if debug:
+            plan = debug_plan(self.cfg.vocab_size, self.cfg.max_seq, [s.n_tokens for s in states], requests)
+            counts = []
+            ro_req = plan["req"][plan["ro_tok"]]
+            g_req = np.repeat(ro_req, np.diff(plan["g_off"]))
+            for r in range(len(states)):
+                counts.append((int((ro_req == r).sum()), int((g_req == r).sum())))
+        outs = (pcd_outputs * len(states))()
+        res = []
+        for r in range(len(states)):
+            d = {"prob": np.zeros(mr.n_cands[r], np.float32), "logscore": np.zeros(mr.n_cands[r], np.float32),
+                 "mass": np.zeros(mr.n_fields[r], np.float32), "margin": np.zeros(mr.n_fields[r], np.float32),
+                 "argmax": np.zeros(mr.n_fields[r], np.int32)}
+            o = outs[r]
+            o.cand_prob, o.cand_logscore = _f32p(d["prob"]), _f32p(d["logscore"])
+            o.field_mass, o.field_margin = _f32p(d["mass"]), _f32p(d["margin"])
+            o.field_argmax = _i32p(d["argmax"])
+            if debug:
+                d["lse"] = np.zeros(max(1, counts[r][0]), np.float32)
+                d["z"] = np.zeros(max(1, counts[r][1]), np.float32)
+                o.readout_lse, o.gather_logit = _f32p(d["lse"]), _f32p(d["z"])
+            res.append(d)
+        hs = (c_void_p * len(states))(*[s.handle for s in states])
+        _check(self.lib.pcd_decide_many(hs, mr.reqs, len(states), temperature, outs, _stream_handle(self.torch)))
+        for r, d in enumerate(res):
+            if debug:
+                d["lse"] = d["lse"][:counts[r][0]]
+                d["z"] = d["z"][:counts[r][1]]
+        return res
+
+    def stats(self) -> dict:
+        s = pcd_stats()
+        _check(self.lib.pcd_get_stats(self.handle, ctypes.byref(s)))
+        return {k: getattr(s, k) for k, _ in pcd_stats._fields_}
+
+    def set_kernel_timing(self, enable: bool):
+        _check(self.lib.pcd_set_kernel_timing(self.handle, int(bool(enable))))
+
+    def kernel_times(self) -> Dict[str, tuple]:
+        """class -> (total ms, launches) since timing was enabled."""
+        n = len(KERNEL_CLASSES)
+        ms = (c_float * n)()
+        cnt = (c_int64 * n)()
+        _check(self.lib.pcd_get_kernel_times(self.handle, ms, cnt))
+        return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_CLASSES)}
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.pcd_free_model(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

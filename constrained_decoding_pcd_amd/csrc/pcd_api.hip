@@ -1,0 +1,778 @@
+// C ABI of the PCD library: validation, workspace layout, plan upload and the
+// launch sequences of prefill and of the batched branch pass + readout.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pcd.h"
+#include "pcd_kernels.h"
+#include "pcd_plan.h"
+
+using namespace pcd;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg) {
+    g_err = msg;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                        \
+    do {                                                                                     \
+        hipError_t e_ = (expr);                                                              \
+        if (e_ != hipSuccess) return fail(PCD_E_DEVICE, std::string(#expr ": ") + hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr int MAX_SPLITS = 8;         // prefix splits of the branch attention
+constexpr int ATT_ROWS = 64;          // query rows per attention workgroup
+constexpr int SPLITK_MAX = 8;
+constexpr int SPLITK_ROWS = 1024;     // split-K is only used below this many rows
+constexpr uint64_t STATE_MAGIC = 0x70636473746174ull;
+
+size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+struct Layout {
+    size_t rope, x, h, q, ao, act, splitk, kvb, part_o, part_ml, hr, ro_part, lse, z, outs, plan;
+    size_t plan_bytes, outs_bytes, total;
+};
+
+int64_t plan_block_cap(const pcd_config &c, const pcd_limits &l) {
+    const int grp = c.n_heads / c.n_kv_heads;
+    const int64_t pre = (int64_t)c.n_kv_heads * (((int64_t)l.max_prefill_tokens * grp + ATT_ROWS - 1) / ATT_ROWS);
+    const int64_t br = (int64_t)c.n_kv_heads *
+                       (((int64_t)l.max_branch_tokens * grp + ATT_ROWS - 1) / ATT_ROWS + l.max_requests) * MAX_SPLITS;
+    return std::max(pre, br);
+}
+
+int64_t path_cap(const pcd_limits &l) { return 8 * (int64_t)l.max_candidates + l.max_gathers; }
+
+Layout layout(const pcd_config &c, const pcd_limits &l) {
+    Layout L{};
+    const size_t esz = c.dtype == PCD_DTYPE_F32 ? 4 : 2;
+    const size_t rows = (size_t)std::max(l.max_prefill_tokens, l.max_branch_tokens);
+    const size_t d = c.d_model, hq = (size_t)c.n_heads * c.head_dim;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L.rope = take((size_t)c.max_seq * (c.head_dim / 2) * sizeof(float2));
+    L.x = take(rows * d * 4);
+    L.h = take(rows * d * esz);
+    L.q = take(rows * hq * esz);
+    L.ao = take(rows * hq * esz);
+    L.act = take(rows * c.ffn_dim * esz);
+    L.splitk = take((size_t)SPLITK_MAX * std::min(rows, (size_t)SPLITK_ROWS) * d * 4);
+    L.kvb = take((size_t)c.n_layers * 2 * c.n_kv_heads * l.max_branch_tokens * c.head_dim * esz);
+    L.part_o = take((size_t)MAX_SPLITS * l.max_branch_tokens * hq * 4);
+    L.part_ml = take((size_t)MAX_SPLITS * l.max_branch_tokens * c.n_heads * sizeof(float2));
+    L.hr = take((size_t)l.max_readouts * d * esz);
+    L.ro_part = take((size_t)(c.vocab_size / 128) * l.max_readouts * sizeof(float2));
+    L.lse = take((size_t)l.max_readouts * 4);
+    L.z = take((size_t)l.max_gathers * 4);
+    L.outs_bytes = align_up((size_t)(2 * l.max_candidates + 3 * l.max_fields + l.max_readouts + l.max_gathers) * 4 + 8 * 256);
+    L.outs = take(L.outs_bytes);
+    const int64_t ints = 6 * (int64_t)rows + 2 * (int64_t)l.max_readouts + 2 + 2 * (int64_t)l.max_gathers +
+                         2 * (int64_t)l.max_fields + 1 + (int64_t)l.max_candidates + 1 + path_cap(l) +
+                         2 * (int64_t)l.max_requests;
+    L.plan_bytes = align_up((size_t)ints * 4 + 20 * 256) + align_up((size_t)l.max_requests * 8) +
+                   align_up((size_t)plan_block_cap(c, l) * sizeof(AttnBlock));
+    L.plan = take(L.plan_bytes);
+    L.total = off;
+    return L;
+}
+
+int check_config(const pcd_config *c, const pcd_limits *l) {
+    if (!c || !l) return fail(PCD_E_ARG, "null config or limits");
+    if (c->dtype != PCD_DTYPE_F32 && c->dtype != PCD_DTYPE_BF16) return fail(PCD_E_ARG, "dtype must be f32 or bf16");
+    if (c->n_layers <= 0 || c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+        c->ffn_dim <= 0 || c->vocab_size <= 0 || c->max_seq <= 0)
+        return fail(PCD_E_ARG, "non-positive model dimension");
+    if (c->n_heads % c->n_kv_heads) return fail(PCD_E_ARG, "n_heads must be a multiple of n_kv_heads");
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return fail(PCD_E_ARG, "head_dim must be 32, 64 or 128");
+    if (c->dtype == PCD_DTYPE_F32 && c->head_dim == 128) return fail(PCD_E_ARG, "f32 models support head_dim 32 or 64");
+    const int kt = gemm_k_tile(c->dtype);
+    if (c->d_model % 128 || c->ffn_dim % 128 || (c->n_heads * c->head_dim) % 128 || c->vocab_size % 128 ||
+        c->d_model % kt || c->ffn_dim % kt)
+        return fail(PCD_E_ARG, "d_model, ffn_dim, n_heads*head_dim and vocab_size must be multiples of 128");
+    if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(PCD_E_ARG, "rms_eps and rope_theta must be positive");
+    if (l->max_prefill_tokens <= 0 || l->max_branch_tokens <= 0 || l->max_readouts <= 0 || l->max_gathers <= 0 ||
+        l->max_fields <= 0 || l->max_candidates <= 0 || l->max_requests <= 0)
+        return fail(PCD_E_ARG, "limits must be positive");
+    if (l->max_prefill_tokens > c->max_seq) return fail(PCD_E_ARG, "max_prefill_tokens exceeds max_seq");
+    return PCD_OK;
+}
+
+}  // namespace
+
+struct pcd_model {
+    pcd_config cfg;
+    pcd_limits lim;
+    Layout L;
+    char *ws = nullptr;
+    size_t ws_bytes = 0;
+    const void *embed = nullptr, *head = nullptr;
+    const float *final_norm = nullptr;
+    std::vector<const void *> wq, wk, wv, wo, wg, wu, wd;
+    std::vector<const float *> an, mn;
+    char *plan_host = nullptr;  // pinned staging for the plan upload
+    char *outs_host = nullptr;  // pinned staging for the results
+    hipEvent_t ev[5] = {};
+    pcd_stats stats{};
+    int n_states = 0;
+    // per-kernel-class timing
+    bool timing = false;
+    std::vector<hipEvent_t> tev;         // pool, used in (start, end) pairs
+    std::vector<int> tcls;               // class of each used pair
+    size_t tused = 0;
+    float kc_ms[PCD_KC_COUNT] = {};
+    int64_t kc_n[PCD_KC_COUNT] = {};
+    void tbegin(int cls, hipStream_t st) {
+        if (!timing) return;
+        if (2 * tused + 2 > tev.size()) {
+            for (int i = 0; i < 256; ++i) {
+                hipEvent_t e;
+                if (hipEventCreate(&e) != hipSuccess) return;
+                tev.push_back(e);
+            }
+        }
+        (void)hipEventRecord(tev[2 * tused], st);
+        if (tcls.size() <= tused) tcls.resize(tused + 1);
+        tcls[tused] = cls;
+    }
+    void tend(hipStream_t st) {
+        if (!timing || 2 * tused + 2 > tev.size()) return;
+        (void)hipEventRecord(tev[2 * tused + 1], st);
+        ++tused;
+    }
+    // after the stream has drained
+    void tcollect() {
+        for (size_t i = 0; i < tused; ++i) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, tev[2 * i], tev[2 * i + 1]) == hipSuccess) {
+                kc_ms[tcls[i]] += ms;
+                kc_n[tcls[i]] += 1;
+            }
+        }
+        tused = 0;
+    }
+};
+
+struct pcd_state {
+    uint64_t magic;
+    pcd_model *m;
+    void *kv;
+    int32_t P;
+};
+
+namespace {
+
+size_t esize(const pcd_model *m) { return m->cfg.dtype == PCD_DTYPE_F32 ? 4 : 2; }
+
+// choose split-K for a GEMM whose epilogue adds into the residual stream
+int splitk_for(const pcd_model *m, int M, int N, int K) {
+    const int kt = gemm_k_tile(m->cfg.dtype);
+    const int tiles = (M + 63) / 64 * (N / 64);
+    if (tiles >= 192 || M > SPLITK_ROWS) return 1;
+    int best = 1;
+    for (int s = 2; s <= SPLITK_MAX; ++s) {
+        if (K % (s * kt) || K / s < 2 * kt) continue;
+        best = s;
+        if (tiles * s >= 256) break;
+    }
+    return best;
+}
+
+bool big_tile(int M, int N) { return ((M + 127) / 128) * (N / 128) >= 256; }
+
+// O projection or down projection into the residual stream
+bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W, hipStream_t st) {
+    GemmCall c{};
+    c.dt = m->cfg.dtype;
+    c.A = A;
+    c.M = M;
+    c.N = N;
+    c.K = K;
+    c.B[0].ptr[0] = W;
+    c.B[0].nseg = 1;
+    float *x = reinterpret_cast<float *>(m->ws + m->L.x);
+    const int s = splitk_for(m, M, N, K);
+    if (s > 1) {
+        c.epi = Epi::Partial;
+        c.splits = s;
+        c.part = reinterpret_cast<float *>(m->ws + m->L.splitk);
+        if (!gemm(c, st)) return false;
+        splitk_reduce(c.part, s, M, N, x, st);
+        return true;
+    }
+    c.epi = Epi::Resid;
+    c.splits = 1;
+    c.x = x;
+    c.big = big_tile(M, N);
+    return gemm(c, st);
+}
+
+// one decoder layer over M rows whose K/V go to (kc, vc) with `cap` tokens per
+// KV head, and whose attention is run by `attn` (prefill or branch)
+template <class Attn>
+int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, int cap, bool branch, Attn attn,
+          hipStream_t st) {
+    const int K_QKV = branch ? PCD_KC_BRANCH_QKV : PCD_KC_PREFILL_QKV;
+    const int K_O = branch ? PCD_KC_BRANCH_O : PCD_KC_PREFILL_O;
+    const int K_GU = branch ? PCD_KC_BRANCH_GATEUP : PCD_KC_PREFILL_GATEUP;
+    const int K_DN = branch ? PCD_KC_BRANCH_DOWN : PCD_KC_PREFILL_DOWN;
+    const pcd_config &c = m->cfg;
+    const int d = c.d_model, hd = c.head_dim, nq = c.n_heads * hd, nk = c.n_kv_heads * hd;
+    float *x = reinterpret_cast<float *>(m->ws + m->L.x);
+    void *h = m->ws + m->L.h, *q = m->ws + m->L.q, *ao = m->ws + m->L.ao, *act = m->ws + m->L.act;
+    m->tbegin(PCD_KC_OTHER, st);
+    rmsnorm(c.dtype, x, nullptr, M, d, m->an[l], c.rms_eps, h, st);
+    m->tend(st);
+    GemmCall g{};
+    g.dt = c.dtype;
+    g.A = h;
+    g.M = M;
+    g.N = nq + 2 * nk;
+    g.K = d;
+    g.B[0].ptr[0] = m->wq[l];
+    g.B[0].ptr[1] = m->wk[l];
+    g.B[0].ptr[2] = m->wv[l];
+    g.B[0].begin[0] = 0;
+    g.B[0].begin[1] = nq;
+    g.B[0].begin[2] = nq + nk;
+    g.B[0].nseg = 3;
+    g.epi = Epi::Qkv;
+    g.splits = 1;
+    g.out = q;
+    g.kc = kc;
+    g.vc = vc;
+    g.cap = cap;
+    g.pos = pos;
+    g.rope = reinterpret_cast<const float2 *>(m->ws + m->L.rope);
+    g.n_q = nq;
+    g.n_k = nk;
+    g.hd = hd;
+    m->tbegin(K_QKV, st);
+    if (!gemm(g, st)) return fail(PCD_E_ARG, "QKV projection: unsupported shape");
+    m->tend(st);
+    int rc = attn(q, ao);
+    if (rc != PCD_OK) return rc;
+    m->tbegin(K_O, st);
+    if (!gemm_resid(m, ao, M, d, nq, m->wo[l], st)) return fail(PCD_E_ARG, "O projection: unsupported shape");
+    m->tend(st);
+    m->tbegin(PCD_KC_OTHER, st);
+    rmsnorm(c.dtype, x, nullptr, M, d, m->mn[l], c.rms_eps, h, st);
+    m->tend(st);
+    GemmCall f{};
+    f.dt = c.dtype;
+    f.A = h;
+    f.M = M;
+    f.N = c.ffn_dim;
+    f.K = d;
+    f.B[0].ptr[0] = m->wg[l];
+    f.B[0].nseg = 1;
+    f.B[1].ptr[0] = m->wu[l];
+    f.B[1].nseg = 1;
+    f.epi = Epi::SwiGlu;
+    f.splits = 1;
+    f.out = act;
+    f.big = big_tile(M, c.ffn_dim);
+    m->tbegin(K_GU, st);
+    if (!gemm(f, st)) return fail(PCD_E_ARG, "gate/up projection: unsupported shape");
+    m->tend(st);
+    m->tbegin(K_DN, st);
+    if (!gemm_resid(m, act, M, d, c.ffn_dim, m->wd[l], st)) return fail(PCD_E_ARG, "down projection: unsupported shape");
+    m->tend(st);
+    return PCD_OK;
+}
+
+// bump-allocator over the pinned plan staging buffer, mirrored on the device
+struct Packer {
+    char *host;
+    char *dev;
+    size_t cap, off = 0;
+    bool overflow = false;
+    template <class T> T *put(const T *src, size_t n) {
+        const size_t o = off;
+        off = align_up(off + n * sizeof(T));
+        if (off > cap) {
+            overflow = true;
+            return nullptr;
+        }
+        if (n) std::memcpy(host + o, src, n * sizeof(T));
+        return reinterpret_cast<T *>(dev + o);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *pcd_last_error(void) { return g_err.c_str(); }
+
+size_t pcd_workspace_bytes(const pcd_config *cfg, const pcd_limits *lim) {
+    if (check_config(cfg, lim) != PCD_OK) return 0;
+    return layout(*cfg, *lim).total;
+}
+
+int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w, void *workspace,
+                     size_t ws_bytes, void *stream, pcd_model **out) {
+    int rc = check_config(cfg, lim);
+    if (rc != PCD_OK) return rc;
+    if (!w || !workspace || !out) return fail(PCD_E_ARG, "null weights, workspace or out");
+    const int L = cfg->n_layers;
+    if (!w->embed || !w->final_norm || !w->attn_norm || !w->mlp_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+        !w->w_gate || !w->w_up || !w->w_down || (!cfg->tied_lm_head && !w->lm_head))
+        return fail(PCD_E_ARG, "null weight pointer");
+    for (int l = 0; l < L; ++l)
+        if (!w->attn_norm[l] || !w->mlp_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->w_gate[l] ||
+            !w->w_up[l] || !w->w_down[l])
+            return fail(PCD_E_ARG, "null per-layer weight pointer");
+    Layout lay = layout(*cfg, *lim);
+    if (ws_bytes < lay.total)
+        return fail(PCD_E_CAP, "workspace of " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(lay.total));
+    pcd_model *m = new (std::nothrow) pcd_model();
+    if (!m) return fail(PCD_E_NOMEM, "model allocation");
+    m->cfg = *cfg;
+    m->lim = *lim;
+    m->L = lay;
+    m->ws = static_cast<char *>(workspace);
+    m->ws_bytes = ws_bytes;
+    m->embed = w->embed;
+    m->head = cfg->tied_lm_head ? w->embed : w->lm_head;
+    m->final_norm = w->final_norm;
+    m->wq.assign(w->wq, w->wq + L);
+    m->wk.assign(w->wk, w->wk + L);
+    m->wv.assign(w->wv, w->wv + L);
+    m->wo.assign(w->wo, w->wo + L);
+    m->wg.assign(w->w_gate, w->w_gate + L);
+    m->wu.assign(w->w_up, w->w_up + L);
+    m->wd.assign(w->w_down, w->w_down + L);
+    m->an.assign(w->attn_norm, w->attn_norm + L);
+    m->mn.assign(w->mlp_norm, w->mlp_norm + L);
+    m->stats.workspace_bytes = (int64_t)lay.total;
+    auto cleanup = [&](int code, const std::string &msg) {
+        pcd_free_model(m);
+        return fail(code, msg);
+    };
+    if (hipHostMalloc((void **)&m->plan_host, lay.plan_bytes, hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc((void **)&m->outs_host, lay.outs_bytes, hipHostMallocDefault) != hipSuccess)
+        return cleanup(PCD_E_DEVICE, "pinned staging allocation failed");
+    for (auto &e : m->ev)
+        if (hipEventCreate(&e) != hipSuccess) return cleanup(PCD_E_DEVICE, "event creation failed");
+    // RoPE table: (cos, sin) of pos * theta^(-2j/hd), computed in double
+    const int half = cfg->head_dim / 2;
+    std::vector<float2> rope((size_t)cfg->max_seq * half);
+    for (int p = 0; p < cfg->max_seq; ++p)
+        for (int j = 0; j < half; ++j) {
+            const double inv = std::pow((double)cfg->rope_theta, -2.0 * j / cfg->head_dim);
+            const double a = p * inv;
+            rope[(size_t)p * half + j] = make_float2((float)std::cos(a), (float)std::sin(a));
+        }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(m->ws + lay.rope, rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return cleanup(PCD_E_DEVICE, std::string("RoPE upload: ") + hipGetErrorString(hipGetLastError()));
+    *out = m;
+    return PCD_OK;
+}
+
+size_t pcd_state_bytes(const pcd_model *m, int32_t n) {
+    if (!m || n < 0) return 0;
+    return (size_t)n * m->cfg.n_layers * 2 * m->cfg.n_kv_heads * m->cfg.head_dim * esize(m);
+}
+
+int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, size_t kv_bytes, void *stream,
+                pcd_state **out) {
+    if (!m || !tokens || !kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+    const pcd_config &c = m->cfg;
+    if (n <= 0) return fail(PCD_E_ARG, "empty prefix");
+    if (n > m->lim.max_prefill_tokens || n > c.max_seq)
+        return fail(PCD_E_CAP, "prefix of " + std::to_string(n) + " tokens exceeds the model's limits");
+    if (kv_bytes < pcd_state_bytes(m, n)) return fail(PCD_E_CAP, "KV buffer too small");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= c.vocab_size)
+            return fail(PCD_E_TOKEN, "token id " + std::to_string(tokens[i]) + " outside the vocabulary");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim;
+    // device tables: tokens, one request (this KV buffer), attention blocks
+    std::vector<AttnBlock> blocks;
+    const int rows = n * grp;
+    for (int g = 0; g < c.n_kv_heads; ++g)
+        for (int r0 = 0; r0 < rows; r0 += ATT_ROWS)
+            blocks.push_back(AttnBlock{0, g, r0, std::min(ATT_ROWS, rows - r0), 0, n, 0});
+    Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
+    const int32_t *d_tok = pk.put(tokens, n);
+    const uint64_t kvaddr = reinterpret_cast<uint64_t>(kv_buf);
+    const uint64_t *d_kv = pk.put(&kvaddr, 1);
+    const int32_t *d_len = pk.put(&n, 1);
+    const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
+    if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
+    HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
+    m->tused = 0;
+    HIP_TRY(hipEventRecord(m->ev[3], st));
+    float *x = reinterpret_cast<float *>(m->ws + m->L.x);
+    m->tbegin(PCD_KC_OTHER, st);
+    embed(c.dtype, d_tok, n, m->embed, c.d_model, x, st);
+    m->tend(st);
+    const size_t layer_elems = (size_t)2 * c.n_kv_heads * n * hd;
+    for (int l = 0; l < c.n_layers; ++l) {
+        char *kc = static_cast<char *>(kv_buf) + (size_t)l * layer_elems * esize(m);
+        char *vc = kc + layer_elems / 2 * esize(m);
+        auto attn = [&](void *q, void *ao) {
+            AttnCall a{};
+            a.dt = c.dtype;
+            a.hd = hd;
+            a.n_heads = c.n_heads;
+            a.n_kv_heads = c.n_kv_heads;
+            a.layer = l;
+            a.q = q;
+            a.req_kv = d_kv;
+            a.req_len = d_len;
+            a.blocks = d_blk;
+            a.n_blocks = (int)blocks.size();
+            a.causal = true;
+            a.out = ao;
+            a.n_tokens = n;
+            m->tbegin(PCD_KC_PREFILL_ATTN, st);
+            const bool ok = attention(a, st);
+            m->tend(st);
+            return ok ? PCD_OK : fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
+        };
+        int rc = layer(m, l, n, nullptr, kc, vc, n, false, attn, st);
+        if (rc != PCD_OK) return rc;
+    }
+    HIP_TRY(hipEventRecord(m->ev[4], st));
+    HIP_TRY(hipGetLastError());
+    HIP_TRY(hipStreamSynchronize(st));
+    m->tcollect();
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, m->ev[3], m->ev[4]);
+    m->stats.last_prefill_ms = ms;
+    m->stats.prefill_passes += 1;
+    pcd_state *s = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_buf, n};
+    if (!s) return fail(PCD_E_NOMEM, "state allocation");
+    m->n_states++;
+    *out = s;
+    return PCD_OK;
+}
+
+int pcd_debug_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_lens, const pcd_request *reqs,
+                   pcd_plan_info *info) {
+    if (!info) return fail(PCD_E_ARG, "null info");
+    Plan p;
+    std::string err;
+    int rc = build_plan(V, max_seq, n_req, prefix_lens, reqs, p, err);
+    if (rc != PCD_OK) return fail(rc, err);
+    info->n_branch = (int32_t)p.tok.size();
+    info->n_readouts = (int32_t)p.ro_tok.size();
+    info->n_gathers = (int32_t)p.g_tok.size();
+    info->n_fields = (int32_t)p.f_ro_root.size();
+    info->n_candidates = (int32_t)p.c_path_off.size() - 1;
+    info->n_paths = (int32_t)p.c_path.size();
+    info->n_anc = (int32_t)p.anc.size();
+    auto cp = [](int32_t *dst, const std::vector<int32_t> &v) {
+        if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * 4);
+    };
+    cp(info->tok, p.tok);
+    cp(info->pos, p.pos);
+    cp(info->req, p.req);
+    cp(info->field, p.field);
+    cp(info->anc_off, p.anc_off);
+    cp(info->anc, p.anc);
+    cp(info->ro_tok, p.ro_tok);
+    cp(info->ro_field, p.ro_field);
+    cp(info->g_off, p.g_off);
+    cp(info->g_tok, p.g_tok);
+    cp(info->f_ro_root, p.f_ro_root);
+    cp(info->f_cand_off, p.f_cand_off);
+    cp(info->c_path_off, p.c_path_off);
+    cp(info->c_path, p.c_path);
+    return PCD_OK;
+}
+
+int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float T, pcd_outputs *outs,
+                    void *stream) {
+    if (!states || !reqs || !outs || n_req <= 0) return fail(PCD_E_ARG, "null argument or no requests");
+    if (!(T > 0.f) || !std::isfinite(T)) return fail(PCD_E_ARG, "temperature must be positive and finite");
+    for (int r = 0; r < n_req; ++r)
+        if (!states[r] || states[r]->magic != STATE_MAGIC) return fail(PCD_E_STATE, "invalid state handle");
+    pcd_model *m = states[0]->m;
+    for (int r = 1; r < n_req; ++r)
+        if (states[r]->m != m) return fail(PCD_E_STATE, "states of different models in one call");
+    for (int r = 0; r < n_req; ++r)
+        if (!outs[r].cand_prob || !outs[r].field_mass || !outs[r].field_margin || !outs[r].field_argmax)
+            return fail(PCD_E_ARG, "null output array");
+    const pcd_config &c = m->cfg;
+    const pcd_limits &lim = m->lim;
+    if (n_req > lim.max_requests) return fail(PCD_E_CAP, "more requests than max_requests");
+    std::vector<int32_t> lens(n_req);
+    for (int r = 0; r < n_req; ++r) lens[r] = states[r]->P;
+    Plan p;
+    std::string err;
+    int rc = build_plan(c.vocab_size, c.max_seq, n_req, lens.data(), reqs, p, err);
+    if (rc != PCD_OK) return fail(rc, err);
+    const int Tb = (int)p.tok.size(), R = (int)p.ro_tok.size(), G = (int)p.g_tok.size();
+    const int F = (int)p.f_ro_root.size(), C = (int)p.c_path_off.size() - 1, NP = (int)p.c_path.size();
+    if (Tb > lim.max_branch_tokens || R > lim.max_readouts || G > lim.max_gathers || F > lim.max_fields ||
+        C > lim.max_candidates || NP > path_cap(lim))
+        return fail(PCD_E_CAP, "decide call of " + std::to_string(Tb) + " branch tokens, " + std::to_string(R) +
+                                   " readouts, " + std::to_string(G) + " gathers exceeds the model's limits");
+    const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim, d = c.d_model;
+
+    // prefix attention blocks: per request, KV head, 64-row block and prefix split
+    int64_t nosplit = 0;
+    for (int r = 0; r < n_req; ++r)
+        nosplit += (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
+    const int want = (int)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, (512 + nosplit - 1) / nosplit));
+    std::vector<int32_t> req_splits(n_req);
+    std::vector<uint64_t> req_kv(n_req);
+    std::vector<AttnBlock> blocks;
+    for (int r = 0; r < n_req; ++r) {
+        const int P = lens[r];
+        int s = std::min(want, (P + 63) / 64);
+        const int slen = ((P + s - 1) / s + 63) / 64 * 64;
+        s = (P + slen - 1) / slen;
+        req_splits[r] = s;
+        req_kv[r] = reinterpret_cast<uint64_t>(states[r]->kv);
+        const int row_beg = p.r_tok[r] * grp, row_end = p.r_tok[r + 1] * grp;
+        for (int g = 0; g < c.n_kv_heads; ++g)
+            for (int r0 = row_beg; r0 < row_end; r0 += ATT_ROWS)
+                for (int k = 0; k < s; ++k)
+                    blocks.push_back(
+                        AttnBlock{r, g, r0, std::min(ATT_ROWS, row_end - r0), k * slen, std::min(P, (k + 1) * slen), k});
+    }
+    if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
+    const int32_t *d_tok = pk.put(p.tok.data(), Tb);
+    const int32_t *d_pos = pk.put(p.pos.data(), Tb);
+    const int32_t *d_req = pk.put(p.req.data(), Tb);
+    const int32_t *d_fs = pk.put(p.fs.data(), Tb);
+    const int32_t *d_nsc = pk.put(p.nsc.data(), Tb);
+    const int32_t *d_par = pk.put(p.par.data(), Tb);
+    const int32_t *d_ro = pk.put(p.ro_tok.data(), R);
+    const int32_t *d_goff = pk.put(p.g_off.data(), R + 1);
+    const int32_t *d_gtok = pk.put(p.g_tok.data(), G);
+    const int32_t *d_gro = pk.put(p.g_ro.data(), G);
+    const int32_t *d_froot = pk.put(p.f_ro_root.data(), F);
+    const int32_t *d_fcand = pk.put(p.f_cand_off.data(), F + 1);
+    const int32_t *d_cpo = pk.put(p.c_path_off.data(), C + 1);
+    const int32_t *d_cp = pk.put(p.c_path.data(), NP);
+    const int32_t *d_len = pk.put(lens.data(), n_req);
+    const int32_t *d_rsp = pk.put(req_splits.data(), n_req);
+    const uint64_t *d_kv = pk.put(req_kv.data(), n_req);
+    const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
+    if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
+
+    // result block on the device, packed by this call's sizes
+    char *ob = m->ws + m->L.outs;
+    size_t oo = 0;
+    auto oslot = [&](size_t bytes) {
+        const size_t o = oo;
+        oo = align_up(oo + bytes);
+        return o;
+    };
+    const size_t o_prob = oslot((size_t)C * 4), o_ls = oslot((size_t)C * 4), o_mass = oslot((size_t)F * 4),
+                 o_marg = oslot((size_t)F * 4), o_arg = oslot((size_t)F * 4), o_lse = oslot((size_t)R * 4),
+                 o_z = oslot((size_t)G * 4);
+    if (oo > m->L.outs_bytes) return fail(PCD_E_CAP, "output staging overflow");
+
+    HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
+    m->tused = 0;
+    HIP_TRY(hipEventRecord(m->ev[0], st));
+    float *x = reinterpret_cast<float *>(m->ws + m->L.x);
+    m->tbegin(PCD_KC_OTHER, st);
+    embed(c.dtype, d_tok, Tb, m->embed, d, x, st);
+    m->tend(st);
+    const size_t layer_elems = (size_t)2 * c.n_kv_heads * Tb * hd;
+    float *part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
+    float2 *part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
+    for (int l = 0; l < c.n_layers; ++l) {
+        char *kc = m->ws + m->L.kvb + (size_t)l * layer_elems * esize(m);
+        char *vc = kc + layer_elems / 2 * esize(m);
+        auto attn = [&](void *q, void *ao) {
+            AttnCall a{};
+            a.dt = c.dtype;
+            a.hd = hd;
+            a.n_heads = c.n_heads;
+            a.n_kv_heads = c.n_kv_heads;
+            a.layer = l;
+            a.q = q;
+            a.req_kv = d_kv;
+            a.req_len = d_len;
+            a.blocks = d_blk;
+            a.n_blocks = (int)blocks.size();
+            a.causal = false;
+            a.part_o = part_o;
+            a.part_ml = part_ml;
+            a.n_tokens = Tb;
+            m->tbegin(PCD_KC_BRANCH_ATTN, st);
+            const bool ok = attention(a, st);
+            m->tend(st);
+            if (!ok) return fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
+            TailCall t{};
+            t.dt = c.dtype;
+            t.hd = hd;
+            t.n_heads = c.n_heads;
+            t.n_kv_heads = c.n_kv_heads;
+            t.n_tokens = Tb;
+            t.q = q;
+            t.kb = kc;
+            t.vb = vc;
+            t.cap = Tb;
+            t.part_o = part_o;
+            t.part_ml = part_ml;
+            t.tok_req = d_req;
+            t.req_splits = d_rsp;
+            t.fs = d_fs;
+            t.nsc = d_nsc;
+            t.par = d_par;
+            t.out = ao;
+            m->tbegin(PCD_KC_BRANCH_TAIL, st);
+            attention_tail(t, st);
+            m->tend(st);
+            return PCD_OK;
+        };
+        rc = layer(m, l, Tb, d_pos, kc, vc, Tb, true, attn, st);
+        if (rc != PCD_OK) return rc;
+    }
+    HIP_TRY(hipEventRecord(m->ev[1], st));
+    // readout: final norm of the readout rows, LM head with online log-sum-exp, combine
+    void *hr = m->ws + m->L.hr;
+    m->tbegin(PCD_KC_OTHER, st);
+    rmsnorm(c.dtype, x, d_ro, R, d, m->final_norm, c.rms_eps, hr, st);
+    m->tend(st);
+    float2 *ro_part = reinterpret_cast<float2 *>(m->ws + m->L.ro_part);
+    float *z = reinterpret_cast<float *>(ob + o_z), *lse = reinterpret_cast<float *>(ob + o_lse);
+    GemmCall g{};
+    g.dt = c.dtype;
+    g.A = hr;
+    g.M = R;
+    g.N = c.vocab_size;
+    g.K = d;
+    g.B[0].ptr[0] = m->head;
+    g.B[0].nseg = 1;
+    g.epi = Epi::Readout;
+    g.splits = 1;
+    g.ro_part = ro_part;
+    g.g_tok = d_gtok;
+    g.g_ro = d_gro;
+    g.n_gather = G;
+    g.g_logit = z;
+    m->tbegin(PCD_KC_READOUT_LMHEAD, st);
+    if (!gemm(g, st)) return fail(PCD_E_ARG, "LM head: unsupported shape");
+    m->tend(st);
+    m->tbegin(PCD_KC_OTHER, st);
+    readout_lse(ro_part, c.vocab_size / 128, R, lse, st);
+    CombineCall cc{};
+    cc.n_fields = F;
+    cc.f_cand_off = d_fcand;
+    cc.f_ro_root = d_froot;
+    cc.c_path_off = d_cpo;
+    cc.c_path = d_cp;
+    cc.g_off = d_goff;
+    cc.g_ro = d_gro;
+    cc.z = z;
+    cc.lse = lse;
+    cc.temperature = T;
+    cc.prob = reinterpret_cast<float *>(ob + o_prob);
+    cc.logscore = reinterpret_cast<float *>(ob + o_ls);
+    cc.mass = reinterpret_cast<float *>(ob + o_mass);
+    cc.margin = reinterpret_cast<float *>(ob + o_marg);
+    cc.argmax = reinterpret_cast<int32_t *>(ob + o_arg);
+    combine(cc, st);
+    m->tend(st);
+    HIP_TRY(hipEventRecord(m->ev[2], st));
+    HIP_TRY(hipGetLastError());
+    HIP_TRY(hipMemcpyAsync(m->outs_host, ob, oo, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    m->tcollect();
+
+    const char *oh = m->outs_host;
+    for (int r = 0; r < n_req; ++r) {
+        const pcd_outputs &o = outs[r];
+        const int c0 = p.r_cand[r], nc = p.r_cand[r + 1] - c0;
+        const int f0 = p.r_field[r], nf = p.r_field[r + 1] - f0;
+        const int r0 = p.r_ro[r], nr = p.r_ro[r + 1] - r0;
+        const int g0 = p.r_g[r], ng = p.r_g[r + 1] - g0;
+        std::memcpy(o.cand_prob, oh + o_prob + (size_t)c0 * 4, (size_t)nc * 4);
+        if (o.cand_logscore) std::memcpy(o.cand_logscore, oh + o_ls + (size_t)c0 * 4, (size_t)nc * 4);
+        std::memcpy(o.field_mass, oh + o_mass + (size_t)f0 * 4, (size_t)nf * 4);
+        std::memcpy(o.field_margin, oh + o_marg + (size_t)f0 * 4, (size_t)nf * 4);
+        std::memcpy(o.field_argmax, oh + o_arg + (size_t)f0 * 4, (size_t)nf * 4);
+        if (o.readout_lse) std::memcpy(o.readout_lse, oh + o_lse + (size_t)r0 * 4, (size_t)nr * 4);
+        if (o.gather_logit) std::memcpy(o.gather_logit, oh + o_z + (size_t)g0 * 4, (size_t)ng * 4);
+    }
+    float ms_b = 0.f, ms_r = 0.f;
+    (void)hipEventElapsedTime(&ms_b, m->ev[0], m->ev[1]);
+    (void)hipEventElapsedTime(&ms_r, m->ev[1], m->ev[2]);
+    m->stats.branch_passes += 1;
+    m->stats.last_branch_ms = ms_b;
+    m->stats.last_readout_ms = ms_r;
+    m->stats.last_branch_tokens = Tb;
+    m->stats.last_readouts = R;
+    m->stats.last_gathers = G;
+    m->stats.last_requests = n_req;
+    return PCD_OK;
+}
+
+int pcd_decide(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pcd_candidate *candidates,
+               int32_t n_candidates, float temperature, pcd_outputs *out, void *stream) {
+    pcd_request r{fields, n_fields, candidates, n_candidates};
+    return pcd_decide_many(&s, &r, 1, temperature, out, stream);
+}
+
+int pcd_get_stats(const pcd_model *m, pcd_stats *out) {
+    if (!m || !out) return fail(PCD_E_ARG, "null argument");
+    *out = m->stats;
+    return PCD_OK;
+}
+
+int pcd_set_kernel_timing(pcd_model *m, int32_t enable) {
+    if (!m) return fail(PCD_E_ARG, "null model");
+    m->timing = enable != 0;
+    m->tused = 0;
+    for (int i = 0; i < PCD_KC_COUNT; ++i) {
+        m->kc_ms[i] = 0.f;
+        m->kc_n[i] = 0;
+    }
+    return PCD_OK;
+}
+
+int pcd_get_kernel_times(const pcd_model *m, float *total_ms, int64_t *launches) {
+    if (!m || !total_ms || !launches) return fail(PCD_E_ARG, "null argument");
+    for (int i = 0; i < PCD_KC_COUNT; ++i) {
+        total_ms[i] = m->kc_ms[i];
+        launches[i] = m->kc_n[i];
+    }
+    return PCD_OK;
+}
+
+void pcd_free_state(pcd_state *s) {
+    if (!s || s->magic != STATE_MAGIC) return;
+    s->magic = 0;
+    s->m->n_states--;
+    delete s;
+}
+
+void pcd_free_model(pcd_model *m) {
+    if (!m) return;
+    if (m->plan_host) (void)hipHostFree(m->plan_host);
+    if (m->outs_host) (void)hipHostFree(m->outs_host);
+    for (auto &e : m->ev)
+        if (e) (void)hipEventDestroy(e);
+    for (auto &e : m->tev) (void)hipEventDestroy(e);
+    delete m;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Launch interface of the gfx950 kernels (internal header, host side).
+//
+// Element type `dt` is PCD_DTYPE_F32 or PCD_DTYPE_BF16 for weights and
+// activations; the residual stream, softmax statistics and all reductions are
+// fp32.  Every launch goes on the given stream; none allocates or syncs.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pcd {
+
+// Rows of B (a weight matrix [N][K], row-major) may come from up to three
+// concatenated matrices: rows [begin[s], begin[s+1]) of the virtual matrix
+// are rows [0, ...) of ptr[s].
+struct BSegs {
+    const void *ptr[3];
+    int32_t begin[3];
+    int32_t nseg;
+};
+
+enum class Epi : int {
+    Qkv,      // RoPE on q and k, q -> q buffer, k and v -> a KV cache
+    Resid,    // x[m][n] += c   (fp32 residual stream)
+    Partial,  // split-K partial sums -> part[split][m][n]
+    SwiGlu,   // two B operands: out[m][n] = silu(c_gate) * c_up
+    Readout,  // per-row (max, sum exp) of the tile + gathered candidate logits
+};
+
+struct GemmCall {
+    int dt;
+    const void *A;   // [M][K] activations, element type dt
+    int32_t M, N, K;
+    BSegs B[2];      // B[1] used by SwiGlu only
+    Epi epi;
+    int splits;      // Partial only; K / splits must be a multiple of the k-tile
+    // epilogue arguments
+    float *x;        // Resid: residual [M][N]
+    float *part;     // Partial: [splits][M][N]
+    void *out;       // SwiGlu: [M][N] of dt;  Qkv: q buffer [M][Hq][hd]
+    void *kc, *vc;   // Qkv: K and V cache of this layer, [Hkv][cap][hd] each
+    int32_t cap;     // Qkv: tokens per KV head in the cache
+    const int32_t *pos;  // Qkv: position of each row (NULL: row index)
+    const float2 *rope;  // Qkv: [max_seq][hd/2] (cos, sin)
+    int32_t n_q, n_k, hd;    // Qkv: columns of q and of k; head dim
+    float2 *ro_part;         // Readout: [N/128][M] (max, sum exp) per vocab tile
+    const int32_t *g_tok, *g_ro;  // Readout: gathered token ids and their readout rows
+    int32_t n_gather;
+    float *g_logit;          // Readout: [n_gather]
+    bool big;                // prefer the 128x128 tile (large M)
+};
+
+// Returns false (and does nothing) on a shape the kernels do not support.
+bool gemm(const GemmCall &c, hipStream_t st);
+int gemm_k_tile(int dt);  // elements of K per pipeline stage
+
+void embed(int dt, const int32_t *tok, int32_t T, const void *E, int32_t d, float *x, hipStream_t st);
+// out[i] = x[rows ? rows[i] : i] / sqrt(mean(x^2) + eps) * w, as dt
+void rmsnorm(int dt, const float *x, const int32_t *rows, int32_t n, int32_t d, const float *w, float eps, void *out,
+             hipStream_t st);
+// x[m][n] += sum over s of part[s][m][n], s in increasing order
+void splitk_reduce(const float *part, int32_t splits, int32_t M, int32_t N, float *x, hipStream_t st);
+
+// Attention over a KV cache, flash style.  Query rows of a block are
+// (token, head within the KV group) pairs, token-major.
+struct AttnBlock {
+    int32_t req, g, row0, nrows, key0, key1, split;
+};
+struct AttnCall {
+    int dt;
+    int32_t hd, n_heads, n_kv_heads, layer;
+    const void *q;          // [tokens][Hq][hd]
+    const uint64_t *req_kv; // per request: device address of its KV buffer ([L][2][Hkv][P][hd])
+    const int32_t *req_len; // per request: P
+    const AttnBlock *blocks;
+    int32_t n_blocks;
+    bool causal;            // prefill: row token t sees keys <= t
+    void *out;              // causal: final output [tokens][Hq][hd] (dt)
+    float *part_o;          // branch: [split][tokens][Hq][hd] unnormalised
+    float2 *part_ml;        // branch: [split][tokens][Hq] (max in log2 units, sum)
+    int32_t n_tokens;       // tokens of this pass (row stride of the partials)
+};
+bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
+
+// Branch tokens: merge the prefix partials, then attend the token's visible
+// branch tokens (its scaffold up to itself, then its trie ancestors).
+struct TailCall {
+    int dt;
+    int32_t hd, n_heads, n_kv_heads, n_tokens;
+    const void *q;
+    const void *kb, *vb;     // branch K/V of this layer, [Hkv][cap][hd]
+    int32_t cap;
+    const float *part_o;
+    const float2 *part_ml;
+    const int32_t *tok_req, *req_splits;  // splits used by each request
+    const int32_t *fs, *nsc, *par;
+    void *out;               // [tokens][Hq][hd]
+};
+void attention_tail(const TailCall &c, hipStream_t st);
+
+// lse[r] from the per-tile partials of the readout GEMM.
+void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hipStream_t st);
+
+// Per field: logscore, softmax(logscore / T), mass, argmax, margin.
+struct CombineCall {
+    int32_t n_fields;
+    const int32_t *f_cand_off, *f_ro_root, *c_path_off, *c_path, *g_off, *g_ro;
+    const float *z, *lse;
+    float temperature;
+    float *prob, *logscore, *mass, *margin;
+    int32_t *argmax;
+};
+void combine(const CombineCall &c, hipStream_t st);
+
+}  // namespace pcd

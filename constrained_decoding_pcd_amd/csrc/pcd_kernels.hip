@@ -1,0 +1,795 @@
+// gfx950 kernels of the PCD hot path.
+//
+// Matrix work runs on the CDNA4 matrix cores: v_mfma_f32_16x16x32_bf16 for
+// bf16 models and v_mfma_f32_16x16x4_f32 for fp32 models, always with fp32
+// accumulation.  A lane of a 64-wide wavefront owns 8 consecutive k-elements
+// of one A row and of one B column (lane%16 picks the row/column, lane/16 the
+// k-octet); which k-octet goes to which lane group only has to agree between A
+// and B, so both operands use the same map.  The 16x16 accumulator of a lane
+// holds rows 4*(lane/16)+i, i<4, of column lane%16.
+#include "pcd_kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pcd {
+
+typedef uint16_t bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int PCD_DT_F32 = 0;
+
+// ---------------------------------------------------------------------------
+// element conversion (bf16 is stored as its 16-bit pattern)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                // round to nearest, ties to even
+    return (bf16_t)(u >> 16);
+}
+
+// 8 consecutive elements of one MFMA operand row/column
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { bf16x8_t v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void ld8(Frag<bf16_t> &f, const bf16_t *p) { f.v = *reinterpret_cast<const bf16x8_t *>(p); }
+__device__ __forceinline__ void ld8(Frag<float> &f, const float *p) {
+    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+// two runs of 4 elements (used for the P*V operand)
+__device__ __forceinline__ void ld4x2(Frag<bf16_t> &f, const bf16_t *p0, const bf16_t *p1) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p0), b = *reinterpret_cast<const uint2 *>(p1);
+    u32x4 u = {a.x, a.y, b.x, b.y};
+    f.v = __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ void ld4x2(Frag<float> &f, const float *p0, const float *p1) {
+    const float4 a = *reinterpret_cast<const float4 *>(p0), b = *reinterpret_cast<const float4 *>(p1);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void from8(Frag<bf16_t> &f, const float *x) {
+    u32x4 u;
+    for (int i = 0; i < 4; ++i)
+        u[i] = (uint32_t)from_f<bf16_t>(x[2 * i]) | ((uint32_t)from_f<bf16_t>(x[2 * i + 1]) << 16);
+    f.v = __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ void from8(Frag<float> &f, const float *x) {
+    for (int i = 0; i < 8; ++i) f.v[i] = x[i];
+}
+
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// GEMM  C[M][N] = A[M][K] . B[N][K]^T  with a fused epilogue
+// ---------------------------------------------------------------------------
+template <int NB> struct GemmArgs {
+    const void *A;
+    BSegs B[NB];
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n, splits, k_per_split, total, per_xcd;
+};
+
+struct EpiArgs {
+    float *x, *part;
+    void *out, *kc, *vc;
+    int32_t cap, n_q, n_k, hd;
+    const int32_t *pos;
+    const float2 *rope;
+    float2 *ro_part;
+    const int32_t *g_tok, *g_ro;
+    int32_t n_gather;
+    float *g_logit;
+};
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+template <typename T, int BM, int BN, int WM, int WN, int NB, Epi E>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
+    constexpr int BK = 128 / sizeof(T);        // 128 bytes of K per row per stage
+    constexpr int PAD = 16 / sizeof(T);
+    constexpr int LDK = BK + PAD;
+    constexpr int CH = 16 / sizeof(T);         // elements per 16-byte chunk
+    constexpr int CPR = BK / CH;               // chunks per row (8)
+    constexpr int A_CH = BM * CPR / 256;
+    constexpr int B_CH = BN * CPR / 256;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int KSTEPS = BK / 32;
+    constexpr bool LDS_EPI = (E == Epi::Qkv || E == Epi::Readout);
+    constexpr int AB_BYTES = (BM + NB * BN) * LDK * (int)sizeof(T);
+    constexpr int C_BYTES = LDS_EPI ? BM * (BN + 4) * 4 : 0;
+    constexpr int LDS_BYTES = AB_BYTES > C_BYTES ? AB_BYTES : C_BYTES;
+    static_assert(A_CH * 256 == BM * CPR && B_CH * 256 == BN * CPR, "tile/thread mismatch");
+    __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
+    T *As = reinterpret_cast<T *>(lds_raw);
+
+    // XCD-aware tile order: consecutive workgroups land on different XCDs, so
+    // hand each XCD a contiguous range of tiles (m fastest) and the tiles that
+    // share a B slab run on one XCD and share its L2.
+    const int b = blockIdx.x;
+    const int t = (b & 7) * g.per_xcd + (b >> 3);
+    if (t >= g.total) return;
+    const int tm = t % g.tiles_m;
+    const int rest = t / g.tiles_m;
+    const int ks = rest % g.splits;
+    const int tn = rest / g.splits;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = ks * g.k_per_split;
+    const int nkt = g.k_per_split / BK;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w % WM, wn = w / WM;
+    const int lr = lane & 15, lg = lane >> 4;
+
+    const T *A = reinterpret_cast<const T *>(g.A);
+    uint4 ra[A_CH], rb[NB][B_CH];
+    const T *bptr[NB][B_CH];
+    const T *aptr[A_CH];
+    bool aval[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
+        const int m = m0 + row;
+        aval[i] = m < g.M;
+        aptr[i] = A + (size_t)(aval[i] ? m : 0) * g.K + kbeg + kc;
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) {
+            const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
+            const int n = n0 + row;
+            const BSegs &s = g.B[q];
+            const int sg = (s.nseg > 2 && n >= s.begin[2]) ? 2 : ((s.nseg > 1 && n >= s.begin[1]) ? 1 : 0);
+            bptr[q][i] = reinterpret_cast<const T *>(s.ptr[sg]) + (size_t)(n - s.begin[sg]) * g.K + kbeg + kc;
+        }
+
+    auto gload = [&](int kt) {
+        const int ko = kt * BK;
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i)
+            ra[i] = aval[i] ? *reinterpret_cast<const uint4 *>(aptr[i] + ko) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int i = 0; i < B_CH; ++i) rb[q][i] = *reinterpret_cast<const uint4 *>(bptr[q][i] + ko);
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) {
+            const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
+            *reinterpret_cast<uint4 *>(As + row * LDK + kc) = ra[i];
+        }
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int i = 0; i < B_CH; ++i) {
+                const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
+                *reinterpret_cast<uint4 *>(As + (BM + q * BN + row) * LDK + kc) = rb[q][i];
+            }
+    };
+
+    f32x4 acc[NB][FM][FN];
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        if (kt + 1 < nkt) gload(kt + 1);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            Frag<T> fa[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ld8(fa[i], As + (wm * WTM + i * 16 + lr) * LDK + s * 32 + lg * 8);
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    Frag<T> fb;
+                    ld8(fb, As + (BM + q * BN + wn * WTN + j * 16 + lr) * LDK + s * 32 + lg * 8);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) mma(acc[q][i][j], fa[i], fb);
+                }
+            }
+        }
+        __syncthreads();
+        if (kt + 1 < nkt) {
+            lstore();
+            __syncthreads();
+        }
+    }
+
+    if constexpr (!LDS_EPI) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm * WTM + i * 16 + lg * 4 + r;
+                    const int n = n0 + wn * WTN + j * 16 + lr;
+                    if (m >= g.M) continue;
+                    if constexpr (E == Epi::Resid) {
+                        e.x[(size_t)m * g.N + n] += acc[0][i][j][r];
+                    } else if constexpr (E == Epi::Partial) {
+                        e.part[((size_t)ks * g.M + m) * g.N + n] = acc[0][i][j][r];
+                    } else if constexpr (E == Epi::SwiGlu) {
+                        const float v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
+                        reinterpret_cast<T *>(e.out)[(size_t)m * g.N + n] = from_f<T>(v);
+                    }
+                }
+    } else {
+        // stage the fp32 tile in LDS (the operand tiles are dead after the last barrier)
+        float *Cs = reinterpret_cast<float *>(lds_raw);
+        constexpr int LDC = BN + 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Cs[(wm * WTM + i * 16 + lg * 4 + r) * LDC + wn * WTN + j * 16 + lr] = acc[0][i][j][r];
+        __syncthreads();
+        if constexpr (E == Epi::Qkv) {
+            // rotate-half RoPE: pair (j, j + hd/2) of each head of q and k
+            const int hd = e.hd, half = hd >> 1;
+            for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
+                const int r = idx / (BN / 2), c = idx % (BN / 2);
+                const int hh = c / half, j = c % half;
+                const int m = m0 + r;
+                if (m >= g.M) continue;
+                const int col = hh * hd + j;
+                const int n = n0 + col;  // first-half column of this pair
+                float v1 = Cs[r * LDC + col], v2 = Cs[r * LDC + col + half];
+                if (n < e.n_q + e.n_k) {
+                    const int p = e.pos ? e.pos[m] : m;
+                    const float2 cs = e.rope[(size_t)p * half + j];
+                    const float o1 = v1 * cs.x - v2 * cs.y, o2 = v2 * cs.x + v1 * cs.y;
+                    v1 = o1;
+                    v2 = o2;
+                }
+                T *dst;
+                if (n < e.n_q) {
+                    dst = reinterpret_cast<T *>(e.out) + (size_t)m * e.n_q + (n - j);
+                } else if (n < e.n_q + e.n_k) {
+                    const int kh = (n - e.n_q) / hd;
+                    dst = reinterpret_cast<T *>(e.kc) + ((size_t)kh * e.cap + m) * hd;
+                } else {
+                    const int vh = (n - e.n_q - e.n_k) / hd;
+                    dst = reinterpret_cast<T *>(e.vc) + ((size_t)vh * e.cap + m) * hd;
+                }
+                dst[j] = from_f<T>(v1);
+                dst[j + half] = from_f<T>(v2);
+            }
+        } else if constexpr (E == Epi::Readout) {
+            // per readout row: max and sum of exp over this vocab tile
+            for (int r = w; r < BM; r += 4) {
+                const int m = m0 + r;
+                if (m >= g.M) break;
+                float mx = -INFINITY;
+                for (int c = lane; c < BN; c += 64) mx = fmaxf(mx, Cs[r * LDC + c]);
+                mx = wave_max(mx);
+                float s = 0.f;
+                for (int c = lane; c < BN; c += 64) s += __expf(Cs[r * LDC + c] - mx);
+                s = wave_sum(s);
+                if (lane == 0) e.ro_part[(size_t)tn * g.M + m] = make_float2(mx, s);
+            }
+            // candidate-token logits that fall in this tile
+            for (int q = tid; q < e.n_gather; q += 256) {
+                const int ro = e.g_ro[q], tk = e.g_tok[q];
+                if (ro >= m0 && ro < m0 + BM && tk >= n0 && tk < n0 + BN) e.g_logit[q] = Cs[(ro - m0) * LDC + (tk - n0)];
+            }
+        }
+    }
+}
+
+template <typename T, int BM, int BN, int NB, Epi E>
+static void launch_gemm(const GemmCall &c, hipStream_t st) {
+    constexpr int BK = 128 / sizeof(T);
+    GemmArgs<NB> g;
+    g.A = c.A;
+    for (int q = 0; q < NB; ++q) g.B[q] = c.B[q];
+    g.M = c.M;
+    g.N = c.N;
+    g.K = c.K;
+    g.tiles_m = (c.M + BM - 1) / BM;
+    g.tiles_n = c.N / BN;
+    g.splits = (E == Epi::Partial) ? c.splits : 1;
+    g.k_per_split = c.K / g.splits;
+    (void)BK;
+    g.total = g.tiles_m * g.tiles_n * g.splits;
+    g.per_xcd = (g.total + 7) / 8;
+    EpiArgs e;
+    e.x = c.x;
+    e.part = c.part;
+    e.out = c.out;
+    e.kc = c.kc;
+    e.vc = c.vc;
+    e.cap = c.cap;
+    e.n_q = c.n_q;
+    e.n_k = c.n_k;
+    e.hd = c.hd;
+    e.pos = c.pos;
+    e.rope = c.rope;
+    e.ro_part = c.ro_part;
+    e.g_tok = c.g_tok;
+    e.g_ro = c.g_ro;
+    e.n_gather = c.n_gather;
+    e.g_logit = c.g_logit;
+    hipLaunchKernelGGL((k_gemm<T, BM, BN, 2, 2, NB, E>), dim3(g.per_xcd * 8), dim3(256), 0, st, g, e);
+}
+
+template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
+    constexpr int BK = 128 / sizeof(T);
+    const int splits = c.epi == Epi::Partial ? c.splits : 1;
+    if (c.M <= 0 || c.K % (BK * splits) != 0) return false;
+    switch (c.epi) {
+        case Epi::Qkv:
+            if (c.N % 128 == 0 && 128 % c.hd == 0) {
+                launch_gemm<T, 64, 128, 1, Epi::Qkv>(c, st);
+                return true;
+            }
+            if (c.N % 64 == 0 && 64 % c.hd == 0) {
+                launch_gemm<T, 64, 64, 1, Epi::Qkv>(c, st);
+                return true;
+            }
+            return false;
+        case Epi::Readout:
+            if (c.N % 128) return false;
+            launch_gemm<T, 64, 128, 1, Epi::Readout>(c, st);
+            return true;
+        case Epi::Resid:
+            if (c.N % 64) return false;
+            if (c.big && c.N % 128 == 0) launch_gemm<T, 128, 128, 1, Epi::Resid>(c, st);
+            else launch_gemm<T, 64, 64, 1, Epi::Resid>(c, st);
+            return true;
+        case Epi::Partial:
+            if (c.N % 64) return false;
+            launch_gemm<T, 64, 64, 1, Epi::Partial>(c, st);
+            return true;
+        case Epi::SwiGlu:
+            if (c.N % 64) return false;
+            if (c.big && c.N % 128 == 0) launch_gemm<T, 128, 128, 2, Epi::SwiGlu>(c, st);
+            else launch_gemm<T, 64, 64, 2, Epi::SwiGlu>(c, st);
+            return true;
+    }
+    return false;
+}
+
+bool gemm(const GemmCall &c, hipStream_t st) {
+    return c.dt == PCD_DT_F32 ? gemm_t<float>(c, st) : gemm_t<bf16_t>(c, st);
+}
+int gemm_k_tile(int dt) { return dt == PCD_DT_F32 ? 32 : 64; }
+
+// ---------------------------------------------------------------------------
+// embedding gather, RMSNorm, split-K reduction
+// ---------------------------------------------------------------------------
+template <typename T> __global__ void k_embed(const int32_t *tok, const T *E, int32_t d, float *x) {
+    const int t = blockIdx.x;
+    const T *row = E + (size_t)tok[t] * d;
+    for (int j = threadIdx.x; j < d; j += blockDim.x) x[(size_t)t * d + j] = to_f(row[j]);
+}
+
+void embed(int dt, const int32_t *tok, int32_t T, const void *E, int32_t d, float *x, hipStream_t st) {
+    if (T <= 0) return;
+    if (dt == PCD_DT_F32) hipLaunchKernelGGL(k_embed<float>, dim3(T), dim3(256), 0, st, tok, (const float *)E, d, x);
+    else hipLaunchKernelGGL(k_embed<bf16_t>, dim3(T), dim3(256), 0, st, tok, (const bf16_t *)E, d, x);
+}
+
+template <typename T>
+__global__ void k_rmsnorm(const float *x, const int32_t *rows, int32_t d, const float *w, float eps, T *out) {
+    __shared__ float red[4];
+    const int i = blockIdx.x;
+    const float *xr = x + (size_t)(rows ? rows[i] : i) * d;
+    float s = 0.f;
+    for (int j = threadIdx.x; j < d; j += 256) s += xr[j] * xr[j];
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+    for (int j = threadIdx.x; j < d; j += 256) out[(size_t)i * d + j] = from_f<T>(xr[j] * inv * w[j]);
+}
+
+void rmsnorm(int dt, const float *x, const int32_t *rows, int32_t n, int32_t d, const float *w, float eps, void *out,
+             hipStream_t st) {
+    if (n <= 0) return;
+    if (dt == PCD_DT_F32)
+        hipLaunchKernelGGL(k_rmsnorm<float>, dim3(n), dim3(256), 0, st, x, rows, d, w, eps, (float *)out);
+    else hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(n), dim3(256), 0, st, x, rows, d, w, eps, (bf16_t *)out);
+}
+
+__global__ void k_splitk_reduce(const float4 *part, int32_t splits, size_t n4, float4 *x) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float4 a = x[i];
+    for (int s = 0; s < splits; ++s) {
+        const float4 p = part[s * n4 + i];
+        a.x += p.x;
+        a.y += p.y;
+        a.z += p.z;
+        a.w += p.w;
+    }
+    x[i] = a;
+}
+
+void splitk_reduce(const float *part, int32_t splits, int32_t M, int32_t N, float *x, hipStream_t st) {
+    const size_t n4 = (size_t)M * N / 4;
+    if (n4 == 0) return;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                       (const float4 *)part, splits, n4, (float4 *)x);
+}
+
+// ---------------------------------------------------------------------------
+// attention over a KV cache: 64 query rows per workgroup (16 per wave), key
+// tiles of 64 staged in LDS once for all of them (K row-major, V transposed),
+// S^T = K Q^T on the matrix cores so that each lane holds 4 keys of one query
+// row, online softmax in base 2 with the row statistics reduced across the
+// four lane groups, then O += P V on the matrix cores.
+// ---------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_attn(AttnCall c) {
+    constexpr int KT = 64;
+    constexpr int KPAD = 16 / sizeof(T);
+    constexpr int LDKS = HD + KPAD;   // K tile row stride
+    constexpr int LDV = KT + KPAD;    // V^T row stride
+    constexpr int HS = HD / 32;       // k-steps of Q.K
+    constexpr int CF = HD / 16;       // output column fragments
+    __shared__ __attribute__((aligned(16))) T Ks[KT * LDKS];
+    __shared__ __attribute__((aligned(16))) T Vt[HD * LDV];
+
+    const AttnBlock blk = c.blocks[blockIdx.x];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
+    const int P = c.req_len[blk.req];
+    const T *kvbase = reinterpret_cast<const T *>(c.req_kv[blk.req]);
+    const T *Kg = kvbase + ((size_t)c.layer * 2 * Hkv + blk.g) * (size_t)P * HD;
+    const T *Vg = kvbase + ((size_t)c.layer * 2 * Hkv + Hkv + blk.g) * (size_t)P * HD;
+    const T *Q = reinterpret_cast<const T *>(c.q);
+    const float qscale = LOG2E / sqrtf((float)HD);
+
+    // this lane's query row (B operand of S^T) and its token
+    const int my_row = blk.row0 + w * 16 + lr;
+    const bool row_ok = (w * 16 + lr) < blk.nrows;
+    const int rr = row_ok ? my_row : blk.row0;
+    const int tq = rr / grp, hq = blk.g * grp + rr % grp;
+    Frag<T> qf[HS];
+#pragma unroll
+    for (int s = 0; s < HS; ++s) ld8(qf[s], Q + ((size_t)tq * Hq + hq) * HD + s * 32 + lg * 8);
+    const int kend_row = c.causal ? (tq + 1) : blk.key1;
+
+    int kmax = blk.key1;
+    if (c.causal) {
+        const int last = (blk.row0 + blk.nrows - 1) / grp + 1;
+        kmax = last < kmax ? last : kmax;
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;  // stats of query row lr (replicated over lg)
+    f32x4 o[CF];
+#pragma unroll
+    for (int j = 0; j < CF; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int CH = 16 / sizeof(T);
+    constexpr int CHUNKS = KT * HD / CH;
+    for (int k0 = blk.key0; k0 < kmax; k0 += KT) {
+        // stage K (row-major) and V (transposed); keys past kmax are zero
+        for (int ci = tid; ci < CHUNKS; ci += 256) {
+            const int key = ci / (HD / CH), dc = (ci % (HD / CH)) * CH;
+            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+            if (k0 + key < kmax) {
+                kv = *reinterpret_cast<const uint4 *>(Kg + (size_t)(k0 + key) * HD + dc);
+                vv = *reinterpret_cast<const uint4 *>(Vg + (size_t)(k0 + key) * HD + dc);
+            }
+            *reinterpret_cast<uint4 *>(Ks + key * LDKS + dc) = kv;
+            const T *ve = reinterpret_cast<const T *>(&vv);
+#pragma unroll
+            for (int i = 0; i < CH; ++i) Vt[(dc + i) * LDV + key] = ve[i];
+        }
+        __syncthreads();
+
+        // S^T tile: s[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r)
+        f32x4 s[KT / 16];
+#pragma unroll
+        for (int kf = 0; kf < KT / 16; ++kf) {
+            s[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < HS; ++st) {
+                Frag<T> kf8;
+                ld8(kf8, Ks + (kf * 16 + lr) * LDKS + st * 32 + lg * 8);
+                mma(s[kf], kf8, qf[st]);
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = k0 + kf * 16 + lg * 4 + r;
+                const float v = (key < kend_row) ? s[kf][r] * qscale : -INFINITY;
+                s[kf][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_ref);
+        float psum = 0.f;
+        float p[KT / 16][4];
+#pragma unroll
+        for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[kf][r] = exp2f(s[kf][r] - m_ref);
+                psum += p[kf][r];
+            }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+
+        // rescale O: its rows are queries 4*lg + r, whose alpha sits in lane 4*lg + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float a = __shfl(alpha, lg * 4 + r);
+#pragma unroll
+            for (int j = 0; j < CF; ++j) o[j][r] *= a;
+        }
+        // O += P V over two 32-key steps; A = P (row lr, keys {4lg..4lg+3} and {16+4lg..}), B = V
+#pragma unroll
+        for (int st = 0; st < KT / 32; ++st) {
+            float pv[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pv[r] = p[2 * st][r];
+                pv[4 + r] = p[2 * st + 1][r];
+            }
+            Frag<T> pa;
+            from8(pa, pv);
+#pragma unroll
+            for (int j = 0; j < CF; ++j) {
+                Frag<T> vb;
+                const T *vrow = Vt + (j * 16 + lr) * LDV + st * 32 + lg * 4;
+                ld4x2(vb, vrow, vrow + 16);
+                mma(o[j], pa, vb);
+            }
+        }
+        __syncthreads();
+    }
+
+    // write: O row 4*lg + r of this wave
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int qi = lg * 4 + r;
+        const float lq = __shfl(l_run, qi);
+        const float mq = __shfl(m_run, qi);
+        if (w * 16 + qi >= blk.nrows) continue;
+        const int row = blk.row0 + w * 16 + qi;
+        const int t = row / grp, h = blk.g * grp + row % grp;
+        if (c.causal) {
+            T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
+            const float inv = 1.0f / lq;
+#pragma unroll
+            for (int j = 0; j < CF; ++j) out[j * 16 + lr] = from_f<T>(o[j][r] * inv);
+        } else {
+            const size_t pr = ((size_t)blk.split * c.n_tokens + t) * Hq + h;
+            float *po = c.part_o + pr * HD;
+#pragma unroll
+            for (int j = 0; j < CF; ++j) po[j * 16 + lr] = o[j][r];
+            if (lr == 0) c.part_ml[pr] = make_float2(mq, lq);
+        }
+    }
+}
+
+template <typename T> static bool attention_t(const AttnCall &c, hipStream_t st) {
+    if (c.n_blocks <= 0) return true;
+    switch (c.hd) {
+        case 32: hipLaunchKernelGGL((k_attn<T, 32>), dim3(c.n_blocks), dim3(256), 0, st, c); return true;
+        case 64: hipLaunchKernelGGL((k_attn<T, 64>), dim3(c.n_blocks), dim3(256), 0, st, c); return true;
+        case 128:
+            // an fp32 128-wide K/V tile pair does not fit the static LDS limit
+            if constexpr (sizeof(T) == 2) {
+                hipLaunchKernelGGL((k_attn<T, 128>), dim3(c.n_blocks), dim3(256), 0, st, c);
+                return true;
+            }
+            return false;
+    }
+    return false;
+}
+bool attention(const AttnCall &c, hipStream_t st) {
+    return c.dt == PCD_DT_F32 ? attention_t<float>(c, st) : attention_t<bf16_t>(c, st);
+}
+
+// One wavefront per (branch token, query head): merge the prefix partials,
+// then the visible branch keys, one at a time.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void k_attn_tail(TailCall c) {
+    constexpr int PL = (HD + 63) / 64;  // dims per lane
+    const int lane = threadIdx.x & 63;
+    const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
+    if (id >= c.n_tokens * Hq) return;
+    const int t = id / Hq, h = id % Hq, g = h / grp;
+    const float qscale = LOG2E / sqrtf((float)HD);
+
+    float m = -INFINITY, l = 0.f, o[PL], q[PL];
+    const int ns = c.req_splits[c.tok_req[t]];
+    const T *Q = reinterpret_cast<const T *>(c.q) + ((size_t)t * Hq + h) * HD;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int d = lane + 64 * i;
+        o[i] = 0.f;
+        q[i] = d < HD ? to_f(Q[d]) : 0.f;
+    }
+    for (int s = 0; s < ns; ++s) {
+        const size_t pr = ((size_t)s * c.n_tokens + t) * Hq + h;
+        const float2 ml = c.part_ml[pr];
+        const float mn = fmaxf(m, ml.x);
+        const float a = exp2f(m - mn), b = exp2f(ml.x - mn);
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int d = lane + 64 * i;
+            if (d < HD) o[i] = o[i] * a + c.part_o[pr * HD + d] * b;
+        }
+        l = l * a + ml.y * b;
+        m = mn;
+    }
+    const T *Kb = reinterpret_cast<const T *>(c.kb) + (size_t)g * c.cap * HD;
+    const T *Vb = reinterpret_cast<const T *>(c.vb) + (size_t)g * c.cap * HD;
+    auto visit = [&](int k) {
+        float sdot = 0.f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int d = lane + 64 * i;
+            if (d < HD) sdot += q[i] * to_f(Kb[(size_t)k * HD + d]);
+        }
+        const float sc = wave_sum(sdot) * qscale;
+        const float mn = fmaxf(m, sc);
+        const float a = exp2f(m - mn), b = exp2f(sc - mn);
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int d = lane + 64 * i;
+            if (d < HD) o[i] = o[i] * a + to_f(Vb[(size_t)k * HD + d]) * b;
+        }
+        l = l * a + b;
+        m = mn;
+    };
+    const int fs = c.fs[t], nsc = c.nsc[t];
+    const int sc_end = (t < fs + nsc) ? t : fs + nsc - 1;  // scaffold tokens up to itself
+    for (int k = fs; k <= sc_end; ++k) visit(k);
+    if (t >= fs + nsc)
+        for (int k = t; k >= 0; k = c.par[k]) visit(k);  // itself, then its trie ancestors
+    T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int d = lane + 64 * i;
+        if (d < HD) out[d] = from_f<T>(o[i] * inv);
+    }
+}
+
+template <typename T> static void tail_t(const TailCall &c, hipStream_t st) {
+    const int waves = c.n_tokens * c.n_heads;
+    if (waves <= 0) return;
+    const dim3 grid((waves + 3) / 4);
+    switch (c.hd) {
+        case 32: hipLaunchKernelGGL((k_attn_tail<T, 32>), grid, dim3(256), 0, st, c); break;
+        case 64: hipLaunchKernelGGL((k_attn_tail<T, 64>), grid, dim3(256), 0, st, c); break;
+        case 128: hipLaunchKernelGGL((k_attn_tail<T, 128>), grid, dim3(256), 0, st, c); break;
+    }
+}
+void attention_tail(const TailCall &c, hipStream_t st) {
+    if (c.dt == PCD_DT_F32) tail_t<float>(c, st);
+    else tail_t<bf16_t>(c, st);
+}
+
+// ---------------------------------------------------------------------------
+// readout statistics and the per-field combine
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    float mx = -INFINITY;
+    for (int i = threadIdx.x; i < n_tiles; i += 256) mx = fmaxf(mx, part[(size_t)i * R + r].x);
+    mx = wave_max(mx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float s = 0.f;
+    for (int i = threadIdx.x; i < n_tiles; i += 256) {
+        const float2 p = part[(size_t)i * R + r];
+        s += p.y * __expf(p.x - mx);
+    }
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) lse[r] = mx + logf(red[0] + red[1] + red[2] + red[3]);
+}
+
+void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hipStream_t st) {
+    if (R <= 0) return;
+    hipLaunchKernelGGL(k_readout_lse, dim3(R), dim3(256), 0, st, part, n_tiles, R, lse);
+}
+
+__global__ void k_combine(CombineCall c) {
+    const int f = blockIdx.x * blockDim.x + threadIdx.x;
+    if (f >= c.n_fields) return;
+    const int c0 = c.f_cand_off[f], c1 = c.f_cand_off[f + 1];
+    auto score = [&](int k) {
+        float s = 0.f;
+        for (int i = c.c_path_off[k]; i < c.c_path_off[k + 1]; ++i) {
+            const int gi = c.c_path[i];
+            s += c.z[gi] - c.lse[c.g_ro[gi]];
+        }
+        return s;
+    };
+    float best = -INFINITY, second = -INFINITY;
+    int arg = 0;
+    for (int k = c0; k < c1; ++k) {
+        const float s = score(k);
+        if (c.logscore) c.logscore[k] = s;
+        if (s > best) {
+            second = best;
+            best = s;
+            arg = k - c0;
+        } else if (s > second) {
+            second = s;
+        }
+    }
+    const float invT = 1.0f / c.temperature;
+    float den = 0.f;
+    for (int k = c0; k < c1; ++k) den += __expf((score(k) - best) * invT);
+    for (int k = c0; k < c1; ++k) c.prob[k] = __expf((score(k) - best) * invT) / den;
+    const int root = c.f_ro_root[f];
+    float mass = 0.f;
+    for (int gi = c.g_off[root]; gi < c.g_off[root + 1]; ++gi) mass += __expf(c.z[gi] - c.lse[root]);
+    c.mass[f] = mass;
+    c.margin[f] = best - second;
+    c.argmax[f] = arg;
+}
+
+void combine(const CombineCall &c, hipStream_t st) {
+    if (c.n_fields <= 0) return;
+    hipLaunchKernelGGL(k_combine, dim3((c.n_fields + 63) / 64), dim3(64), 0, st, c);
+}
+
+}  // namespace pcd

@@ -1,0 +1,245 @@
+/*
+ * pcd.h -- C ABI of the parallel constrained decoding (PCD) library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   - "Parallel Constrained Decoding from Scratch" (faritgaleev.com), sections
+ *     "The piece of plumbing you need: the KV cache" and "The idea: parallel
+ *     constrained decoding": prefill a shared prompt once; give every schema
+ *     field one short row that ends where its labels part ways; run all rows
+ *     in one batched pass over the shared prompt's KV cache; read each row's
+ *     next-token distribution restricted to the tokens that start an allowed
+ *     label; report the renormalised probabilities and the candidate mass.
+ *   - same page, "When one token is not enough": labels whose first tokens
+ *     collide are told apart by extending the row down the shared branch in
+ *     the same batched pass and multiplying along the path.
+ *   - "Parallel Constrained Decoding: A Technical Reference" (shivam2003.com),
+ *     section 4 "The algorithm": candidate softmax with temperature, argmax.
+ *
+ * Everything here works on token ids; tokenizing is the caller's business.
+ *
+ * Conventions
+ *   - Every function returns an int status: PCD_OK (0) or a negative PCD_E_*
+ *     code; pcd_last_error() then holds a message (thread-local).
+ *   - All validation happens before any device work: a failing call leaves
+ *     no partial state and writes no output.
+ *   - Device memory (weights, KV buffers, workspace) is allocated by the
+ *     caller and borrowed by the library; it must outlive the handles that
+ *     use it.  Handles are library-owned host objects, freed with pcd_free_*.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call that
+ *     takes a stream enqueues its device work there and returns after that
+ *     stream has drained: the API is synchronous.
+ *   - A model is used from one host thread at a time.
+ */
+#ifndef PCD_H
+#define PCD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PCD_OK 0
+#define PCD_E_ARG (-1)     /* null pointer, negative count, unsupported shape */
+#define PCD_E_TOKEN (-2)   /* token id outside [0, vocab_size) */
+#define PCD_E_NCAND (-3)   /* a field with fewer than 2 or more than 255 candidates */
+#define PCD_E_EMPTY (-4)   /* empty scaffold or empty candidate */
+#define PCD_E_DUP (-5)     /* two identical candidate token sequences in one field */
+#define PCD_E_PREFIX (-6)  /* a candidate is a proper prefix of another one */
+#define PCD_E_CAP (-7)     /* a size exceeds max_seq, the workspace limits or a buffer */
+#define PCD_E_STATE (-8)   /* state handle of another model */
+#define PCD_E_DEVICE (-9)  /* HIP runtime error; the HIP message is in pcd_last_error() */
+#define PCD_E_NOMEM (-10)  /* host allocation failed */
+
+#define PCD_MAX_CANDIDATES 255
+
+#define PCD_DTYPE_F32 0
+#define PCD_DTYPE_BF16 1
+
+/* ---- model description ---------------------------------------------------- */
+/* A Qwen2.5-shaped decoder: RMSNorm, rotate-half RoPE, grouped-query attention
+ * without biases, SwiGLU MLP.  head_dim must be 32, 64 or 128; d_model,
+ * n_heads*head_dim and ffn_dim must be multiples of 128 (64 for f32 models);
+ * vocab_size a multiple of 128. */
+typedef struct {
+    int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size;
+    int32_t max_seq;       /* largest position id + 1 (RoPE table size) */
+    float rope_theta;      /* inverse frequency of pair j is theta^(-2j/head_dim) */
+    float rms_eps;         /* x / sqrt(mean(x^2) + eps) * w */
+    int32_t tied_lm_head;  /* 1: the LM head is the embedding matrix */
+    int32_t dtype;         /* PCD_DTYPE_F32 or PCD_DTYPE_BF16: weights and activations */
+} pcd_config;
+
+/* Device pointers to the weights, elements of cfg.dtype (bf16 = raw 16-bit
+ * patterns), every matrix [out][in] row-major.  The per-layer fields are HOST
+ * arrays of n_layers DEVICE pointers; the library copies the arrays.  Norm
+ * weights are fp32 vectors of d_model. */
+typedef struct {
+    const void *embed;          /* [vocab][d] */
+    const void *lm_head;        /* [vocab][d]; NULL when tied_lm_head */
+    const float *final_norm;    /* [d] */
+    const float *const *attn_norm, *const *mlp_norm;           /* [L] -> [d] */
+    const void *const *wq, *const *wk, *const *wv, *const *wo; /* [Hq*hd][d], [Hkv*hd][d] x2, [d][Hq*hd] */
+    const void *const *w_gate, *const *w_up, *const *w_down;   /* [F][d] x2, [d][F] */
+} pcd_weights;
+
+/* Upper bounds a model's workspace is sized for. */
+typedef struct {
+    int32_t max_prefill_tokens;  /* tokens per pcd_prefill call */
+    int32_t max_branch_tokens;   /* scaffold + trie tokens of one decide call, all requests */
+    int32_t max_readouts;        /* readout rows of one decide call */
+    int32_t max_gathers;         /* candidate-token logits gathered by one decide call */
+    int32_t max_fields;          /* fields of one decide call, all requests */
+    int32_t max_candidates;      /* candidates of one decide call, all requests */
+    int32_t max_requests;        /* requests of one pcd_decide_many call */
+} pcd_limits;
+
+/* ---- one request's schema (host memory, read during the call) ------------ */
+typedef struct {
+    const int32_t *tokens;  /* the candidate's token ids */
+    int32_t n_tokens;
+} pcd_candidate;
+
+typedef struct {
+    const int32_t *scaffold;  /* the field's row: key tokens up to where its labels part ways */
+    int32_t n_scaffold;
+    int32_t cand_offset;      /* first candidate of this field in the request's candidate array */
+    int32_t n_cands;          /* 2..255 */
+} pcd_field;
+
+typedef struct {
+    const pcd_field *fields;
+    int32_t n_fields;
+    const pcd_candidate *candidates;
+    int32_t n_candidates;
+} pcd_request;
+
+/* ---- results (caller-owned HOST arrays, written only on PCD_OK) ---------- */
+typedef struct {
+    float *cand_prob;        /* [n_candidates] softmax of logscore / T over each field's candidates */
+    float *cand_logscore;    /* [n_candidates] nullable: sum of log p along the candidate's scored path */
+    float *field_mass;       /* [n_fields] full-vocabulary probability of the distinct first tokens */
+    float *field_margin;     /* [n_fields] top-1 minus top-2 logscore, nats */
+    int32_t *field_argmax;   /* [n_fields] candidate index within the field; ties to the lowest index */
+    float *readout_lse;      /* nullable [n_readouts]: log-sum-exp of each readout row's logits */
+    float *gather_logit;     /* nullable [n_gathers]: the gathered candidate-token logits */
+} pcd_outputs;
+
+/* Counters of the last calls on a model. */
+typedef struct {
+    int64_t prefill_passes;   /* batched decoder passes run by prefill calls */
+    int64_t branch_passes;    /* batched decoder passes run by decide calls */
+    int32_t last_branch_tokens, last_readouts, last_gathers, last_requests;
+    float last_prefill_ms, last_branch_ms, last_readout_ms; /* hipEvent times of the last calls */
+    int64_t workspace_bytes;
+} pcd_stats;
+
+/* Plan of one decide call, as laid out for the batched pass (host only). */
+typedef struct {
+    int32_t n_branch, n_readouts, n_gathers, n_fields, n_candidates, n_paths, n_anc;
+    /* Optional host arrays (NULL to skip), sized by the counts above:
+     * per branch token: tok, pos, req, field; anc_off [n_branch+1] and anc
+     * [n_anc]: the branch tokens each one sees (ascending, itself last);
+     * per readout: ro_tok, ro_field, g_off [n_readouts+1]; per gather: g_tok;
+     * per field: f_ro_root, f_cand_off [n_fields+1]; per candidate:
+     * c_path_off [n_candidates+1] and c_path [n_paths] (gather indices). */
+    int32_t *tok, *pos, *req, *field, *anc_off, *anc;
+    int32_t *ro_tok, *ro_field, *g_off, *g_tok;
+    int32_t *f_ro_root, *f_cand_off, *c_path_off, *c_path;
+} pcd_plan_info;
+
+/* ---- functions -------------------------------------------------------------- */
+
+typedef struct pcd_model pcd_model;  /* opaque, library-owned host object */
+typedef struct pcd_state pcd_state;  /* opaque: a prefilled prefix over a caller-owned KV buffer */
+
+/* Bytes of device workspace a model with this config and these limits needs.
+ * Returns 0 on invalid arguments. */
+size_t pcd_workspace_bytes(const pcd_config *cfg, const pcd_limits *lim);
+
+/* Create a model over caller-owned device weights and a caller-owned device
+ * workspace of ws_bytes >= pcd_workspace_bytes(cfg, lim).  Uploads the RoPE
+ * cos/sin table (computed on the host in double precision, stored as fp32)
+ * into the workspace on `stream`.  The weights are only read, never written. */
+int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w,
+                     void *workspace, size_t ws_bytes, void *stream, pcd_model **out);
+
+/* Bytes of the KV buffer a state of n_tokens needs:
+ * n_tokens x n_layers x 2 (K, V) x n_kv_heads x head_dim x element size
+ * ("Parallel Constrained Decoding from Scratch", "the KV cache").
+ * Layout: [layer][K|V][kv head][token][head_dim], K after RoPE. */
+size_t pcd_state_bytes(const pcd_model *m, int32_t n_tokens);
+
+/* Prefill: one causal pass of the decoder over tokens[0..n_tokens) (host
+ * array) at positions 0..n_tokens-1, writing every layer's K and V into the
+ * caller's device buffer kv_buf (kv_bytes >= pcd_state_bytes).  No final norm
+ * and no LM head are run ("The idea: parallel constrained decoding", step 1:
+ * the shared prompt is read once).  On success *out is a new state handle
+ * that borrows kv_buf. */
+int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n_tokens, void *kv_buf, size_t kv_bytes,
+                void *stream, pcd_state **out);
+
+/* Decide every field of one request against a prefilled state in ONE batched
+ * decoder pass.  Each field's row is its scaffold, placed right after the
+ * state's prefix (positions P, P+1, ...).  Candidates whose leading tokens
+ * are shared by other candidates are extended by teacher-forced continuation
+ * tokens in the same pass (a trie per field); a candidate's logscore sums
+ * log p(token | prefix + scaffold + earlier tokens) over its tokens up to and
+ * including the first one no other candidate shares.  cand_prob is
+ * softmax(logscore / temperature) over the field, field_mass the
+ * full-vocabulary probability of the field's distinct first tokens at the
+ * scaffold's end (temperature 1).  The state's KV buffer is read, never
+ * written, so any number of decide calls may share one state. */
+int pcd_decide(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pcd_candidate *candidates,
+               int32_t n_candidates, float temperature, pcd_outputs *out, void *stream);
+
+/* Several requests, each on its own state, in ONE batched pass; outs[i]
+ * receives request i's results (arrays indexed within that request). */
+int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float temperature,
+                    pcd_outputs *outs, void *stream);
+
+/* Plan of a decide call over requests with the given prefix lengths, without
+ * any device work (the branch-token layout, readouts and gathers the batched
+ * pass uses).  Fills the counts; fills each non-NULL array. */
+int pcd_debug_plan(int32_t vocab_size, int32_t max_seq, int32_t n_req, const int32_t *prefix_lens,
+                   const pcd_request *reqs, pcd_plan_info *info);
+
+int pcd_get_stats(const pcd_model *m, pcd_stats *out);
+
+/* Per-kernel timing (for measurement; off by default).  With timing on, every
+ * launch of the classes below is bracketed by a pair of hipEvents on the
+ * call's stream, and after each call the elapsed times are added to
+ * per-class totals.  Enabling resets the totals. */
+#define PCD_KC_PREFILL_QKV 0     /* prefill: QKV projection + RoPE + KV write */
+#define PCD_KC_PREFILL_ATTN 1    /* prefill: causal attention */
+#define PCD_KC_PREFILL_O 2       /* prefill: O projection + residual */
+#define PCD_KC_PREFILL_GATEUP 3  /* prefill: gate/up projection + SwiGLU */
+#define PCD_KC_PREFILL_DOWN 4    /* prefill: down projection + residual */
+#define PCD_KC_BRANCH_QKV 5
+#define PCD_KC_BRANCH_ATTN 6     /* branch: shared-prefix attention over the prefix */
+#define PCD_KC_BRANCH_TAIL 7     /* branch: split merge + scaffold/trie-ancestor keys */
+#define PCD_KC_BRANCH_O 8
+#define PCD_KC_BRANCH_GATEUP 9
+#define PCD_KC_BRANCH_DOWN 10
+#define PCD_KC_READOUT_LMHEAD 11 /* LM head with online log-sum-exp and candidate gather */
+#define PCD_KC_OTHER 12          /* embedding, RMSNorm, log-sum-exp merge, combine */
+#define PCD_KC_COUNT 13
+
+int pcd_set_kernel_timing(pcd_model *m, int32_t enable);
+/* total_ms[PCD_KC_COUNT] and launches[PCD_KC_COUNT], host arrays. */
+int pcd_get_kernel_times(const pcd_model *m, float *total_ms, int64_t *launches);
+
+/* NULL-safe.  A state must be freed before its model. */
+void pcd_free_state(pcd_state *s);
+void pcd_free_model(pcd_model *m);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *pcd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

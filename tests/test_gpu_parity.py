@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case runs the same seeded inputs through the library (libpcd.so on
+cuda:0) and through the fp64 oracle, and compares readout log-sum-exps,
+gathered candidate logits, candidate log-scores and probabilities, candidate
+mass and argmax.  Integer work (the plan) is checked bit-exactly on the CPU
+(test_host.py); here the plan's effect is checked through the outputs.
+
+Tolerances (GPU minus fp64 oracle on the same weights):
+  fp32 model:  lse, z, logscore <= 1e-4 abs;  prob <= 1e-5 abs;  mass <= 1e-4 rel
+  bf16 models: lse, z <= 2.5e-2 abs; logscore <= 2.5e-2 x path length;
+               prob <= 1.25e-2 abs; mass <= 5e-2 rel
+  argmax equal unless the oracle's top-2 margin is under 0.05 nats (two
+  logits each off by the 2.5e-2 bound can swap at most that margin).
+The bf16 bounds come from rounding the GEMM inputs (normalised activations,
+attention outputs, SwiGLU outputs) and the KV cache to bf16, a relative
+error of 2^-9 per element; over 2 to 28 layers the measured spread is well
+inside them.
+"""
+import numpy as np
+import pytest
+
+import pcd_inputs as pi
+from oracle import decoder as odec
+from oracle import pcd as opcd
+
+cpd = pytest.importorskip("constrained_decoding_pcd_amd")
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {
+    "f32": dict(z=1e-4, ls=1e-4, prob=1e-5, mass=1e-4),
+    "bf16": dict(z=2.5e-2, ls=2.5e-2, prob=1.25e-2, mass=5e-2),
+}
+MARGIN_WAIVER = 0.05
+
+
+def _model(shape, weights, requests, max_prefill=0):
+    dev = cpd.upload_weights(weights.mats, shape.n_layers, shape.d_model, "cuda:0")
+    lens = [len(p) for p, _ in requests]
+    lim = cpd.limits_for(shape.vocab_size, shape.max_seq, lens, [f for _, f in requests], max_prefill)
+    return cpd.PcdModel(cpd.config_of(shape), dev, lim)
+
+
+def _compare(name, got, ref, plan_paths, dtype, label=""):
+    """got: list of per-request dicts from the library; ref: oracle result."""
+    tol = TOL[dtype]
+    lse = np.concatenate([g["lse"] for g in got])
+    z = np.concatenate([g["z"] for g in got])
+    prob = np.concatenate([g["prob"] for g in got])
+    ls = np.concatenate([g["logscore"] for g in got])
+    mass = np.concatenate([g["mass"] for g in got])
+    arg = np.concatenate([g["argmax"] for g in got])
+    rprob = np.concatenate([f.prob for f in ref.fields])
+    rls = np.concatenate([f.logscore for f in ref.fields])
+    rmass = np.array([f.mass for f in ref.fields])
+    plen = np.diff(plan_paths)
+    d = {
+        "lse": float(np.max(np.abs(lse - ref.lse))),
+        "z": float(np.max(np.abs(z - ref.z))),
+        "ls/len": float(np.max(np.abs(ls - rls) / plen)),
+        "prob": float(np.max(np.abs(prob - rprob))),
+        "mass_rel": float(np.max(np.abs(mass - rmass) / rmass)),
+    }
+    print(f"[{name}{label}] max errors: " + ", ".join(f"{k} {v:.3e}" for k, v in d.items()), flush=True)
+    assert d["lse"] <= tol["z"] and d["z"] <= tol["z"]
+    assert d["ls/len"] <= tol["ls"]
+    assert d["prob"] <= tol["prob"]
+    assert d["mass_rel"] <= tol["mass"]
+    for i, f in enumerate(ref.fields):
+        if f.margin >= MARGIN_WAIVER:
+            assert int(arg[i]) == f.argmax, (i, f.margin)
+    # invariants of every field
+    off = 0
+    for g in got:
+        assert np.all(g["mass"] <= 1.0 + 1e-6) and np.all(g["mass"] > 0)
+    for f in ref.fields:
+        k = len(f.prob)
+        assert abs(float(prob[off:off + k].sum()) - 1.0) <= 1e-6
+        off += k
+
+
+def _run_case(name, shape, weights, requests, temperature=1.0, dec=None):
+    print(f"case {name}: {len(requests)} request(s), prefixes {[len(p) for p, _ in requests]}", flush=True)
+    m = _model(shape, weights, requests)
+    states = [m.prefill(p) for p, _ in requests]
+    got = m.decide_many(states, [f for _, f in requests], temperature, debug=True)
+    dec = dec or odec.Decoder(weights, np.float64)
+    ref = opcd.decide(dec, requests, temperature)
+    _compare(name, got, ref, ref.plan.c_path_off, shape.dtype)
+    for s in states:
+        s.close()
+    m.close()
+    return got, ref
+
+
+@pytest.fixture(scope="module")
+def tiny_w():
+    return pi.make_weights(pi.SHAPES["tiny"], 1000)
+
+
+@pytest.fixture(scope="module")
+def tiny_dec(tiny_w):
+    return odec.Decoder(tiny_w, np.float64)
+
+
+def _reqs(wl):
+    return [(r.prefix, r.fields) for r in wl.requests]
+
+
+def test_tiny_cfg0(tiny_w, tiny_dec):
+    wl = pi.make_workload("cfg0")
+    _run_case("cfg0", wl.shape, tiny_w, _reqs(wl), dec=tiny_dec)
+
+
+def test_tiny_cfg0_trie(tiny_w, tiny_dec):
+    wl = pi.make_workload("cfg0t")
+    _run_case("cfg0t", wl.shape, tiny_w, _reqs(wl), dec=tiny_dec)
+
+
+@pytest.mark.parametrize("temperature", [0.5, 2.0])
+def test_tiny_temperature(tiny_w, tiny_dec, temperature):
+    wl = pi.make_workload("cfg0t")
+    _run_case(f"cfg0t-T{temperature}", wl.shape, tiny_w, _reqs(wl), temperature, dec=tiny_dec)
+
+
+def test_tiny_ragged_multi_request_deep_tries(tiny_w, tiny_dec):
+    """Three requests in one branch pass, prefixes of 1, 65 and 130 tokens
+    (below, above and across the 64-key tile), deep random tries."""
+    V = pi.SHAPES["tiny"].vocab_size
+    rng = np.random.default_rng(5)
+    reqs = []
+    for k, P in enumerate((1, 65, 130)):
+        prefix = [int(t) for t in rng.integers(0, V, size=P)]
+        reqs.append((prefix, pi.random_trie_fields(700 + k, V, 4, max_cands=12, max_len=4)))
+    _run_case("tiny-multi", pi.SHAPES["tiny"], tiny_w, reqs, dec=tiny_dec)
+
+
+def test_tiny_prefill_kv(tiny_w, tiny_dec):
+    """The state's KV buffer holds every layer's K (after RoPE) and V of the
+    prefix, [layer][K|V][kv head][token][head_dim]."""
+    sh = pi.SHAPES["tiny"]
+    wl = pi.make_workload("cfg0")
+    prefix = wl.requests[0].prefix
+    m = _model(sh, tiny_w, _reqs(wl))
+    st = m.prefill(prefix)
+    kv = st.kv.view(torch.float32).cpu().numpy().reshape(sh.n_layers, 2, sh.n_kv_heads, len(prefix), sh.head_dim)
+    ref = opcd.prefill(tiny_dec, prefix)
+    err = max(float(np.max(np.abs(kv[l, i] - ref[l][i]))) for l in range(sh.n_layers) for i in range(2))
+    print(f"[prefill-kv] max abs error {err:.3e}", flush=True)
+    assert err < 1e-4
+    st.close()
+    m.close()
+
+
+def test_tiny_invariants(tiny_w):
+    """One prefill + one branch pass per request; decide never writes the
+    state's KV; results are bit-identical from run to run."""
+    wl = pi.make_workload("cfg0t")
+    reqs = _reqs(wl)
+    m = _model(wl.shape, tiny_w, reqs)
+    st = m.prefill(reqs[0][0])
+    kv0 = st.kv.clone()
+    a = m.decide(st, reqs[0][1], debug=True)
+    b = m.decide(st, reqs[0][1], debug=True)
+    assert torch.equal(kv0, st.kv)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    s = m.stats()
+    assert s["prefill_passes"] == 1 and s["branch_passes"] == 2
+    plan = cpd.debug_plan(wl.shape.vocab_size, wl.shape.max_seq, [len(reqs[0][0])], [reqs[0][1]])
+    assert s["last_branch_tokens"] == len(plan["tok"]) and s["last_readouts"] == len(plan["ro_tok"])
+    st.close()
+    m.close()
+
+
+def test_tiny_errors_before_device_work(tiny_w):
+    wl = pi.make_workload("cfg0")
+    reqs = _reqs(wl)
+    m = _model(wl.shape, tiny_w, reqs)
+    st = m.prefill(reqs[0][0])
+    bad = [pi.Field([1, 2], [[3], [3]])]
+    with pytest.raises(cpd.PcdError) as e:
+        m.decide(st, bad)
+    assert e.value.name == "DUP"
+    with pytest.raises(cpd.PcdError) as e:
+        m.prefill([0, 1, 99999])
+    assert e.value.name == "TOKEN"
+    with pytest.raises(cpd.PcdError) as e:
+        m.decide(st, reqs[0][1], temperature=0.0)
+    assert e.value.name == "ARG"
+    # the model still works after rejected calls
+    got = m.decide(st, reqs[0][1])
+    assert np.all(np.isfinite(got["prob"]))
+    st.close()
+    m.close()
+
+
+# ---------------------------------------------------------------------------
+# Qwen2.5-1.5B widths in bf16
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def q15_l2():
+    sh = pi.SHAPES["qwen2.5-1.5b"]
+    w = pi.make_weights(sh, 1001, n_layers=2)
+    return w.shape, w, odec.Decoder(w, np.float64)
+
+
+def test_bf16_two_layer_cfg1(q15_l2):
+    """The 28-field workload (512-token prefix) on the first 2 layers of the
+    1.5B-shaped model: every output of every field."""
+    sh, w, dec = q15_l2
+    _run_case("q15-L2-cfg1", sh, w, _reqs(pi.make_workload("cfg1")), dec=dec)
+
+
+def test_bf16_two_layer_cfg2_id_field(q15_l2):
+    """2048-token prefix; 3 booleans and one 255-option 3-token ID field whose
+    options share their lead token (18 trie readouts)."""
+    sh, w, dec = q15_l2
+    _run_case("q15-L2-cfg2", sh, w, _reqs(pi.make_workload("cfg2")), dec=dec)
+
+
+def test_bf16_two_layer_batched_requests(q15_l2):
+    """Four requests of the throughput workload (1024-token prefixes, 28
+    fields each) in one branch pass."""
+    sh, w, dec = q15_l2
+    wl = pi.make_workload("cfg3")
+    _run_case("q15-L2-cfg3x4", sh, w, [(r.prefix, r.fields) for r in wl.requests[:4]], dec=dec)

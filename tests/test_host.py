@@ -1,0 +1,117 @@
+"""Host-side checks of the C-ABI library (no device work).
+
+The library's plan builder (C++) must equal the oracle's plan element by
+element, and reject the same invalid inputs with the same error codes.
+"""
+import ctypes
+import re
+import os
+
+import numpy as np
+import pytest
+
+import pcd_inputs as pi
+from oracle import plan as oplan
+
+cpd = pytest.importorskip("constrained_decoding_pcd_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cpd.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "pcd.h")).read()
+    declared = set(re.findall(r"\b(pcd_[a-z_]+)\s*\(", hdr))
+    assert declared == set(cpd.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _compare_plans(requests, V, max_seq=1 << 20):
+    lens = [len(p) for p, _ in requests]
+    ours = cpd.debug_plan(V, max_seq, lens, [f for _, f in requests])
+    ref = oplan.build_plan([(len(p), f) for p, f in requests], V)
+    names = {"field": "tfield"}
+    for k, v in ours.items():
+        r = getattr(ref, names.get(k, k))
+        assert v.dtype == np.int32
+        assert np.array_equal(v, r), k
+
+
+@pytest.mark.parametrize("name", ["cfg0", "cfg0t", "cfg1", "cfg2"])
+def test_plan_equals_oracle_on_workloads(name):
+    wl = pi.make_workload(name)
+    _compare_plans([(r.prefix, r.fields) for r in wl.requests], wl.shape.vocab_size)
+
+
+def test_plan_equals_oracle_multi_request():
+    wl = pi.make_workload("cfg3")
+    reqs = [(r.prefix, r.fields) for r in wl.requests[:5]]
+    _compare_plans(reqs, wl.shape.vocab_size)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_equals_oracle_random_tries(seed):
+    V = 5000
+    rng = np.random.default_rng(seed)
+    reqs = []
+    for r in range(1 + seed % 3):
+        prefix = [int(t) for t in rng.integers(0, V, size=int(rng.integers(1, 50)))]
+        reqs.append((prefix, pi.random_trie_fields(100 * seed + r, V, 5, max_cands=20, max_len=5)))
+    _compare_plans(reqs, V)
+
+
+def test_plan_id_field_with_255_options():
+    wl = pi.make_workload("cfg2")
+    r = wl.requests[0]
+    plan = cpd.debug_plan(wl.shape.vocab_size, 1 << 20, [len(r.prefix)], [r.fields])
+    assert len(plan["ro_tok"]) == 21 and len(plan["g_tok"]) == 278
+
+
+@pytest.mark.parametrize("bad,code", [
+    (pi.Field([], [[1], [2]]), "EMPTY"),
+    (pi.Field([3], [[1]]), "NCAND"),
+    (pi.Field([3], [[i] for i in range(256)]), "NCAND"),
+    (pi.Field([3], [[1], []]), "EMPTY"),
+    (pi.Field([3], [[1], [1]]), "DUP"),
+    (pi.Field([3], [[1], [1, 2]]), "PREFIX"),
+    (pi.Field([3], [[1], [5000]]), "TOKEN"),
+    (pi.Field([-1], [[1], [2]]), "TOKEN"),
+])
+def test_plan_rejects_like_the_oracle(bad, code):
+    with pytest.raises(oplan.PlanError) as e:
+        oplan.build_plan([(4, [bad])], 1000)
+    assert e.value.code == code
+    with pytest.raises(cpd.PcdError) as e2:
+        cpd.debug_plan(1000, 1 << 20, [4], [[bad]])
+    assert e2.value.name == code
+
+
+def test_positions_beyond_max_seq_are_rejected():
+    f = pi.Field([1, 2, 3], [[4, 5], [4, 6]])
+    cpd.debug_plan(1000, 10, [5], [[f]])         # last position 5 + 3 + 1 - 1 = 8 < 10
+    with pytest.raises(cpd.PcdError) as e:
+        cpd.debug_plan(1000, 8, [5], [[f]])
+    assert e.value.name == "CAP"
+
+
+def test_workspace_bytes_rejects_bad_configs(lib):
+    good = dict(n_layers=2, d_model=128, n_heads=4, n_kv_heads=2, head_dim=32, ffn_dim=384, vocab_size=2048,
+                max_seq=512, rope_theta=1e4, rms_eps=1e-6, tied_lm_head=1, dtype=0)
+    lim = cpd.binding.pcd_limits(256, 64, 16, 64, 8, 32, 2)
+    assert lib.pcd_workspace_bytes(ctypes.byref(cpd.binding.pcd_config(**good)), ctypes.byref(lim)) > 0
+    for k, v in (("head_dim", 48), ("n_kv_heads", 3), ("d_model", 100), ("dtype", 7), ("vocab_size", 2000)):
+        bad = dict(good, **{k: v})
+        assert lib.pcd_workspace_bytes(ctypes.byref(cpd.binding.pcd_config(**bad)), ctypes.byref(lim)) == 0
+
+
+def test_null_arguments_are_rejected(lib):
+    assert lib.pcd_decide_many(None, None, 0, 1.0, None, None) == -1
+    assert lib.pcd_prefill(None, None, 0, None, 0, None, None) == -1
+    assert b"null" in lib.pcd_last_error()
+    lib.pcd_free_state(None)
+    lib.pcd_free_model(None)
