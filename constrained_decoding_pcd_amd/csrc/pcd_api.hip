@@ -176,23 +176,8 @@ namespace {
 
 size_t esize(const pcd_model *m) { return m->cfg.dtype == PCD_DTYPE_F32 ? 4 : 2; }
 
-// choose split-K for a GEMM whose epilogue adds into the residual stream
-int splitk_for(const pcd_model *m, int M, int N, int K) {
-    const int kt = gemm_k_tile(m->cfg.dtype);
-    const int tiles = (M + 63) / 64 * (N / 64);
-    if (tiles >= 192 || M > SPLITK_ROWS) return 1;
-    int best = 1;
-    for (int s = 2; s <= SPLITK_MAX; ++s) {
-        if (K % (s * kt) || K / s < 2 * kt) continue;
-        best = s;
-        if (tiles * s >= 256) break;
-    }
-    return best;
-}
-
-bool big_tile(int M, int N) { return ((M + 127) / 128) * (N / 128) >= 256; }
-
-// O projection or down projection into the residual stream
+// O projection or down projection into the residual stream (split-K inside
+// gemm() when the tile count is too small for the chip)
 bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W, hipStream_t st) {
     GemmCall c{};
     c.dt = m->cfg.dtype;
@@ -202,20 +187,11 @@ bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W,
     c.K = K;
     c.B[0].ptr[0] = W;
     c.B[0].nseg = 1;
-    float *x = reinterpret_cast<float *>(m->ws + m->L.x);
-    const int s = splitk_for(m, M, N, K);
-    if (s > 1) {
-        c.epi = Epi::Partial;
-        c.splits = s;
-        c.part = reinterpret_cast<float *>(m->ws + m->L.splitk);
-        if (!gemm(c, st)) return false;
-        splitk_reduce(c.part, s, M, N, x, st);
-        return true;
-    }
     c.epi = Epi::Resid;
-    c.splits = 1;
-    c.x = x;
-    c.big = big_tile(M, N);
+    c.x = reinterpret_cast<float *>(m->ws + m->L.x);
+    c.part = reinterpret_cast<float *>(m->ws + m->L.splitk);
+    c.part_cap = (size_t)SPLITK_MAX * std::min(std::max(m->lim.max_prefill_tokens, m->lim.max_branch_tokens),
+                                               SPLITK_ROWS) * m->cfg.d_model;
     return gemm(c, st);
 }
 
@@ -249,7 +225,6 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     g.B[0].begin[2] = nq + nk;
     g.B[0].nseg = 3;
     g.epi = Epi::Qkv;
-    g.splits = 1;
     g.out = q;
     g.kc = kc;
     g.vc = vc;
@@ -281,9 +256,7 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     f.B[1].ptr[0] = m->wu[l];
     f.B[1].nseg = 1;
     f.epi = Epi::SwiGlu;
-    f.splits = 1;
     f.out = act;
-    f.big = big_tile(M, c.ffn_dim);
     m->tbegin(K_GU, st);
     if (!gemm(f, st)) return fail(PCD_E_ARG, "gate/up projection: unsupported shape");
     m->tend(st);
@@ -663,7 +636,6 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     g.B[0].ptr[0] = m->head;
     g.B[0].nseg = 1;
     g.epi = Epi::Readout;
-    g.splits = 1;
     g.ro_part = ro_part;
     g.g_tok = d_gtok;
     g.g_ro = d_gro;

@@ -22,7 +22,7 @@ struct BSegs {
 enum class Epi : int {
     Qkv,      // RoPE on q and k, q -> q buffer, k and v -> a KV cache
     Resid,    // x[m][n] += c   (fp32 residual stream)
-    Partial,  // split-K partial sums -> part[split][m][n]
+    Partial,  // split-K partial sums -> part[split][m][n] (chosen inside gemm() for Resid)
     SwiGlu,   // two B operands: out[m][n] = silu(c_gate) * c_up
     Readout,  // per-row (max, sum exp) of the tile + gathered candidate logits
 };
@@ -33,10 +33,10 @@ struct GemmCall {
     int32_t M, N, K;
     BSegs B[2];      // B[1] used by SwiGlu only
     Epi epi;
-    int splits;      // Partial only; K / splits must be a multiple of the k-tile
     // epilogue arguments
     float *x;        // Resid: residual [M][N]
-    float *part;     // Partial: [splits][M][N]
+    float *part;     // Resid: scratch for split-K partial sums (NULL: never split)
+    size_t part_cap; // floats available at part
     void *out;       // SwiGlu: [M][N] of dt;  Qkv: q buffer [M][Hq][hd]
     void *kc, *vc;   // Qkv: K and V cache of this layer, [Hkv][cap][hd] each
     int32_t cap;     // Qkv: tokens per KV head in the cache
@@ -47,7 +47,6 @@ struct GemmCall {
     const int32_t *g_tok, *g_ro;  // Readout: gathered token ids and their readout rows
     int32_t n_gather;
     float *g_logit;          // Readout: [n_gather]
-    bool big;                // prefer the 128x128 tile (large M)
 };
 
 // Returns false (and does nothing) on a shape the kernels do not support.

@@ -93,6 +93,16 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
 // GEMM  C[M][N] = A[M][K] . B[N][K]^T  with a fused epilogue
+//
+// Both operands stream through an S-stage ring of LDS tiles, filled straight
+// from global memory by gfx950's global_load_lds_dwordx4 (each lane's 16
+// bytes land at M0 + 16*lane), so S-1 k-tiles are in flight while the
+// matrix cores work on the current one and no registers stage the copies.
+// A tile row holds 128 bytes of K (8 chunks of 16 B); chunk c of row r is
+// stored in slot c ^ (r % 8) of that row, which makes the 16-byte fragment
+// reads of 8 consecutive rows hit 8 disjoint bank groups.  One barrier per
+// k-tile: after it, every wave has finished the previous tile, whose slot is
+// then refilled.
 // ---------------------------------------------------------------------------
 template <int NB> struct GemmArgs {
     const void *A;
@@ -115,29 +125,50 @@ struct EpiArgs {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-template <typename T, int BM, int BN, int WM, int WN, int NB, Epi E>
+// 16 bytes per lane from global memory into LDS at lds_addr + 16 * lane.
+// Issued from inline assembly so that the compiler does not add a wait for
+// it before every LDS read; completion is tracked by vm_wait below.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N> __device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// workgroup barrier that does not wait for in-flight global loads
+__device__ __forceinline__ void barrier_keep_loads() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <typename T, int BM, int BN, int NB, Epi E> struct GemmLds {
+    static constexpr bool LDS_EPI = (E == Epi::Qkv || E == Epi::Readout);
+    static constexpr int STAGE = (BM + NB * BN) * 128;
+    static constexpr int C_BYTES = LDS_EPI ? BM * (BN + 4) * 4 : 0;
+    static int bytes(int S) { return S * STAGE > C_BYTES ? S * STAGE : C_BYTES; }
+};
+
+template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
-    constexpr int BK = 128 / sizeof(T);        // 128 bytes of K per row per stage
-    constexpr int PAD = 16 / sizeof(T);
-    constexpr int LDK = BK + PAD;
-    constexpr int CH = 16 / sizeof(T);         // elements per 16-byte chunk
-    constexpr int CPR = BK / CH;               // chunks per row (8)
-    constexpr int A_CH = BM * CPR / 256;
-    constexpr int B_CH = BN * CPR / 256;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
+    constexpr int BK = 8 * CH;          // K elements per stage (128 bytes per row)
+    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + NB * B_BYTES;
+    constexpr int A_INS = BM / 32, B_INS = BN / 32;  // DMA instructions per wave per stage
+    constexpr int LPS = A_INS + NB * B_INS;           // ... in total
+    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16;
     constexpr int KSTEPS = BK / 32;
-    constexpr bool LDS_EPI = (E == Epi::Qkv || E == Epi::Readout);
-    constexpr int AB_BYTES = (BM + NB * BN) * LDK * (int)sizeof(T);
-    constexpr int C_BYTES = LDS_EPI ? BM * (BN + 4) * 4 : 0;
-    constexpr int LDS_BYTES = AB_BYTES > C_BYTES ? AB_BYTES : C_BYTES;
-    static_assert(A_CH * 256 == BM * CPR && B_CH * 256 == BN * CPR, "tile/thread mismatch");
-    __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
-    T *As = reinterpret_cast<T *>(lds_raw);
+    constexpr int CPL = 8 / CH;  // chunks holding one lane's 8 k-elements
+    constexpr bool LDS_EPI = GemmLds<T, BM, BN, NB, E>::LDS_EPI;
+    static_assert(WM * WN == 4 && BM % 32 == 0 && BN % 32 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
+    static_assert(S >= 2 && S <= 4 && (S - 2) * LPS < 64, "pipeline depth");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
 
     // XCD-aware tile order: consecutive workgroups land on different XCDs, so
-    // hand each XCD a contiguous range of tiles (m fastest) and the tiles that
-    // share a B slab run on one XCD and share its L2.
+    // hand each XCD a contiguous range of tiles (m fastest): tiles that share
+    // a B slab run on one XCD and share its L2.
     const int b = blockIdx.x;
     const int t = (b & 7) * g.per_xcd + (b >> 3);
     if (t >= g.total) return;
@@ -153,52 +184,46 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
     const int wm = w % WM, wn = w / WM;
     const int lr = lane & 15, lg = lane >> 4;
 
+    // DMA sources: slot p = (i*4 + w)*64 + lane of a tile is row p/8, chunk (p%8) ^ (row%8)
     const T *A = reinterpret_cast<const T *>(g.A);
-    uint4 ra[A_CH], rb[NB][B_CH];
-    const T *bptr[NB][B_CH];
-    const T *aptr[A_CH];
-    bool aval[A_CH];
+    const char *asrc[A_INS];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
-        const int m = m0 + row;
-        aval[i] = m < g.M;
-        aptr[i] = A + (size_t)(aval[i] ? m : 0) * g.K + kbeg + kc;
+    for (int i = 0; i < A_INS; ++i) {
+        const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
+        const int m = min(m0 + r, g.M - 1);  // rows past M load row M-1; their results are dropped
+        asrc[i] = reinterpret_cast<const char *>(A + (size_t)m * g.K + kbeg + c * CH);
     }
+    const char *bsrc[NB][B_INS];
 #pragma unroll
     for (int q = 0; q < NB; ++q)
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
-            const int n = n0 + row;
-            const BSegs &s = g.B[q];
-            const int sg = (s.nseg > 2 && n >= s.begin[2]) ? 2 : ((s.nseg > 1 && n >= s.begin[1]) ? 1 : 0);
-            bptr[q][i] = reinterpret_cast<const T *>(s.ptr[sg]) + (size_t)(n - s.begin[sg]) * g.K + kbeg + kc;
+        for (int i = 0; i < B_INS; ++i) {
+            const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
+            const int n = n0 + r;
+            const BSegs &sg = g.B[q];
+            const int s = (sg.nseg > 2 && n >= sg.begin[2]) ? 2 : ((sg.nseg > 1 && n >= sg.begin[1]) ? 1 : 0);
+            bsrc[q][i] = reinterpret_cast<const char *>(reinterpret_cast<const T *>(sg.ptr[s]) +
+                                                         (size_t)(n - sg.begin[s]) * g.K + kbeg + c * CH);
         }
-
-    auto gload = [&](int kt) {
-        const int ko = kt * BK;
+    auto issue = [&](int kt) {
+        const uint32_t sb = lds_base + (uint32_t)((kt % S) * STAGE);
+        const size_t ko = (size_t)kt * 128;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            ra[i] = aval[i] ? *reinterpret_cast<const uint4 *>(aptr[i] + ko) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + ko, sb + (uint32_t)((i * 4 + w) * 1024));
 #pragma unroll
         for (int q = 0; q < NB; ++q)
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i) rb[q][i] = *reinterpret_cast<const uint4 *>(bptr[q][i] + ko);
+            for (int i = 0; i < B_INS; ++i)
+                dma16(bsrc[q][i] + ko, sb + (uint32_t)(A_BYTES + q * B_BYTES + (i * 4 + w) * 1024));
     };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
-            *reinterpret_cast<uint4 *>(As + row * LDK + kc) = ra[i];
+    auto frag = [&](Frag<T> &f, const char *tile, int row, int chunk) {
+        const char *p0 = tile + (row * 8 + (chunk ^ (row & 7))) * 16;
+        if constexpr (CPL == 1) {
+            ld8(f, reinterpret_cast<const T *>(p0));
+        } else {
+            const char *p1 = tile + (row * 8 + ((chunk + 1) ^ (row & 7))) * 16;
+            ld4x2(f, reinterpret_cast<const T *>(p0), reinterpret_cast<const T *>(p1));
         }
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-#pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int c = tid + i * 256, row = c / CPR, kc = (c % CPR) * CH;
-                *reinterpret_cast<uint4 *>(As + (BM + q * BN + row) * LDK + kc) = rb[q][i];
-            }
     };
 
     f32x4 acc[NB][FM][FN];
@@ -209,31 +234,38 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    gload(0);
-    lstore();
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if (s < nkt) issue(s);
     for (int kt = 0; kt < nkt; ++kt) {
-        if (kt + 1 < nkt) gload(kt + 1);
+        const int ahead = min(S - 2, nkt - 1 - kt);  // stages after kt already in flight
+        if constexpr (S == 4) {
+            if (ahead >= 2) vm_wait<2 * LPS>();
+            else if (ahead == 1) vm_wait<LPS>();
+            else vm_wait<0>();
+        } else if constexpr (S == 3) {
+            if (ahead >= 1) vm_wait<LPS>();
+            else vm_wait<0>();
+        } else {
+            vm_wait<0>();
+        }
+        barrier_keep_loads();
+        if (kt + S - 1 < nkt) issue(kt + S - 1);
+        const char *st = lds + (kt % S) * STAGE;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             Frag<T> fa[FM];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) ld8(fa[i], As + (wm * WTM + i * 16 + lr) * LDK + s * 32 + lg * 8);
+            for (int i = 0; i < FM; ++i) frag(fa[i], st, wm * WTM + i * 16 + lr, s * 4 * CPL + lg * CPL);
 #pragma unroll
-            for (int q = 0; q < NB; ++q) {
+            for (int q = 0; q < NB; ++q)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     Frag<T> fb;
-                    ld8(fb, As + (BM + q * BN + wn * WTN + j * 16 + lr) * LDK + s * 32 + lg * 8);
+                    frag(fb, st + A_BYTES + q * B_BYTES, wn * WTN + j * 16 + lr, s * 4 * CPL + lg * CPL);
 #pragma unroll
                     for (int i = 0; i < FM; ++i) mma(acc[q][i][j], fa[i], fb);
                 }
-            }
-        }
-        __syncthreads();
-        if (kt + 1 < nkt) {
-            lstore();
-            __syncthreads();
         }
     }
 
@@ -257,8 +289,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
                     }
                 }
     } else {
-        // stage the fp32 tile in LDS (the operand tiles are dead after the last barrier)
-        float *Cs = reinterpret_cast<float *>(lds_raw);
+        // stage the fp32 tile in LDS once every wave is done with the operand tiles
+        __syncthreads();
+        float *Cs = reinterpret_cast<float *>(lds);
         constexpr int LDC = BN + 4;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -321,8 +354,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
     }
 }
 
-template <typename T, int BM, int BN, int NB, Epi E>
-static void launch_gemm(const GemmCall &c, hipStream_t st) {
+template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E>
+static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     constexpr int BK = 128 / sizeof(T);
     GemmArgs<NB> g;
     g.A = c.A;
@@ -332,11 +365,11 @@ static void launch_gemm(const GemmCall &c, hipStream_t st) {
     g.K = c.K;
     g.tiles_m = (c.M + BM - 1) / BM;
     g.tiles_n = c.N / BN;
-    g.splits = (E == Epi::Partial) ? c.splits : 1;
-    g.k_per_split = c.K / g.splits;
-    (void)BK;
+    g.splits = splits;
+    g.k_per_split = c.K / splits;
     g.total = g.tiles_m * g.tiles_n * g.splits;
     g.per_xcd = (g.total + 7) / 8;
+    static_assert(BK > 0, "");
     EpiArgs e;
     e.x = c.x;
     e.part = c.part;
@@ -354,42 +387,73 @@ static void launch_gemm(const GemmCall &c, hipStream_t st) {
     e.g_ro = c.g_ro;
     e.n_gather = c.n_gather;
     e.g_logit = c.g_logit;
-    hipLaunchKernelGGL((k_gemm<T, BM, BN, 2, 2, NB, E>), dim3(g.per_xcd * 8), dim3(256), 0, st, g, e);
+    const int shmem = GemmLds<T, BM, BN, NB, E>::bytes(S);
+    auto kern = k_gemm<T, BM, BN, WM, WN, NB, S, E>;
+    static bool attr_set = false;  // one model per thread at a time; a repeated set is harmless
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  shmem);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(g.per_xcd * 8), dim3(256), shmem, st, g, e);
+}
+
+enum class Reg { Small, Medium, Big };
+static Reg regime(int M) { return M >= 384 ? Reg::Big : (M > 48 ? Reg::Medium : Reg::Small); }
+
+// split-K for an epilogue that adds into the residual stream: enough
+// workgroups for the chip, partial sums within the caller's buffer
+static int pick_splits(const GemmCall &c, int tiles, int BK) {
+    if (tiles >= 200 || !c.part) return 1;
+    int best = 1;
+    for (int s = 2; s <= 8; ++s) {
+        if (c.K % (s * BK) || c.K / s < 2 * BK || (size_t)s * c.M * c.N > c.part_cap) continue;
+        best = s;
+        if (tiles * s >= 240) break;
+    }
+    return best;
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int S>
+static void gemm_resid_cfg(const GemmCall &c, hipStream_t st) {
+    constexpr int BK = 128 / sizeof(T);
+    const int tiles = (c.M + BM - 1) / BM * (c.N / BN);
+    const int s = pick_splits(c, tiles, BK);
+    if (s > 1) {
+        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Partial>(c, s, st);
+        splitk_reduce(c.part, s, c.M, c.N, c.x, st);
+    } else {
+        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Resid>(c, 1, st);
+    }
 }
 
 template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
     constexpr int BK = 128 / sizeof(T);
-    const int splits = c.epi == Epi::Partial ? c.splits : 1;
-    if (c.M <= 0 || c.K % (BK * splits) != 0) return false;
+    if (c.M <= 0 || c.N % 128 || c.K % BK) return false;
+    const Reg rg = regime(c.M);
     switch (c.epi) {
         case Epi::Qkv:
-            if (c.N % 128 == 0 && 128 % c.hd == 0) {
-                launch_gemm<T, 64, 128, 1, Epi::Qkv>(c, st);
-                return true;
-            }
-            if (c.N % 64 == 0 && 64 % c.hd == 0) {
-                launch_gemm<T, 64, 64, 1, Epi::Qkv>(c, st);
-                return true;
-            }
-            return false;
+            if (128 % c.hd) return false;
+            if (rg == Reg::Small) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Qkv>(c, 1, st);
+            else launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Qkv>(c, 1, st);
+            return true;
         case Epi::Readout:
-            if (c.N % 128) return false;
-            launch_gemm<T, 64, 128, 1, Epi::Readout>(c, st);
+            if (rg == Reg::Small) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Readout>(c, 1, st);
+            else if (rg == Reg::Medium) launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Readout>(c, 1, st);
+            else launch_gemm<T, 128, 128, 2, 2, 1, 3, Epi::Readout>(c, 1, st);
             return true;
         case Epi::Resid:
-            if (c.N % 64) return false;
-            if (c.big && c.N % 128 == 0) launch_gemm<T, 128, 128, 1, Epi::Resid>(c, st);
-            else launch_gemm<T, 64, 64, 1, Epi::Resid>(c, st);
-            return true;
-        case Epi::Partial:
-            if (c.N % 64) return false;
-            launch_gemm<T, 64, 64, 1, Epi::Partial>(c, st);
+            if (rg == Reg::Small) gemm_resid_cfg<T, 32, 128, 1, 4, 4>(c, st);
+            else if (rg == Reg::Medium) gemm_resid_cfg<T, 64, 128, 2, 2, 4>(c, st);
+            else gemm_resid_cfg<T, 128, 128, 2, 2, 3>(c, st);
             return true;
         case Epi::SwiGlu:
-            if (c.N % 64) return false;
-            if (c.big && c.N % 128 == 0) launch_gemm<T, 128, 128, 2, Epi::SwiGlu>(c, st);
-            else launch_gemm<T, 64, 64, 2, Epi::SwiGlu>(c, st);
+            if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
+            else if (rg == Reg::Medium) launch_gemm<T, 64, 64, 2, 2, 2, 4, Epi::SwiGlu>(c, 1, st);
+            else launch_gemm<T, 128, 128, 2, 2, 2, 3, Epi::SwiGlu>(c, 1, st);
             return true;
+        case Epi::Partial:
+            return false;  // chosen internally by Resid
     }
     return false;
 }
