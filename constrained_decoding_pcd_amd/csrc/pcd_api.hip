@@ -44,7 +44,8 @@ struct Layout {
 
 int64_t plan_block_cap(const pcd_config &c, const pcd_limits &l) {
     const int grp = c.n_heads / c.n_kv_heads;
-    const int64_t pre = (int64_t)c.n_kv_heads * (((int64_t)l.max_prefill_tokens * grp + ATT_ROWS - 1) / ATT_ROWS);
+    const int64_t pre =
+        (int64_t)c.n_kv_heads * (((int64_t)l.max_prefill_tokens * grp + ATT_ROWS - 1) / ATT_ROWS) * MAX_SPLITS;
     const int64_t br = (int64_t)c.n_kv_heads *
                        (((int64_t)l.max_branch_tokens * grp + ATT_ROWS - 1) / ATT_ROWS + l.max_requests) * MAX_SPLITS;
     return std::max(pre, br);
@@ -71,8 +72,8 @@ Layout layout(const pcd_config &c, const pcd_limits &l) {
     L.act = take(rows * c.ffn_dim * esz);
     L.splitk = take((size_t)SPLITK_MAX * std::min(rows, (size_t)SPLITK_ROWS) * d * 4);
     L.kvb = take((size_t)c.n_layers * 2 * c.n_kv_heads * l.max_branch_tokens * c.head_dim * esz);
-    L.part_o = take((size_t)MAX_SPLITS * l.max_branch_tokens * hq * 4);
-    L.part_ml = take((size_t)MAX_SPLITS * l.max_branch_tokens * c.n_heads * sizeof(float2));
+    L.part_o = take((size_t)MAX_SPLITS * rows * hq * 4);
+    L.part_ml = take((size_t)MAX_SPLITS * rows * c.n_heads * sizeof(float2));
     L.hr = take((size_t)l.max_readouts * d * esz);
     L.ro_part = take((size_t)(c.vocab_size / 128) * l.max_readouts * sizeof(float2));
     L.lse = take((size_t)l.max_readouts * 4);
@@ -376,12 +377,24 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
             return fail(PCD_E_TOKEN, "token id " + std::to_string(tokens[i]) + " outside the vocabulary");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim;
-    // device tables: tokens, one request (this KV buffer), attention blocks
+    // device tables: tokens, one request (this KV buffer), attention blocks.
+    // Causal attention is split over the keys when there are too few 64-row
+    // blocks for the chip: split s covers keys [s*slen, (s+1)*slen), and only
+    // row blocks that reach key s*slen get a workgroup for it.
     std::vector<AttnBlock> blocks;
     const int rows = n * grp;
+    const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + ATT_ROWS - 1) / ATT_ROWS);
+    int want = (int)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, (1024 + row_blocks - 1) / row_blocks));
+    want = std::min(want, (n + 63) / 64);
+    const int slen = ((n + want - 1) / want + 63) / 64 * 64;
+    const bool split = slen < n;
     for (int g = 0; g < c.n_kv_heads; ++g)
-        for (int r0 = 0; r0 < rows; r0 += ATT_ROWS)
-            blocks.push_back(AttnBlock{0, g, r0, std::min(ATT_ROWS, rows - r0), 0, n, 0});
+        for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
+            const int nr = std::min(ATT_ROWS, rows - r0);
+            const int t_last = (r0 + nr - 1) / grp;
+            for (int k0 = 0, sp = 0; k0 <= t_last; k0 += slen, ++sp)
+                blocks.push_back(AttnBlock{0, g, r0, nr, k0, std::min(n, k0 + slen), sp});
+        }
     Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
     const int32_t *d_tok = pk.put(tokens, n);
     const uint64_t kvaddr = reinterpret_cast<uint64_t>(kv_buf);
@@ -413,10 +426,26 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
             a.causal = true;
-            a.out = ao;
+            a.out = split ? nullptr : ao;
+            a.part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
+            a.part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
             a.n_tokens = n;
             m->tbegin(PCD_KC_PREFILL_ATTN, st);
             const bool ok = attention(a, st);
+            if (ok && split) {
+                TailCall t{};
+                t.dt = c.dtype;
+                t.hd = hd;
+                t.n_heads = c.n_heads;
+                t.n_kv_heads = c.n_kv_heads;
+                t.n_tokens = n;
+                t.q = q;
+                t.part_o = a.part_o;
+                t.part_ml = a.part_ml;
+                t.split_len = slen;
+                t.out = ao;
+                attention_tail(t, st);
+            }
             m->tend(st);
             return ok ? PCD_OK : fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
         };
@@ -586,6 +615,7 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
             a.causal = false;
+            a.out = nullptr;
             a.part_o = part_o;
             a.part_ml = part_ml;
             a.n_tokens = Tb;

@@ -73,16 +73,17 @@ struct AttnCall {
     const int32_t *req_len; // per request: P
     const AttnBlock *blocks;
     int32_t n_blocks;
-    bool causal;            // prefill: row token t sees keys <= t
-    void *out;              // causal: final output [tokens][Hq][hd] (dt)
-    float *part_o;          // branch: [split][tokens][Hq][hd] unnormalised
-    float2 *part_ml;        // branch: [split][tokens][Hq] (max in log2 units, sum)
+    bool causal;            // prefill: row token t sees keys <= t (rows with t < key0 are skipped)
+    void *out;              // non-NULL: one split per row, final output [tokens][Hq][hd] (dt)
+    float *part_o;          // otherwise: [split][tokens][Hq][hd] unnormalised
+    float2 *part_ml;        //            [split][tokens][Hq] (max in log2 units, sum)
     int32_t n_tokens;       // tokens of this pass (row stride of the partials)
 };
 bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
 
-// Branch tokens: merge the prefix partials, then attend the token's visible
-// branch tokens (its scaffold up to itself, then its trie ancestors).
+// Merge the split partials of each (token, head); for branch tokens then
+// attend the token's visible branch tokens (its scaffold up to itself, then
+// its trie ancestors).
 struct TailCall {
     int dt;
     int32_t hd, n_heads, n_kv_heads, n_tokens;
@@ -91,8 +92,9 @@ struct TailCall {
     int32_t cap;
     const float *part_o;
     const float2 *part_ml;
-    const int32_t *tok_req, *req_splits;  // splits used by each request
-    const int32_t *fs, *nsc, *par;
+    const int32_t *tok_req, *req_splits;  // branch: splits used by each request
+    int32_t split_len;                    // prefill (> 0): token t has splits 0..t/split_len
+    const int32_t *fs, *nsc, *par;        // branch tokens; NULL for prefill
     void *out;               // [tokens][Hq][hd]
 };
 void attention_tail(const TailCall &c, hipStream_t st);

@@ -143,25 +143,30 @@ __device__ __forceinline__ void barrier_keep_loads() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename T, int BM, int BN, int NB, Epi E> struct GemmLds {
+template <typename T, int BM, int BN, int NB, Epi E, int KB = 128> struct GemmLds {
     static constexpr bool LDS_EPI = (E == Epi::Qkv || E == Epi::Readout);
-    static constexpr int STAGE = (BM + NB * BN) * 128;
+    static constexpr int STAGE = (BM + NB * BN) * KB;
     static constexpr int C_BYTES = LDS_EPI ? BM * (BN + 4) * 4 : 0;
     static int bytes(int S) { return S * STAGE > C_BYTES ? S * STAGE : C_BYTES; }
 };
 
-template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
+template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E, int KB = 128>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
+    constexpr int NW = WM * WN;         // waves per workgroup
+    constexpr int NT = NW * 64;
     constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
-    constexpr int BK = 8 * CH;          // K elements per stage (128 bytes per row)
-    constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + NB * B_BYTES;
-    constexpr int A_INS = BM / 32, B_INS = BN / 32;  // DMA instructions per wave per stage
-    constexpr int LPS = A_INS + NB * B_INS;           // ... in total
+    constexpr int CPR = KB / 16;        // chunks per tile row per stage
+    constexpr int BK = CPR * CH;        // K elements per stage
+    constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB, STAGE = A_BYTES + NB * B_BYTES;
+    constexpr int A_INS = BM * CPR / (64 * NW), B_INS = BN * CPR / (64 * NW);  // DMA instructions per wave per stage
+    constexpr int LPS = A_INS + NB * B_INS;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16;
     constexpr int KSTEPS = BK / 32;
     constexpr int CPL = 8 / CH;  // chunks holding one lane's 8 k-elements
-    constexpr bool LDS_EPI = GemmLds<T, BM, BN, NB, E>::LDS_EPI;
-    static_assert(WM * WN == 4 && BM % 32 == 0 && BN % 32 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
+    constexpr bool LDS_EPI = GemmLds<T, BM, BN, NB, E, KB>::LDS_EPI;
+    static_assert((NW == 4 || NW == 8) && (KB == 128 || KB == 256), "workgroup shape");
+    static_assert(A_INS * 64 * NW == BM * CPR && B_INS * 64 * NW == BN * CPR, "tile rows per DMA instruction");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
     static_assert(S >= 2 && S <= 4 && (S - 2) * LPS < 64, "pipeline depth");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
@@ -184,12 +189,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
     const int wm = w % WM, wn = w / WM;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // DMA sources: slot p = (i*4 + w)*64 + lane of a tile is row p/8, chunk (p%8) ^ (row%8)
+    // DMA sources: slot p = (i*NW + w)*64 + lane of a tile is row p/CPR, chunk (p%CPR) ^ (row%8)
     const T *A = reinterpret_cast<const T *>(g.A);
     const char *asrc[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-        const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
+        const int p = (i * NW + w) * 64 + lane, r = p / CPR, c = (p % CPR) ^ (r & 7);
         const int m = min(m0 + r, g.M - 1);  // rows past M load row M-1; their results are dropped
         asrc[i] = reinterpret_cast<const char *>(A + (size_t)m * g.K + kbeg + c * CH);
     }
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
     for (int q = 0; q < NB; ++q)
 #pragma unroll
         for (int i = 0; i < B_INS; ++i) {
-            const int p = (i * 4 + w) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
+            const int p = (i * NW + w) * 64 + lane, r = p / CPR, c = (p % CPR) ^ (r & 7);
             const int n = n0 + r;
             const BSegs &sg = g.B[q];
             const int s = (sg.nseg > 2 && n >= sg.begin[2]) ? 2 : ((sg.nseg > 1 && n >= sg.begin[1]) ? 1 : 0);
@@ -207,21 +212,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
         }
     auto issue = [&](int kt) {
         const uint32_t sb = lds_base + (uint32_t)((kt % S) * STAGE);
-        const size_t ko = (size_t)kt * 128;
+        const size_t ko = (size_t)kt * KB;
 #pragma unroll
-        for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + ko, sb + (uint32_t)((i * 4 + w) * 1024));
+        for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + ko, sb + (uint32_t)((i * NW + w) * 1024));
 #pragma unroll
         for (int q = 0; q < NB; ++q)
 #pragma unroll
             for (int i = 0; i < B_INS; ++i)
-                dma16(bsrc[q][i] + ko, sb + (uint32_t)(A_BYTES + q * B_BYTES + (i * 4 + w) * 1024));
+                dma16(bsrc[q][i] + ko, sb + (uint32_t)(A_BYTES + q * B_BYTES + (i * NW + w) * 1024));
     };
     auto frag = [&](Frag<T> &f, const char *tile, int row, int chunk) {
-        const char *p0 = tile + (row * 8 + (chunk ^ (row & 7))) * 16;
+        const char *p0 = tile + (row * CPR + (chunk ^ (row & 7))) * 16;
         if constexpr (CPL == 1) {
             ld8(f, reinterpret_cast<const T *>(p0));
         } else {
-            const char *p1 = tile + (row * 8 + ((chunk + 1) ^ (row & 7))) * 16;
+            const char *p1 = tile + (row * CPR + ((chunk + 1) ^ (row & 7))) * 16;
             ld4x2(f, reinterpret_cast<const T *>(p0), reinterpret_cast<const T *>(p1));
         }
     };
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
         if constexpr (E == Epi::Qkv) {
             // rotate-half RoPE: pair (j, j + hd/2) of each head of q and k
             const int hd = e.hd, half = hd >> 1;
-            for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
+            for (int idx = tid; idx < BM * (BN / 2); idx += NT) {
                 const int r = idx / (BN / 2), c = idx % (BN / 2);
                 const int hh = c / half, j = c % half;
                 const int m = m0 + r;
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
             }
         } else if constexpr (E == Epi::Readout) {
             // per readout row: max and sum of exp over this vocab tile
-            for (int r = w; r < BM; r += 4) {
+            for (int r = w; r < BM; r += NW) {
                 const int m = m0 + r;
                 if (m >= g.M) break;
                 float mx = -INFINITY;
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
                 if (lane == 0) e.ro_part[(size_t)tn * g.M + m] = make_float2(mx, s);
             }
             // candidate-token logits that fall in this tile
-            for (int q = tid; q < e.n_gather; q += 256) {
+            for (int q = tid; q < e.n_gather; q += NT) {
                 const int ro = e.g_ro[q], tk = e.g_tok[q];
                 if (ro >= m0 && ro < m0 + BM && tk >= n0 && tk < n0 + BN) e.g_logit[q] = Cs[(ro - m0) * LDC + (tk - n0)];
             }
@@ -354,9 +359,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
     }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E>
+template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E, int KB = 128>
 static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
-    constexpr int BK = 128 / sizeof(T);
+    constexpr int BK = KB / sizeof(T);
     GemmArgs<NB> g;
     g.A = c.A;
     for (int q = 0; q < NB; ++q) g.B[q] = c.B[q];
@@ -387,15 +392,15 @@ static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     e.g_ro = c.g_ro;
     e.n_gather = c.n_gather;
     e.g_logit = c.g_logit;
-    const int shmem = GemmLds<T, BM, BN, NB, E>::bytes(S);
-    auto kern = k_gemm<T, BM, BN, WM, WN, NB, S, E>;
+    const int shmem = GemmLds<T, BM, BN, NB, E, KB>::bytes(S);
+    auto kern = k_gemm<T, BM, BN, WM, WN, NB, S, E, KB>;
     static bool attr_set = false;  // one model per thread at a time; a repeated set is harmless
     if (!attr_set) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   shmem);
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(g.per_xcd * 8), dim3(256), shmem, st, g, e);
+    hipLaunchKernelGGL(kern, dim3(g.per_xcd * 8), dim3(WM * WN * 64), shmem, st, g, e);
 }
 
 enum class Reg { Small, Medium, Big };
@@ -414,19 +419,21 @@ static int pick_splits(const GemmCall &c, int tiles, int BK) {
     return best;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int S>
+template <typename T, int BM, int BN, int WM, int WN, int S, int KB = 128>
 static void gemm_resid_cfg(const GemmCall &c, hipStream_t st) {
-    constexpr int BK = 128 / sizeof(T);
+    constexpr int BK = KB / sizeof(T);
     const int tiles = (c.M + BM - 1) / BM * (c.N / BN);
     const int s = pick_splits(c, tiles, BK);
     if (s > 1) {
-        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Partial>(c, s, st);
+        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Partial, KB>(c, s, st);
         splitk_reduce(c.part, s, c.M, c.N, c.x, st);
     } else {
-        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Resid>(c, 1, st);
+        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Resid, KB>(c, 1, st);
     }
 }
 
+// Tile shapes per row-count regime, chosen from measurements at the 1.5B
+// widths (d 1536, FFN 8960, vocabulary 151936) on MI355X.
 template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
     constexpr int BK = 128 / sizeof(T);
     if (c.M <= 0 || c.N % 128 || c.K % BK) return false;
@@ -434,23 +441,23 @@ template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
     switch (c.epi) {
         case Epi::Qkv:
             if (128 % c.hd) return false;
-            if (rg == Reg::Small) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Qkv>(c, 1, st);
+            if (c.M <= 1024) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Qkv>(c, 1, st);
             else launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Qkv>(c, 1, st);
             return true;
         case Epi::Readout:
             if (rg == Reg::Small) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Readout>(c, 1, st);
             else if (rg == Reg::Medium) launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Readout>(c, 1, st);
-            else launch_gemm<T, 128, 128, 2, 2, 1, 3, Epi::Readout>(c, 1, st);
+            else launch_gemm<T, 128, 128, 2, 4, 1, 3, Epi::Readout>(c, 1, st);
             return true;
         case Epi::Resid:
             if (rg == Reg::Small) gemm_resid_cfg<T, 32, 128, 1, 4, 4>(c, st);
-            else if (rg == Reg::Medium) gemm_resid_cfg<T, 64, 128, 2, 2, 4>(c, st);
-            else gemm_resid_cfg<T, 128, 128, 2, 2, 3>(c, st);
+            else if (c.K >= 4096) gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
+            else gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
             return true;
         case Epi::SwiGlu:
             if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
-            else if (rg == Reg::Medium) launch_gemm<T, 64, 64, 2, 2, 2, 4, Epi::SwiGlu>(c, 1, st);
-            else launch_gemm<T, 128, 128, 2, 2, 2, 3, Epi::SwiGlu>(c, 1, st);
+            else if (rg == Reg::Medium) launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
+            else launch_gemm<T, 64, 64, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
             return true;
         case Epi::Partial:
             return false;  // chosen internally by Resid
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     Frag<T> qf[HS];
 #pragma unroll
     for (int s = 0; s < HS; ++s) ld8(qf[s], Q + ((size_t)tq * Hq + hq) * HD + s * 32 + lg * 8);
-    const int kend_row = c.causal ? (tq + 1) : blk.key1;
+    const int kend_row = c.causal ? min(tq + 1, blk.key1) : blk.key1;
 
     int kmax = blk.key1;
     if (c.causal) {
@@ -668,7 +675,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
         if (w * 16 + qi >= blk.nrows) continue;
         const int row = blk.row0 + w * 16 + qi;
         const int t = row / grp, h = blk.g * grp + row % grp;
-        if (c.causal) {
+        if (c.causal && t < blk.key0) continue;  // causal row with no key in this split
+        if (c.out) {
             T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
             const float inv = 1.0f / lq;
 #pragma unroll
@@ -715,7 +723,8 @@ __global__ __launch_bounds__(256) void k_attn_tail(TailCall c) {
     const float qscale = LOG2E / sqrtf((float)HD);
 
     float m = -INFINITY, l = 0.f, o[PL], q[PL];
-    const int ns = c.req_splits[c.tok_req[t]];
+    // prefill: token t has keys 0..t, so splits 0..t/split_len; branch: its request's count
+    const int ns = c.split_len > 0 ? t / c.split_len + 1 : c.req_splits[c.tok_req[t]];
     const T *Q = reinterpret_cast<const T *>(c.q) + ((size_t)t * Hq + h) * HD;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
@@ -756,11 +765,13 @@ __global__ __launch_bounds__(256) void k_attn_tail(TailCall c) {
         l = l * a + b;
         m = mn;
     };
-    const int fs = c.fs[t], nsc = c.nsc[t];
-    const int sc_end = (t < fs + nsc) ? t : fs + nsc - 1;  // scaffold tokens up to itself
-    for (int k = fs; k <= sc_end; ++k) visit(k);
-    if (t >= fs + nsc)
-        for (int k = t; k >= 0; k = c.par[k]) visit(k);  // itself, then its trie ancestors
+    if (c.fs) {
+        const int fs = c.fs[t], nsc = c.nsc[t];
+        const int sc_end = (t < fs + nsc) ? t : fs + nsc - 1;  // scaffold tokens up to itself
+        for (int k = fs; k <= sc_end; ++k) visit(k);
+        if (t >= fs + nsc)
+            for (int k = t; k >= 0; k = c.par[k]) visit(k);  // itself, then its trie ancestors
+    }
     T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
     const float inv = 1.0f / l;
 #pragma unroll
