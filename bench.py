@@ -112,6 +112,41 @@ def cpu_baseline(weights, wl, budget_layers):
             "est_request_s": round(est, 2)}
 
 
+def kernel_source_sha():
+    import hashlib
+    src = os.path.join(ROOT, "constrained_decoding_pcd_amd", "csrc", "pcd_kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
+def measured_traffic(cls):
+    """HBM bytes per launch of kernel class `cls` from the committed rocprofv3
+    counter summary, or None when there is none for it or the kernel source
+    has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_cfg1.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_class") != cls or kv.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,7 +154,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cfg1", help="cfg0 (tiny) or cfg1 (1.5B, 512-token prefix, 28 fields)")
     ap.add_argument("--cpu-layers", type=int, default=2, help="layers of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the path is single-GPU by design (requests are independent and "
@@ -169,6 +209,7 @@ def main():
     print(f"# {args.steps} steps: {ms_per_step:.3f} ms/step, p50 {p50:.3f} ms, p90 {p90:.3f} ms",
           file=sys.stderr, flush=True)
     stats = model.stats()
+    dev_ms = stats["last_prefill_ms"] + stats["last_branch_ms"] + stats["last_readout_ms"]
 
     # the same steps again with every kernel launch bracketed by hipEvents on the library's stream
     model.set_kernel_timing(True)
@@ -183,6 +224,9 @@ def main():
     peak_mfma = BF16_PEAK_TFLOPS if sh.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernels = {c: roofline_entry(c, ms, n, work, peak_mfma) for c, (ms, n) in kt.items() if n > 0 and c in work}
     dominant = max(kernels, key=lambda c: kt[c][0])
+    traffic = measured_traffic(dominant)
+    if traffic is not None:
+        kernels[dominant]["traffic"] = traffic
     timed_ms_per_step = sum(ms for ms, _ in kt.values()) / args.steps
     res = {
         "metric": "schema fields decided/sec + p50 28-field request ms, 1.5B-shaped bf16",
@@ -205,6 +249,7 @@ def main():
                    "branch_tokens": Tb, "readouts": R},
         "phases_ms": {"prefill": round(stats["last_prefill_ms"], 4), "branch": round(stats["last_branch_ms"], 4),
                       "readout": round(stats["last_readout_ms"], 4)},
+        "device_fields_per_s": round(nf / (dev_ms / 1e3), 2),
         "passes": {"prefill": 1, "branch": 1,
                    "token_by_token_equivalent": int(sum(len(f.scaffold) + len(f.candidates[int(a)])
                                                         for f, a in zip(req.fields, out["argmax"])))},
