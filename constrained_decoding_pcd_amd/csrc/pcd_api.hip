@@ -53,6 +53,13 @@ int64_t plan_block_cap(const pcd_config &c, const pcd_limits &l) {
 
 int64_t path_cap(const pcd_limits &l) { return 8 * (int64_t)l.max_candidates + l.max_gathers; }
 
+// partial sums of the residual GEMMs: up to SPLITK_MAX splits below
+// SPLITK_ROWS rows, one above
+size_t splitk_floats(const pcd_config &c, const pcd_limits &l) {
+    const size_t rows = (size_t)std::max(l.max_prefill_tokens, l.max_branch_tokens);
+    return std::max((size_t)SPLITK_MAX * std::min(rows, (size_t)SPLITK_ROWS), rows) * c.d_model;
+}
+
 Layout layout(const pcd_config &c, const pcd_limits &l) {
     Layout L{};
     const size_t esz = c.dtype == PCD_DTYPE_F32 ? 4 : 2;
@@ -70,7 +77,7 @@ Layout layout(const pcd_config &c, const pcd_limits &l) {
     L.q = take(rows * hq * esz);
     L.ao = take(rows * hq * esz);
     L.act = take(rows * c.ffn_dim * esz);
-    L.splitk = take((size_t)SPLITK_MAX * std::min(rows, (size_t)SPLITK_ROWS) * d * 4);
+    L.splitk = take(splitk_floats(c, l) * 4);
     L.kvb = take((size_t)c.n_layers * 2 * c.n_kv_heads * l.max_branch_tokens * c.head_dim * esz);
     L.part_o = take((size_t)MAX_SPLITS * rows * hq * 4);
     L.part_ml = take((size_t)MAX_SPLITS * rows * c.n_heads * sizeof(float2));
@@ -178,8 +185,9 @@ namespace {
 size_t esize(const pcd_model *m) { return m->cfg.dtype == PCD_DTYPE_F32 ? 4 : 2; }
 
 // O projection or down projection into the residual stream (split-K inside
-// gemm() when the tile count is too small for the chip)
-bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W, hipStream_t st) {
+// gemm() when the tile count is too small for the chip), followed by the
+// RMSNorm with weight `norm_w` whose output is the next GEMM's input
+bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W, const float *norm_w, hipStream_t st) {
     GemmCall c{};
     c.dt = m->cfg.dtype;
     c.A = A;
@@ -191,8 +199,10 @@ bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W,
     c.epi = Epi::Resid;
     c.x = reinterpret_cast<float *>(m->ws + m->L.x);
     c.part = reinterpret_cast<float *>(m->ws + m->L.splitk);
-    c.part_cap = (size_t)SPLITK_MAX * std::min(std::max(m->lim.max_prefill_tokens, m->lim.max_branch_tokens),
-                                               SPLITK_ROWS) * m->cfg.d_model;
+    c.part_cap = splitk_floats(m->cfg, m->lim);
+    c.norm_w = norm_w;
+    c.eps = m->cfg.rms_eps;
+    c.h_out = m->ws + m->L.h;
     return gemm(c, st);
 }
 
@@ -209,9 +219,7 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     const int d = c.d_model, hd = c.head_dim, nq = c.n_heads * hd, nk = c.n_kv_heads * hd;
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     void *h = m->ws + m->L.h, *q = m->ws + m->L.q, *ao = m->ws + m->L.ao, *act = m->ws + m->L.act;
-    m->tbegin(PCD_KC_OTHER, st);
-    rmsnorm(c.dtype, x, nullptr, M, d, m->an[l], c.rms_eps, h, st);
-    m->tend(st);
+    (void)x;  // h holds rmsnorm(x) * attn_norm[l] on entry (embedding or previous layer)
     GemmCall g{};
     g.dt = c.dtype;
     g.A = h;
@@ -241,10 +249,7 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     int rc = attn(q, ao);
     if (rc != PCD_OK) return rc;
     m->tbegin(K_O, st);
-    if (!gemm_resid(m, ao, M, d, nq, m->wo[l], st)) return fail(PCD_E_ARG, "O projection: unsupported shape");
-    m->tend(st);
-    m->tbegin(PCD_KC_OTHER, st);
-    rmsnorm(c.dtype, x, nullptr, M, d, m->mn[l], c.rms_eps, h, st);
+    if (!gemm_resid(m, ao, M, d, nq, m->wo[l], m->mn[l], st)) return fail(PCD_E_ARG, "O projection: unsupported shape");
     m->tend(st);
     GemmCall f{};
     f.dt = c.dtype;
@@ -262,7 +267,9 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     if (!gemm(f, st)) return fail(PCD_E_ARG, "gate/up projection: unsupported shape");
     m->tend(st);
     m->tbegin(K_DN, st);
-    if (!gemm_resid(m, act, M, d, c.ffn_dim, m->wd[l], st)) return fail(PCD_E_ARG, "down projection: unsupported shape");
+    const float *next_norm = l + 1 < c.n_layers ? m->an[l + 1] : nullptr;
+    if (!gemm_resid(m, act, M, d, c.ffn_dim, m->wd[l], next_norm, st))
+        return fail(PCD_E_ARG, "down projection: unsupported shape");
     m->tend(st);
     return PCD_OK;
 }
@@ -407,7 +414,7 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
     HIP_TRY(hipEventRecord(m->ev[3], st));
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     m->tbegin(PCD_KC_OTHER, st);
-    embed(c.dtype, d_tok, n, m->embed, c.d_model, x, st);
+    embed(c.dtype, d_tok, n, m->embed, c.d_model, x, m->an[0], c.rms_eps, m->ws + m->L.h, st);
     m->tend(st);
     const size_t layer_elems = (size_t)2 * c.n_kv_heads * n * hd;
     for (int l = 0; l < c.n_layers; ++l) {
@@ -594,7 +601,7 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     HIP_TRY(hipEventRecord(m->ev[0], st));
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     m->tbegin(PCD_KC_OTHER, st);
-    embed(c.dtype, d_tok, Tb, m->embed, d, x, st);
+    embed(c.dtype, d_tok, Tb, m->embed, d, x, m->an[0], c.rms_eps, m->ws + m->L.h, st);
     m->tend(st);
     const size_t layer_elems = (size_t)2 * c.n_kv_heads * Tb * hd;
     float *part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);

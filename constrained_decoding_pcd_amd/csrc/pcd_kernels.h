@@ -21,7 +21,7 @@ struct BSegs {
 
 enum class Epi : int {
     Qkv,      // RoPE on q and k, q -> q buffer, k and v -> a KV cache
-    Resid,    // x[m][n] += c   (fp32 residual stream)
+    Resid,    // x[m][n] += c (fp32 residual stream), then h = rmsnorm(x) * norm_w for the next GEMM
     Partial,  // split-K partial sums -> part[split][m][n] (chosen inside gemm() for Resid)
     SwiGlu,   // two B operands: out[m][n] = silu(c_gate) * c_up
     Readout,  // per-row (max, sum exp) of the tile + gathered candidate logits
@@ -35,8 +35,11 @@ struct GemmCall {
     Epi epi;
     // epilogue arguments
     float *x;        // Resid: residual [M][N]
-    float *part;     // Resid: scratch for split-K partial sums (NULL: never split)
-    size_t part_cap; // floats available at part
+    float *part;     // Resid: scratch for the (split-K) partial sums
+    size_t part_cap; // floats available at part (at least M*N)
+    const float *norm_w;  // Resid: weight of the RMSNorm that follows (NULL: none)
+    float eps;
+    void *h_out;     // Resid: [M][N] normalised rows (dt)
     void *out;       // SwiGlu: [M][N] of dt;  Qkv: q buffer [M][Hq][hd]
     void *kc, *vc;   // Qkv: K and V cache of this layer, [Hkv][cap][hd] each
     int32_t cap;     // Qkv: tokens per KV head in the cache
@@ -53,12 +56,15 @@ struct GemmCall {
 bool gemm(const GemmCall &c, hipStream_t st);
 int gemm_k_tile(int dt);  // elements of K per pipeline stage
 
-void embed(int dt, const int32_t *tok, int32_t T, const void *E, int32_t d, float *x, hipStream_t st);
+// x[t] = E[tok[t]]; h[t] = rmsnorm(x[t]) * w as dt
+void embed(int dt, const int32_t *tok, int32_t T, const void *E, int32_t d, float *x, const float *w, float eps,
+           void *h, hipStream_t st);
 // out[i] = x[rows ? rows[i] : i] / sqrt(mean(x^2) + eps) * w, as dt
 void rmsnorm(int dt, const float *x, const int32_t *rows, int32_t n, int32_t d, const float *w, float eps, void *out,
              hipStream_t st);
-// x[m][n] += sum over s of part[s][m][n], s in increasing order
-void splitk_reduce(const float *part, int32_t splits, int32_t M, int32_t N, float *x, hipStream_t st);
+// x[m][n] += sum over s of part[s][m][n] (s increasing); then, if w, h[m] = rmsnorm(x[m]) * w
+void resid_norm(int dt, const float *part, int32_t splits, int32_t M, int32_t N, float *x, const float *w, float eps,
+                void *h, hipStream_t st);
 
 // Attention over a KV cache, flash style.  Query rows of a block are
 // (token, head within the KV group) pairs, token-major.

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace pcd {
 
@@ -136,6 +137,12 @@ template <int N> __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// wait until this wave's LDS reads have returned (lgkmcnt 0; vmcnt untouched)
+__device__ __forceinline__ void lds_reads_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 // workgroup barrier that does not wait for in-flight global loads
 __device__ __forceinline__ void barrier_keep_loads() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -167,7 +174,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
     static_assert((NW == 4 || NW == 8) && (KB == 128 || KB == 256), "workgroup shape");
     static_assert(A_INS * 64 * NW == BM * CPR && B_INS * 64 * NW == BN * CPR, "tile rows per DMA instruction");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(S >= 2 && S <= 4 && (S - 2) * LPS < 64, "pipeline depth");
+    static_assert(S >= 2 && S <= 4 && (S - 1) * LPS < 64, "pipeline depth");
+    static_assert(S * STAGE <= 160 * 1024, "operand ring exceeds the 160 KB of LDS");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
 
@@ -239,38 +247,79 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[q][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Fragments are double-buffered in registers: the LDS reads of the next
+    // k-step go out before the matrix-core work of the current one, and the
+    // per-tile wait + barrier sit between two MFMA batches.  Stage kt lives in
+    // slot kt % S; S stages are issued ahead; stage kt+S refills slot kt % S
+    // right after the barrier that follows the last read of stage kt.
+    Frag<T> fa[2][FM], fb[2][NB][FN];
+    auto read_frags = [&](auto BUF, int kt, int s) {
+        constexpr int bb = decltype(BUF)::value;
+        const char *st = lds + (kt % S) * STAGE;
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-        if (s < nkt) issue(s);
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int ahead = min(S - 2, nkt - 1 - kt);  // stages after kt already in flight
-        if constexpr (S == 4) {
-            if (ahead >= 2) vm_wait<2 * LPS>();
+        for (int i = 0; i < FM; ++i) frag(fa[bb][i], st, wm * WTM + i * 16 + lr, s * 4 * CPL + lg * CPL);
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                frag(fb[bb][q][j], st + A_BYTES + q * B_BYTES, wn * WTN + j * 16 + lr, s * 4 * CPL + lg * CPL);
+    };
+    auto mfmas = [&](auto BUF) {
+        constexpr int bb = decltype(BUF)::value;
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i) mma(acc[q][i][j], fa[bb][i], fb[bb][q][j]);
+    };
+    // wait until stage `next` has landed; the stages issued after it may stay in
+    // flight: S-1 of them before the loop, S-2 inside it (stage next+S-1 is
+    // issued only after this wait)
+    auto wait_stage = [&](int next) {
+        const int ahead = min(next == 0 ? S - 1 : S - 2, nkt - 1 - next);
+        if constexpr (S >= 4) {
+            if (ahead >= 3) vm_wait<3 * LPS>();
+            else if (ahead == 2) vm_wait<2 * LPS>();
             else if (ahead == 1) vm_wait<LPS>();
             else vm_wait<0>();
         } else if constexpr (S == 3) {
-            if (ahead >= 1) vm_wait<LPS>();
+            if (ahead >= 2) vm_wait<2 * LPS>();
+            else if (ahead == 1) vm_wait<LPS>();
             else vm_wait<0>();
         } else {
-            vm_wait<0>();
+            if (ahead >= 1) vm_wait<LPS>();
+            else vm_wait<0>();
         }
-        barrier_keep_loads();
-        if (kt + S - 1 < nkt) issue(kt + S - 1);
-        const char *st = lds + (kt % S) * STAGE;
+    };
+    static_assert(KSTEPS % 2 == 0, "k-steps per stage must be even for the fragment ping-pong");
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            Frag<T> fa[FM];
+    for (int s = 0; s < S; ++s)
+        if (s < nkt) issue(s);
+    wait_stage(0);
+    barrier_keep_loads();
+    read_frags(B0{}, 0, 0);
+    for (int kt = 0; kt < nkt; ++kt) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) frag(fa[i], st, wm * WTM + i * 16 + lr, s * 4 * CPL + lg * CPL);
-#pragma unroll
-            for (int q = 0; q < NB; ++q)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    Frag<T> fb;
-                    frag(fb, st + A_BYTES + q * B_BYTES, wn * WTN + j * 16 + lr, s * 4 * CPL + lg * CPL);
-#pragma unroll
-                    for (int i = 0; i < FM; ++i) mma(acc[q][i][j], fa[i], fb);
-                }
+        for (int s = 0; s < KSTEPS; s += 2) {
+            // even k-step: compute buffer 0 while buffer 1 loads
+            read_frags(B1{}, kt, s + 1);
+            mfmas(B0{});
+            // odd k-step: compute buffer 1 while buffer 0 loads (possibly from the next stage)
+            if (s + 2 < KSTEPS) {
+                read_frags(B0{}, kt, s + 2);
+            } else if (kt + 1 < nkt) {
+                // this wave's reads of stage kt must be done before anyone refills its slot
+                lds_reads_done();
+                wait_stage(kt + 1);
+                barrier_keep_loads();
+                if (kt + S < nkt) issue(kt + S);
+                read_frags(B0{}, kt + 1, 0);
+            }
+            mfmas(B1{});
         }
     }
 
@@ -409,7 +458,7 @@ static Reg regime(int M) { return M >= 384 ? Reg::Big : (M > 48 ? Reg::Medium : 
 // split-K for an epilogue that adds into the residual stream: enough
 // workgroups for the chip, partial sums within the caller's buffer
 static int pick_splits(const GemmCall &c, int tiles, int BK) {
-    if (tiles >= 200 || !c.part) return 1;
+    if (tiles >= 200) return 1;
     int best = 1;
     for (int s = 2; s <= 8; ++s) {
         if (c.K % (s * BK) || c.K / s < 2 * BK || (size_t)s * c.M * c.N > c.part_cap) continue;
@@ -419,70 +468,104 @@ static int pick_splits(const GemmCall &c, int tiles, int BK) {
     return best;
 }
 
+// Residual GEMMs write fp32 partial sums (split-K when the tile count is
+// small), then one kernel per row adds them into the residual stream and
+// writes the next RMSNorm's bf16 input.
 template <typename T, int BM, int BN, int WM, int WN, int S, int KB = 128>
 static void gemm_resid_cfg(const GemmCall &c, hipStream_t st) {
     constexpr int BK = KB / sizeof(T);
     const int tiles = (c.M + BM - 1) / BM * (c.N / BN);
     const int s = pick_splits(c, tiles, BK);
-    if (s > 1) {
-        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Partial, KB>(c, s, st);
-        splitk_reduce(c.part, s, c.M, c.N, c.x, st);
-    } else {
-        launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Resid, KB>(c, 1, st);
-    }
+    launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Partial, KB>(c, s, st);
+    resid_norm(c.dt, c.part, s, c.M, c.N, c.x, c.norm_w, c.eps, c.h_out, st);
 }
 
 // Tile shapes per row-count regime, chosen from measurements at the 1.5B
-// widths (d 1536, FFN 8960, vocabulary 151936) on MI355X.
+// widths (d 1536, FFN 8960, vocabulary 151936) on MI355X.  fp32 models (the
+// tiny configuration) use 32-row tiles with 256-byte k-tiles throughout.
 template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
-    constexpr int BK = 128 / sizeof(T);
+    constexpr int KB = sizeof(T) == 2 ? 128 : 256;
+    constexpr int BK = KB / sizeof(T);
     if (c.M <= 0 || c.N % 128 || c.K % BK) return false;
-    const Reg rg = regime(c.M);
-    switch (c.epi) {
-        case Epi::Qkv:
-            if (128 % c.hd) return false;
-            if (c.M <= 1024) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Qkv>(c, 1, st);
-            else launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Qkv>(c, 1, st);
-            return true;
-        case Epi::Readout:
-            if (rg == Reg::Small) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Readout>(c, 1, st);
-            else if (rg == Reg::Medium) launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Readout>(c, 1, st);
-            else launch_gemm<T, 128, 128, 2, 4, 1, 3, Epi::Readout>(c, 1, st);
-            return true;
-        case Epi::Resid:
-            if (rg == Reg::Small) gemm_resid_cfg<T, 32, 128, 1, 4, 4>(c, st);
-            else if (c.K >= 4096) gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
-            else gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
-            return true;
-        case Epi::SwiGlu:
-            if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
-            else if (rg == Reg::Medium) launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
-            else launch_gemm<T, 64, 64, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
-            return true;
-        case Epi::Partial:
-            return false;  // chosen internally by Resid
+    if constexpr (sizeof(T) == 4) {
+        switch (c.epi) {
+            case Epi::Qkv:
+                if (128 % c.hd) return false;
+                launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Qkv, KB>(c, 1, st);
+                return true;
+            case Epi::Readout: launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Readout, KB>(c, 1, st); return true;
+            case Epi::Resid: gemm_resid_cfg<T, 32, 128, 1, 4, 4, KB>(c, st); return true;
+            case Epi::SwiGlu: launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu, KB>(c, 1, st); return true;
+            case Epi::Partial: return false;
+        }
+        return false;
+    } else {
+        const Reg rg = regime(c.M);
+        switch (c.epi) {
+            case Epi::Qkv:
+                if (128 % c.hd) return false;
+                if (c.M <= 1024) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Qkv>(c, 1, st);
+                else launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Qkv>(c, 1, st);
+                return true;
+            case Epi::Readout:
+                if (rg == Reg::Small) launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Readout>(c, 1, st);
+                else if (rg == Reg::Medium) launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Readout>(c, 1, st);
+                else launch_gemm<T, 128, 128, 2, 4, 1, 3, Epi::Readout>(c, 1, st);
+                return true;
+            case Epi::Resid:
+                if (rg == Reg::Small) gemm_resid_cfg<T, 32, 128, 1, 4, 4>(c, st);
+                else if (c.K >= 4096) gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
+                else gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
+                return true;
+            case Epi::SwiGlu:
+                if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
+                else if (rg == Reg::Medium) launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
+                else launch_gemm<T, 64, 64, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
+                return true;
+            case Epi::Partial:
+                return false;  // chosen internally by Resid
+        }
+        return false;
     }
-    return false;
 }
 
 bool gemm(const GemmCall &c, hipStream_t st) {
     return c.dt == PCD_DT_F32 ? gemm_t<float>(c, st) : gemm_t<bf16_t>(c, st);
 }
-int gemm_k_tile(int dt) { return dt == PCD_DT_F32 ? 32 : 64; }
+int gemm_k_tile(int dt) { return dt == PCD_DT_F32 ? 64 : 64; }
 
 // ---------------------------------------------------------------------------
 // embedding gather, RMSNorm, split-K reduction
 // ---------------------------------------------------------------------------
-template <typename T> __global__ void k_embed(const int32_t *tok, const T *E, int32_t d, float *x) {
+// x[t] = E[tok[t]] (fp32) and h[t] = rmsnorm(x[t]) * w (dt): the first
+// layer's normalised input comes out of the embedding gather.
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed(const int32_t *tok, const T *E, int32_t d, float *x, const float *w,
+                                               float eps, T *h) {
+    __shared__ float red[4];
     const int t = blockIdx.x;
     const T *row = E + (size_t)tok[t] * d;
-    for (int j = threadIdx.x; j < d; j += blockDim.x) x[(size_t)t * d + j] = to_f(row[j]);
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < d; j += 256) {
+        const float v = to_f(row[j]);
+        x[(size_t)t * d + j] = v;
+        ss += v * v;
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+    for (int j = threadIdx.x; j < d; j += 256) h[(size_t)t * d + j] = from_f<T>(to_f(row[j]) * inv * w[j]);
 }
 
-void embed(int dt, const int32_t *tok, int32_t T, const void *E, int32_t d, float *x, hipStream_t st) {
+void embed(int dt, const int32_t *tok, int32_t T, const void *E, int32_t d, float *x, const float *w, float eps,
+           void *h, hipStream_t st) {
     if (T <= 0) return;
-    if (dt == PCD_DT_F32) hipLaunchKernelGGL(k_embed<float>, dim3(T), dim3(256), 0, st, tok, (const float *)E, d, x);
-    else hipLaunchKernelGGL(k_embed<bf16_t>, dim3(T), dim3(256), 0, st, tok, (const bf16_t *)E, d, x);
+    if (dt == PCD_DT_F32)
+        hipLaunchKernelGGL(k_embed<float>, dim3(T), dim3(256), 0, st, tok, (const float *)E, d, x, w, eps, (float *)h);
+    else
+        hipLaunchKernelGGL(k_embed<bf16_t>, dim3(T), dim3(256), 0, st, tok, (const bf16_t *)E, d, x, w, eps,
+                           (bf16_t *)h);
 }
 
 template <typename T>
@@ -508,25 +591,38 @@ void rmsnorm(int dt, const float *x, const int32_t *rows, int32_t n, int32_t d, 
     else hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(n), dim3(256), 0, st, x, rows, d, w, eps, (bf16_t *)out);
 }
 
-__global__ void k_splitk_reduce(const float4 *part, int32_t splits, size_t n4, float4 *x) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n4) return;
-    float4 a = x[i];
-    for (int s = 0; s < splits; ++s) {
-        const float4 p = part[s * n4 + i];
-        a.x += p.x;
-        a.y += p.y;
-        a.z += p.z;
-        a.w += p.w;
+// One workgroup per row m: x[m] += sum over s of part[s][m] (s in increasing
+// order, so the result does not depend on scheduling), then, if w is given,
+// h[m] = rmsnorm(x[m]) * w as the next GEMM's input.
+template <typename T>
+__global__ __launch_bounds__(256) void k_resid_norm(const float *part, int32_t splits, int32_t M, int32_t N, float *x,
+                                                    const float *w, float eps, T *h) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    float *xr = x + (size_t)m * N;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < N; j += 256) {
+        float v = xr[j];
+        for (int s = 0; s < splits; ++s) v += part[((size_t)s * M + m) * N + j];
+        xr[j] = v;
+        ss += v * v;
     }
-    x[i] = a;
+    if (!w) return;
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+    for (int j = threadIdx.x; j < N; j += 256) h[(size_t)m * N + j] = from_f<T>(xr[j] * inv * w[j]);
 }
 
-void splitk_reduce(const float *part, int32_t splits, int32_t M, int32_t N, float *x, hipStream_t st) {
-    const size_t n4 = (size_t)M * N / 4;
-    if (n4 == 0) return;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                       (const float4 *)part, splits, n4, (float4 *)x);
+void resid_norm(int dt, const float *part, int32_t splits, int32_t M, int32_t N, float *x, const float *w, float eps,
+                void *h, hipStream_t st) {
+    if (M <= 0) return;
+    if (dt == PCD_DT_F32)
+        hipLaunchKernelGGL(k_resid_norm<float>, dim3(M), dim3(256), 0, st, part, splits, M, N, x, w, eps, (float *)h);
+    else
+        hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(M), dim3(256), 0, st, part, splits, M, N, x, w, eps,
+                           (bf16_t *)h);
 }
 
 // ---------------------------------------------------------------------------
