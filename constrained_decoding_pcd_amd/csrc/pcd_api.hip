@@ -29,13 +29,25 @@ int fail(int code, const std::string &msg) {
         if (e_ != hipSuccess) return fail(PCD_E_DEVICE, std::string(#expr ": ") + hipGetErrorString(e_)); \
     } while (0)
 
-constexpr int MAX_SPLITS = 8;         // prefix splits of the branch attention
+constexpr int MAX_SPLITS = 8;         // key splits of one attention row block
 constexpr int ATT_ROWS = 64;          // query rows per attention workgroup
 constexpr int SPLITK_MAX = 8;
 constexpr int SPLITK_ROWS = 1024;     // split-K is only used below this many rows
 constexpr uint64_t STATE_MAGIC = 0x70636473746174ull;
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+// Attention workgroups per launch that keep every compute unit busy (two
+// per unit), and the shortest key range worth a workgroup of its own.
+constexpr int ATT_TARGET_BLOCKS = 512;
+constexpr int ATT_MIN_SPLIT_TILES = 2;  // 64-key tiles
+// Key splits of a row block: enough for `row_blocks` blocks to reach the
+// target count, no split shorter than the minimum, at most MAX_SPLITS.
+static int att_splits(int64_t row_blocks, int key_tiles) {
+    const int64_t want = (ATT_TARGET_BLOCKS + row_blocks - 1) / std::max<int64_t>(1, row_blocks);
+    const int by_len = std::max(1, key_tiles / ATT_MIN_SPLIT_TILES);
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)MAX_SPLITS, (int64_t)by_len}));
+}
 
 struct Layout {
     size_t rope, x, h, q, ao, act, splitk, kvb, part_o, part_ml, hr, ro_part, lse, z, outs, plan;
@@ -384,23 +396,22 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
             return fail(PCD_E_TOKEN, "token id " + std::to_string(tokens[i]) + " outside the vocabulary");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim;
-    // device tables: tokens, one request (this KV buffer), attention blocks.
-    // Causal attention is split over the keys when there are too few 64-row
-    // blocks for the chip: split s covers keys [s*slen, (s+1)*slen), and only
-    // row blocks that reach key s*slen get a workgroup for it.
+    // device tables: tokens, one request (this KV buffer), attention blocks:
+    // per KV head, 64 query rows each, causal keys 0..t of every row.  With
+    // too few row blocks for the chip the keys are split: split k covers
+    // [k*slen, (k+1)*slen), only row blocks that reach key k*slen get a
+    // workgroup for it, and a merge kernel combines the partials.
     std::vector<AttnBlock> blocks;
     const int rows = n * grp;
     const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + ATT_ROWS - 1) / ATT_ROWS);
-    int want = (int)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, (1024 + row_blocks - 1) / row_blocks));
-    want = std::min(want, (n + 63) / 64);
-    const int slen = ((n + want - 1) / want + 63) / 64 * 64;
-    const bool split = slen < n;
+    int ns = att_splits(row_blocks, (n + 63) / 64);
+    const int slen = ((n + ns - 1) / ns + 63) / 64 * 64;
+    ns = (n + slen - 1) / slen;
     for (int g = 0; g < c.n_kv_heads; ++g)
         for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
-            const int nr = std::min(ATT_ROWS, rows - r0);
-            const int t_last = (r0 + nr - 1) / grp;
-            for (int k0 = 0, sp = 0; k0 <= t_last; k0 += slen, ++sp)
-                blocks.push_back(AttnBlock{0, g, r0, nr, k0, std::min(n, k0 + slen), sp});
+            const int nr = std::min(ATT_ROWS, rows - r0), t_last = (r0 + nr - 1) / grp;
+            for (int k = 0; k < ns && k * slen <= t_last; ++k)
+                blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(n, (k + 1) * slen), k, ns, 0, 0});
         }
     Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
     const int32_t *d_tok = pk.put(tokens, n);
@@ -433,28 +444,30 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
             a.causal = true;
-            a.out = split ? nullptr : ao;
+            a.out = ao;
             a.part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
             a.part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
             a.n_tokens = n;
             m->tbegin(PCD_KC_PREFILL_ATTN, st);
             const bool ok = attention(a, st);
-            if (ok && split) {
+            m->tend(st);
+            if (!ok) return fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
+            if (ns > 1) {
                 TailCall t{};
                 t.dt = c.dtype;
                 t.hd = hd;
                 t.n_heads = c.n_heads;
                 t.n_kv_heads = c.n_kv_heads;
                 t.n_tokens = n;
-                t.q = q;
                 t.part_o = a.part_o;
                 t.part_ml = a.part_ml;
                 t.split_len = slen;
                 t.out = ao;
-                attention_tail(t, st);
+                m->tbegin(PCD_KC_PREFILL_ATTN, st);
+                attention_merge(t, st);
+                m->tend(st);
             }
-            m->tend(st);
-            return ok ? PCD_OK : fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
+            return PCD_OK;
         };
         int rc = layer(m, l, n, nullptr, kc, vc, n, false, attn, st);
         if (rc != PCD_OK) return rc;
@@ -537,27 +550,35 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
                                    " readouts, " + std::to_string(G) + " gathers exceeds the model's limits");
     const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim, d = c.d_model;
 
-    // prefix attention blocks: per request, KV head, 64-row block and prefix split
-    int64_t nosplit = 0;
-    for (int r = 0; r < n_req; ++r)
-        nosplit += (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
-    const int want = (int)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, (512 + nosplit - 1) / nosplit));
+    // attention blocks: per request, KV head and 64-row block; with too few
+    // row blocks for the chip the prefix keys are split over workgroups (the
+    // partials are then merged by a second kernel).  The last split of a row
+    // block also covers the branch keys of the fields its rows belong to.
     std::vector<int32_t> req_splits(n_req);
     std::vector<uint64_t> req_kv(n_req);
     std::vector<AttnBlock> blocks;
+    bool any_split = false;
+    int64_t row_blocks = 0;
+    for (int r = 0; r < n_req; ++r)
+        row_blocks += (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
     for (int r = 0; r < n_req; ++r) {
         const int P = lens[r];
-        int s = std::min(want, (P + 63) / 64);
+        const int tiles = (P + 63) / 64;
+        int s = att_splits(row_blocks, tiles);
         const int slen = ((P + s - 1) / s + 63) / 64 * 64;
         s = (P + slen - 1) / slen;
+        any_split |= s > 1;
         req_splits[r] = s;
         req_kv[r] = reinterpret_cast<uint64_t>(states[r]->kv);
         const int row_beg = p.r_tok[r] * grp, row_end = p.r_tok[r + 1] * grp;
         for (int g = 0; g < c.n_kv_heads; ++g)
-            for (int r0 = row_beg; r0 < row_end; r0 += ATT_ROWS)
+            for (int r0 = row_beg; r0 < row_end; r0 += ATT_ROWS) {
+                const int nr = std::min(ATT_ROWS, row_end - r0);
+                const int t_first = r0 / grp, t_last = (r0 + nr - 1) / grp;
                 for (int k = 0; k < s; ++k)
-                    blocks.push_back(
-                        AttnBlock{r, g, r0, std::min(ATT_ROWS, row_end - r0), k * slen, std::min(P, (k + 1) * slen), k});
+                    blocks.push_back(AttnBlock{r, g, r0, nr, k * slen, std::min(P, (k + 1) * slen), k, s,
+                                               k == s - 1 ? p.fs[t_first] : 0, k == s - 1 ? t_last + 1 : 0});
+            }
     }
     if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
 
@@ -622,35 +643,36 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
             a.causal = false;
-            a.out = nullptr;
+            a.out = ao;
             a.part_o = part_o;
             a.part_ml = part_ml;
             a.n_tokens = Tb;
+            a.kb = kc;
+            a.vb = vc;
+            a.cap = Tb;
+            a.fs = d_fs;
+            a.nsc = d_nsc;
+            a.par = d_par;
             m->tbegin(PCD_KC_BRANCH_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);
             if (!ok) return fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
-            TailCall t{};
-            t.dt = c.dtype;
-            t.hd = hd;
-            t.n_heads = c.n_heads;
-            t.n_kv_heads = c.n_kv_heads;
-            t.n_tokens = Tb;
-            t.q = q;
-            t.kb = kc;
-            t.vb = vc;
-            t.cap = Tb;
-            t.part_o = part_o;
-            t.part_ml = part_ml;
-            t.tok_req = d_req;
-            t.req_splits = d_rsp;
-            t.fs = d_fs;
-            t.nsc = d_nsc;
-            t.par = d_par;
-            t.out = ao;
-            m->tbegin(PCD_KC_BRANCH_TAIL, st);
-            attention_tail(t, st);
-            m->tend(st);
+            if (any_split) {
+                TailCall t{};
+                t.dt = c.dtype;
+                t.hd = hd;
+                t.n_heads = c.n_heads;
+                t.n_kv_heads = c.n_kv_heads;
+                t.n_tokens = Tb;
+                t.part_o = part_o;
+                t.part_ml = part_ml;
+                t.tok_req = d_req;
+                t.req_splits = d_rsp;
+                t.out = ao;
+                m->tbegin(PCD_KC_BRANCH_TAIL, st);
+                attention_merge(t, st);
+                m->tend(st);
+            }
             return PCD_OK;
         };
         rc = layer(m, l, Tb, d_pos, kc, vc, Tb, true, attn, st);

@@ -66,10 +66,14 @@ void rmsnorm(int dt, const float *x, const int32_t *rows, int32_t n, int32_t d, 
 void resid_norm(int dt, const float *part, int32_t splits, int32_t M, int32_t N, float *x, const float *w, float eps,
                 void *h, hipStream_t st);
 
-// Attention over a KV cache, flash style.  Query rows of a block are
-// (token, head within the KV group) pairs, token-major.
+// Attention over KV caches, flash style.  Query rows of a block are (token,
+// head within the KV group) pairs, token-major.  A block covers prefix keys
+// [key0, key1) of its request's state and, for branch tokens, the branch keys
+// [sfx_lo, sfx_hi) (masked to each row's scaffold up to itself and its trie
+// ancestors).  nsplit == 1: the block writes the final output; otherwise
+// partials for attention_merge.
 struct AttnBlock {
-    int32_t req, g, row0, nrows, key0, key1, split;
+    int32_t req, g, row0, nrows, key0, key1, split, nsplit, sfx_lo, sfx_hi;
 };
 struct AttnCall {
     int dt;
@@ -79,31 +83,29 @@ struct AttnCall {
     const int32_t *req_len; // per request: P
     const AttnBlock *blocks;
     int32_t n_blocks;
-    bool causal;            // prefill: row token t sees keys <= t (rows with t < key0 are skipped)
-    void *out;              // non-NULL: one split per row, final output [tokens][Hq][hd] (dt)
-    float *part_o;          // otherwise: [split][tokens][Hq][hd] unnormalised
-    float2 *part_ml;        //            [split][tokens][Hq] (max in log2 units, sum)
+    bool causal;            // prefill: row token t sees prefix keys <= t (rows with t < key0 are skipped)
+    void *out;              // [tokens][Hq][hd] (dt)
+    float *part_o;          // [split][tokens][Hq][hd] unnormalised
+    float2 *part_ml;        // [split][tokens][Hq] (max in log2 units, sum)
     int32_t n_tokens;       // tokens of this pass (row stride of the partials)
+    const void *kb, *vb;    // branch K/V of this layer, [Hkv][cap][hd] (branch pass only)
+    int32_t cap;
+    const int32_t *fs, *nsc, *par;  // per branch token: field start, scaffold length, trie parent
 };
 bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
 
-// Merge the split partials of each (token, head); for branch tokens then
-// attend the token's visible branch tokens (its scaffold up to itself, then
-// its trie ancestors).
+// Merge the split partials of each (token, head) whose request used more
+// than one split.
 struct TailCall {
     int dt;
     int32_t hd, n_heads, n_kv_heads, n_tokens;
-    const void *q;
-    const void *kb, *vb;     // branch K/V of this layer, [Hkv][cap][hd]
-    int32_t cap;
     const float *part_o;
     const float2 *part_ml;
     const int32_t *tok_req, *req_splits;  // branch: splits used by each request
     int32_t split_len;                    // prefill (> 0): token t has splits 0..t/split_len
-    const int32_t *fs, *nsc, *par;        // branch tokens; NULL for prefill
-    void *out;               // [tokens][Hq][hd]
+    void *out;                            // [tokens][Hq][hd]
 };
-void attention_tail(const TailCall &c, hipStream_t st);
+void attention_merge(const TailCall &c, hipStream_t st);
 
 // lse[r] from the per-tile partials of the readout GEMM.
 void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hipStream_t st);

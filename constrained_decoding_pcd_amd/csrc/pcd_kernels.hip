@@ -137,6 +137,15 @@ template <int N> __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// vm_wait<ahead * LPS> for a run-time ahead in [0, A]
+template <int LPS, int A> __device__ __forceinline__ void vm_wait_ahead(int ahead) {
+    if constexpr (A <= 0) {
+        vm_wait<0>();
+    } else {
+        if (ahead >= A) vm_wait<A * LPS>();
+        else vm_wait_ahead<LPS, A - 1>(ahead);
+    }
+}
 // wait until this wave's LDS reads have returned (lgkmcnt 0; vmcnt untouched)
 __device__ __forceinline__ void lds_reads_done() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
     static_assert((NW == 4 || NW == 8) && (KB == 128 || KB == 256), "workgroup shape");
     static_assert(A_INS * 64 * NW == BM * CPR && B_INS * 64 * NW == BN * CPR, "tile rows per DMA instruction");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(S >= 2 && S <= 4 && (S - 1) * LPS < 64, "pipeline depth");
+    static_assert(S >= 2 && S <= 8 && (S - 1) * LPS < 64, "pipeline depth");
     static_assert(S * STAGE <= 160 * 1024, "operand ring exceeds the 160 KB of LDS");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
@@ -278,19 +287,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
     // issued only after this wait)
     auto wait_stage = [&](int next) {
         const int ahead = min(next == 0 ? S - 1 : S - 2, nkt - 1 - next);
-        if constexpr (S >= 4) {
-            if (ahead >= 3) vm_wait<3 * LPS>();
-            else if (ahead == 2) vm_wait<2 * LPS>();
-            else if (ahead == 1) vm_wait<LPS>();
-            else vm_wait<0>();
-        } else if constexpr (S == 3) {
-            if (ahead >= 2) vm_wait<2 * LPS>();
-            else if (ahead == 1) vm_wait<LPS>();
-            else vm_wait<0>();
-        } else {
-            if (ahead >= 1) vm_wait<LPS>();
-            else vm_wait<0>();
-        }
+        vm_wait_ahead<LPS, S - 1>(ahead);
     };
     static_assert(KSTEPS % 2 == 0, "k-steps per stage must be even for the fragment ping-pong");
     using B0 = std::integral_constant<int, 0>;
@@ -593,45 +590,162 @@ void rmsnorm(int dt, const float *x, const int32_t *rows, int32_t n, int32_t d, 
 
 // One workgroup per row m: x[m] += sum over s of part[s][m] (s in increasing
 // order, so the result does not depend on scheduling), then, if w is given,
-// h[m] = rmsnorm(x[m]) * w as the next GEMM's input.
-template <typename T>
-__global__ __launch_bounds__(256) void k_resid_norm(const float *part, int32_t splits, int32_t M, int32_t N, float *x,
-                                                    const float *w, float eps, T *h) {
+// h[m] = rmsnorm(x[m]) * w as the next GEMM's input.  SMAX >= splits: the
+// loads of every split are issued together (splits beyond the real count
+// re-read the last one and add nothing), so a row costs one memory round
+// trip rather than one per split.  VEC2: N is a multiple of 512 and at most
+// 8192, each thread moves float2s.
+template <typename T, int SMAX, bool VEC2>
+__global__ __launch_bounds__(256) void k_resid_norm(const float *__restrict__ part, int32_t splits, int32_t M,
+                                                    int32_t N, float *__restrict__ x, const float *__restrict__ w,
+                                                    float eps, T *__restrict__ h) {
     __shared__ float red[4];
-    const int m = blockIdx.x;
+    const int m = blockIdx.x, tid = threadIdx.x;
     float *xr = x + (size_t)m * N;
+    const size_t pstride = (size_t)M * N;
+    const float *prow = part + (size_t)m * N;
     float ss = 0.f;
-    for (int j = threadIdx.x; j < N; j += 256) {
-        float v = xr[j];
-        for (int s = 0; s < splits; ++s) v += part[((size_t)s * M + m) * N + j];
-        xr[j] = v;
-        ss += v * v;
+    if constexpr (VEC2) {
+        constexpr int MAXE = 16;
+        const int ne = N / 512;
+        float2 acc[MAXE];
+#pragma unroll
+        for (int i = 0; i < MAXE; ++i) {
+            if (i >= ne) break;
+            const int j = tid + 256 * i;
+            float2 v = reinterpret_cast<const float2 *>(xr)[j];
+            float2 pv[SMAX];
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s)
+                pv[s] = reinterpret_cast<const float2 *>(prow + (size_t)min(s, splits - 1) * pstride)[j];
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s)
+                if (s < splits) {
+                    v.x += pv[s].x;
+                    v.y += pv[s].y;
+                }
+            acc[i] = v;
+            reinterpret_cast<float2 *>(xr)[j] = v;
+            ss += v.x * v.x + v.y * v.y;
+        }
+        if (!w) return;
+        ss = wave_sum(ss);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+        __syncthreads();
+        const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+#pragma unroll
+        for (int i = 0; i < MAXE; ++i) {
+            if (i >= ne) break;
+            const int j = 2 * (tid + 256 * i);
+            h[(size_t)m * N + j] = from_f<T>(acc[i].x * inv * w[j]);
+            h[(size_t)m * N + j + 1] = from_f<T>(acc[i].y * inv * w[j + 1]);
+        }
+    } else {
+        for (int j = tid; j < N; j += 256) {
+            float v = xr[j];
+            float pv[SMAX];
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s) pv[s] = prow[(size_t)min(s, splits - 1) * pstride + j];
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s)
+                if (s < splits) v += pv[s];
+            xr[j] = v;
+            ss += v * v;
+        }
+        if (!w) return;
+        ss = wave_sum(ss);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+        __syncthreads();
+        const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+        for (int j = tid; j < N; j += 256) h[(size_t)m * N + j] = from_f<T>(xr[j] * inv * w[j]);
     }
-    if (!w) return;
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
-    for (int j = threadIdx.x; j < N; j += 256) h[(size_t)m * N + j] = from_f<T>(xr[j] * inv * w[j]);
+}
+
+template <typename T, int SMAX>
+static void resid_norm_t(const float *part, int32_t splits, int32_t M, int32_t N, float *x, const float *w, float eps,
+                         void *h, hipStream_t st) {
+    if (N % 512 == 0 && N <= 8192)
+        hipLaunchKernelGGL((k_resid_norm<T, SMAX, true>), dim3(M), dim3(256), 0, st, part, splits, M, N, x, w, eps,
+                           (T *)h);
+    else
+        hipLaunchKernelGGL((k_resid_norm<T, SMAX, false>), dim3(M), dim3(256), 0, st, part, splits, M, N, x, w, eps,
+                           (T *)h);
+}
+template <typename T>
+static void resid_norm_s(const float *part, int32_t splits, int32_t M, int32_t N, float *x, const float *w, float eps,
+                         void *h, hipStream_t st) {
+    if (splits <= 1) resid_norm_t<T, 1>(part, splits, M, N, x, w, eps, h, st);
+    else if (splits <= 2) resid_norm_t<T, 2>(part, splits, M, N, x, w, eps, h, st);
+    else if (splits <= 4) resid_norm_t<T, 4>(part, splits, M, N, x, w, eps, h, st);
+    else resid_norm_t<T, 8>(part, splits, M, N, x, w, eps, h, st);
 }
 
 void resid_norm(int dt, const float *part, int32_t splits, int32_t M, int32_t N, float *x, const float *w, float eps,
                 void *h, hipStream_t st) {
     if (M <= 0) return;
-    if (dt == PCD_DT_F32)
-        hipLaunchKernelGGL(k_resid_norm<float>, dim3(M), dim3(256), 0, st, part, splits, M, N, x, w, eps, (float *)h);
-    else
-        hipLaunchKernelGGL(k_resid_norm<bf16_t>, dim3(M), dim3(256), 0, st, part, splits, M, N, x, w, eps,
-                           (bf16_t *)h);
+    if (dt == PCD_DT_F32) resid_norm_s<float>(part, splits, M, N, x, w, eps, h, st);
+    else resid_norm_s<bf16_t>(part, splits, M, N, x, w, eps, h, st);
 }
 
 // ---------------------------------------------------------------------------
-// attention over a KV cache: 64 query rows per workgroup (16 per wave), key
-// tiles of 64 staged in LDS once for all of them (K row-major, V transposed),
-// S^T = K Q^T on the matrix cores so that each lane holds 4 keys of one query
-// row, online softmax in base 2 with the row statistics reduced across the
-// four lane groups, then O += P V on the matrix cores.
+// Attention over KV caches: 64 query rows per workgroup (16 per wave); query
+// rows are (token, head within the KV group) pairs, so the heads of a GQA
+// group share every staged K/V tile.  Key tiles of 64 are double-buffered:
+// while the matrix cores work on tile i from LDS, tile i+1 is already on its
+// way from global memory into registers.  S^T = K Q^T on the matrix cores so
+// that each lane holds 4 keys of one query row; online softmax in base 2 with
+// the row statistics reduced across the four lane groups; O += P V on the
+// matrix cores.
+//
+// A block first walks its prefix keys [key0, key1) (causal for prefill), then
+// -- branch tokens only -- the branch keys [sfx_lo, sfx_hi) of the fields its
+// rows belong to, masked to each row's scaffold up to itself and its trie
+// ancestors.  One split: the block writes the final output; several: it
+// writes (max, sum, unnormalised O) partials for the merge kernel.
 // ---------------------------------------------------------------------------
+// Visibility of branch key k to branch token t, from t's field start fs,
+// scaffold length ns and its trie chain (itself, parent, ...): a scaffold key
+// is seen by every trie token of its field and by the scaffold tokens after
+// it; a trie key only by itself and its descendants.  The first 8 links of
+// the chain sit in registers; longer chains continue through memory.
+struct RowVis {
+    int t, fs, ns, nch, tail;  // tail: parent of the last stored link (-1: chain complete)
+    int chain[8];
+    bool trie;
+};
+__device__ __forceinline__ void row_vis_init(RowVis &v, const AttnCall &c, int t) {
+    v.t = t;
+    v.fs = c.fs[t];
+    v.ns = c.nsc[t];
+    v.trie = t >= v.fs + v.ns;
+    v.nch = 0;
+    v.tail = -1;
+    if (v.trie) {
+        int a = t;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v.chain[i] = a;
+            if (a >= 0) {
+                v.nch = i + 1;
+                a = c.par[a];
+            }
+        }
+        v.tail = a;
+    }
+}
+__device__ __forceinline__ bool row_vis_sees(const RowVis &v, const AttnCall &c, int k) {
+    if (k < v.fs) return false;
+    if (k < v.fs + v.ns) return v.trie || k <= v.t;
+    if (!v.trie) return false;
+    bool hit = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hit |= (i < v.nch && v.chain[i] == k);
+    if (hit || v.tail < 0) return hit;
+    int a = v.tail;
+    while (a > k) a = c.par[a];
+    return a == k;
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     constexpr int KT = 64;
@@ -640,8 +754,15 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     constexpr int LDV = KT + KPAD;    // V^T row stride
     constexpr int HS = HD / 32;       // k-steps of Q.K
     constexpr int CF = HD / 16;       // output column fragments
-    __shared__ __attribute__((aligned(16))) T Ks[KT * LDKS];
-    __shared__ __attribute__((aligned(16))) T Vt[HD * LDV];
+    constexpr int CH = 16 / sizeof(T);
+    constexpr int CHUNKS = KT * HD / CH;
+    constexpr int PER_T = CHUNKS / 256;  // 16-byte chunks per thread per tile (K and V each)
+    static_assert(PER_T * 256 == CHUNKS, "tile / thread mismatch");
+    extern __shared__ __attribute__((aligned(16))) char attn_lds[];
+    T *Ks0 = reinterpret_cast<T *>(attn_lds);
+    T *Vt0 = Ks0 + KT * LDKS;
+    T *Ks1 = Vt0 + HD * LDV;
+    T *Vt1 = Ks1 + KT * LDKS;
 
     const AttnBlock blk = c.blocks[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -650,13 +771,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     const T *kvbase = reinterpret_cast<const T *>(c.req_kv[blk.req]);
     const T *Kg = kvbase + ((size_t)c.layer * 2 * Hkv + blk.g) * (size_t)P * HD;
     const T *Vg = kvbase + ((size_t)c.layer * 2 * Hkv + Hkv + blk.g) * (size_t)P * HD;
+    const T *Kb = reinterpret_cast<const T *>(c.kb) + (size_t)blk.g * c.cap * HD;
+    const T *Vb = reinterpret_cast<const T *>(c.vb) + (size_t)blk.g * c.cap * HD;
     const T *Q = reinterpret_cast<const T *>(c.q);
     const float qscale = LOG2E / sqrtf((float)HD);
 
     // this lane's query row (B operand of S^T) and its token
-    const int my_row = blk.row0 + w * 16 + lr;
     const bool row_ok = (w * 16 + lr) < blk.nrows;
-    const int rr = row_ok ? my_row : blk.row0;
+    const int rr = row_ok ? blk.row0 + w * 16 + lr : blk.row0;
     const int tq = rr / grp, hq = blk.g * grp + rr % grp;
     Frag<T> qf[HS];
 #pragma unroll
@@ -668,40 +790,82 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
         const int last = (blk.row0 + blk.nrows - 1) / grp + 1;
         kmax = last < kmax ? last : kmax;
     }
+    const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;
+    const int n_sfx = blk.sfx_hi > blk.sfx_lo ? (blk.sfx_hi - blk.sfx_lo + KT - 1) / KT : 0;
+    const int n_tiles = n_pre + n_sfx;
+    RowVis vis{};
+    if (n_sfx > 0) row_vis_init(vis, c, tq);
+
+    // K chunks: 16 consecutive threads cover one key row (coalesced, row-major
+    // LDS store).  V chunks: the 64 lanes of a wave hold 64 consecutive keys of
+    // one column chunk, so the transposed LDS stores of a wave hit consecutive
+    // addresses.
+    uint4 rk[PER_T], rv[PER_T];
+    auto k_chunk = [&](int u, int &key, int &dc) {
+        const int ci = tid + u * 256;
+        key = ci / (HD / CH);
+        dc = (ci % (HD / CH)) * CH;
+    };
+    auto v_chunk = [&](int u, int &key, int &dc) {
+        const int ci = tid + u * 256;
+        key = ci % KT;
+        dc = (ci / KT) * CH;
+    };
+    auto gload = [&](int i) {
+        const bool sfx = i >= n_pre;
+        const int k0 = sfx ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
+        const int kl = sfx ? blk.sfx_hi : kmax;
+        const T *Ksrc = sfx ? Kb : Kg, *Vsrc = sfx ? Vb : Vg;
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+            int key, dc;
+            k_chunk(u, key, dc);
+            rk[u] = k0 + key < kl ? *reinterpret_cast<const uint4 *>(Ksrc + (size_t)(k0 + key) * HD + dc)
+                                  : make_uint4(0, 0, 0, 0);
+            v_chunk(u, key, dc);
+            rv[u] = k0 + key < kl ? *reinterpret_cast<const uint4 *>(Vsrc + (size_t)(k0 + key) * HD + dc)
+                                  : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto lstore = [&](T *Ks, T *Vt) {
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+            int key, dc;
+            k_chunk(u, key, dc);
+            *reinterpret_cast<uint4 *>(Ks + key * LDKS + dc) = rk[u];
+            v_chunk(u, key, dc);
+            const T *ve = reinterpret_cast<const T *>(&rv[u]);
+#pragma unroll
+            for (int e = 0; e < CH; ++e) Vt[(dc + e) * LDV + key] = ve[e];
+        }
+    };
 
     float m_run = -INFINITY, l_run = 0.f;  // stats of query row lr (replicated over lg)
     f32x4 o[CF];
 #pragma unroll
     for (int j = 0; j < CF; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int CH = 16 / sizeof(T);
-    constexpr int CHUNKS = KT * HD / CH;
-    for (int k0 = blk.key0; k0 < kmax; k0 += KT) {
-        // stage K (row-major) and V (transposed); keys past kmax are zero
-        for (int ci = tid; ci < CHUNKS; ci += 256) {
-            const int key = ci / (HD / CH), dc = (ci % (HD / CH)) * CH;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (k0 + key < kmax) {
-                kv = *reinterpret_cast<const uint4 *>(Kg + (size_t)(k0 + key) * HD + dc);
-                vv = *reinterpret_cast<const uint4 *>(Vg + (size_t)(k0 + key) * HD + dc);
-            }
-            *reinterpret_cast<uint4 *>(Ks + key * LDKS + dc) = kv;
-            const T *ve = reinterpret_cast<const T *>(&vv);
-#pragma unroll
-            for (int i = 0; i < CH; ++i) Vt[(dc + i) * LDV + key] = ve[i];
-        }
-        __syncthreads();
+    if (n_tiles > 0) {
+        gload(0);
+        lstore(Ks0, Vt0);
+    }
+    __syncthreads();
+    for (int i = 0; i < n_tiles; ++i) {
+        T *Ks = (i & 1) ? Ks1 : Ks0, *Vt = (i & 1) ? Vt1 : Vt0;
+        if (i + 1 < n_tiles) gload(i + 1);
+        const bool sfx = i >= n_pre;
+        const int k0 = sfx ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
 
-        // S^T tile: s[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r)
-        f32x4 s[KT / 16];
+        // S^T tile: sc[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r)
+        f32x4 sc[KT / 16];
 #pragma unroll
         for (int kf = 0; kf < KT / 16; ++kf) {
-            s[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sc[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < HS; ++st) {
                 Frag<T> kf8;
                 ld8(kf8, Ks + (kf * 16 + lr) * LDKS + st * 32 + lg * 8);
-                mma(s[kf], kf8, qf[st]);
+                mma(sc[kf], kf8, qf[st]);
             }
         }
         float mx = -INFINITY;
@@ -710,8 +874,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = k0 + kf * 16 + lg * 4 + r;
-                const float v = (key < kend_row) ? s[kf][r] * qscale : -INFINITY;
-                s[kf][r] = v;
+                bool see;
+                if (!sfx) see = key < kend_row;
+                else see = row_ok && key < blk.sfx_hi && row_vis_sees(vis, c, key);
+                const float v = see ? sc[kf][r] * qscale : -INFINITY;
+                sc[kf][r] = v;
                 mx = fmaxf(mx, v);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -720,13 +887,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
         const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_ref);
         float psum = 0.f;
-        float p[KT / 16][4];
+        float pr[KT / 16][4];
 #pragma unroll
         for (int kf = 0; kf < KT / 16; ++kf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[kf][r] = exp2f(s[kf][r] - m_ref);
-                psum += p[kf][r];
+                pr[kf][r] = exp2f(sc[kf][r] - m_ref);
+                psum += pr[kf][r];
             }
         psum += __shfl_xor(psum, 16);
         psum += __shfl_xor(psum, 32);
@@ -746,8 +913,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
             float pv[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pv[r] = p[2 * st][r];
-                pv[4 + r] = p[2 * st + 1][r];
+                pv[r] = pr[2 * st][r];
+                pv[4 + r] = pr[2 * st + 1][r];
             }
             Frag<T> pa;
             from8(pa, pv);
@@ -759,6 +926,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
                 mma(o[j], pa, vb);
             }
         }
+        // tile i+1 goes into the other buffer, last read during iteration i-1
+        if (i + 1 < n_tiles) lstore((i & 1) ? Ks0 : Ks1, (i & 1) ? Vt0 : Vt1);
         __syncthreads();
     }
 
@@ -772,30 +941,46 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
         const int row = blk.row0 + w * 16 + qi;
         const int t = row / grp, h = blk.g * grp + row % grp;
         if (c.causal && t < blk.key0) continue;  // causal row with no key in this split
-        if (c.out) {
+        // a causal row whose keys all lie in split 0 has no partials to merge
+        if (blk.nsplit == 1 || (c.causal && blk.split == 0 && t < blk.key1)) {
             T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
             const float inv = 1.0f / lq;
 #pragma unroll
             for (int j = 0; j < CF; ++j) out[j * 16 + lr] = from_f<T>(o[j][r] * inv);
         } else {
-            const size_t pr = ((size_t)blk.split * c.n_tokens + t) * Hq + h;
-            float *po = c.part_o + pr * HD;
+            const size_t pi = ((size_t)blk.split * c.n_tokens + t) * Hq + h;
+            float *po = c.part_o + pi * HD;
 #pragma unroll
             for (int j = 0; j < CF; ++j) po[j * 16 + lr] = o[j][r];
-            if (lr == 0) c.part_ml[pr] = make_float2(mq, lq);
+            if (lr == 0) c.part_ml[pi] = make_float2(mq, lq);
         }
     }
+}
+
+template <typename T, int HD> static int attn_lds_bytes() {
+    constexpr int KPAD = 16 / sizeof(T);
+    return 2 * (64 * (HD + KPAD) + HD * (64 + KPAD)) * (int)sizeof(T);
+}
+
+template <typename T, int HD> static void launch_attn(const AttnCall &c, hipStream_t st) {
+    const int shmem = attn_lds_bytes<T, HD>();
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_attn<T, HD>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_attn<T, HD>), dim3(c.n_blocks), dim3(256), shmem, st, c);
 }
 
 template <typename T> static bool attention_t(const AttnCall &c, hipStream_t st) {
     if (c.n_blocks <= 0) return true;
     switch (c.hd) {
-        case 32: hipLaunchKernelGGL((k_attn<T, 32>), dim3(c.n_blocks), dim3(256), 0, st, c); return true;
-        case 64: hipLaunchKernelGGL((k_attn<T, 64>), dim3(c.n_blocks), dim3(256), 0, st, c); return true;
+        case 32: launch_attn<T, 32>(c, st); return true;
+        case 64: launch_attn<T, 64>(c, st); return true;
         case 128:
-            // an fp32 128-wide K/V tile pair does not fit the static LDS limit
             if constexpr (sizeof(T) == 2) {
-                hipLaunchKernelGGL((k_attn<T, 128>), dim3(c.n_blocks), dim3(256), 0, st, c);
+                launch_attn<T, 128>(c, st);
                 return true;
             }
             return false;
@@ -806,67 +991,33 @@ bool attention(const AttnCall &c, hipStream_t st) {
     return c.dt == PCD_DT_F32 ? attention_t<float>(c, st) : attention_t<bf16_t>(c, st);
 }
 
-// One wavefront per (branch token, query head): merge the prefix partials,
-// then the visible branch keys, one at a time.
+// Merge the split partials of each (token, head) of the requests that used
+// more than one split: m = max, l = sum l_s 2^(m_s - m), O = sum O_s 2^(m_s - m).
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attn_tail(TailCall c) {
-    constexpr int PL = (HD + 63) / 64;  // dims per lane
+__global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
+    constexpr int PL = (HD + 63) / 64;
     const int lane = threadIdx.x & 63;
     const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
+    const int Hq = c.n_heads;
     if (id >= c.n_tokens * Hq) return;
-    const int t = id / Hq, h = id % Hq, g = h / grp;
-    const float qscale = LOG2E / sqrtf((float)HD);
-
-    float m = -INFINITY, l = 0.f, o[PL], q[PL];
-    // prefill: token t has keys 0..t, so splits 0..t/split_len; branch: its request's count
+    const int t = id / Hq, h = id % Hq;
     const int ns = c.split_len > 0 ? t / c.split_len + 1 : c.req_splits[c.tok_req[t]];
-    const T *Q = reinterpret_cast<const T *>(c.q) + ((size_t)t * Hq + h) * HD;
+    if (ns <= 1) return;  // written directly by the attention kernel
+    float m = -INFINITY, l = 0.f, o[PL];
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-        const int d = lane + 64 * i;
-        o[i] = 0.f;
-        q[i] = d < HD ? to_f(Q[d]) : 0.f;
-    }
+    for (int i = 0; i < PL; ++i) o[i] = 0.f;
     for (int s = 0; s < ns; ++s) {
-        const size_t pr = ((size_t)s * c.n_tokens + t) * Hq + h;
-        const float2 ml = c.part_ml[pr];
+        const size_t pi = ((size_t)s * c.n_tokens + t) * Hq + h;
+        const float2 ml = c.part_ml[pi];
         const float mn = fmaxf(m, ml.x);
         const float a = exp2f(m - mn), b = exp2f(ml.x - mn);
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
             const int d = lane + 64 * i;
-            if (d < HD) o[i] = o[i] * a + c.part_o[pr * HD + d] * b;
+            if (d < HD) o[i] = o[i] * a + c.part_o[pi * HD + d] * b;
         }
         l = l * a + ml.y * b;
         m = mn;
-    }
-    const T *Kb = reinterpret_cast<const T *>(c.kb) + (size_t)g * c.cap * HD;
-    const T *Vb = reinterpret_cast<const T *>(c.vb) + (size_t)g * c.cap * HD;
-    auto visit = [&](int k) {
-        float sdot = 0.f;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            const int d = lane + 64 * i;
-            if (d < HD) sdot += q[i] * to_f(Kb[(size_t)k * HD + d]);
-        }
-        const float sc = wave_sum(sdot) * qscale;
-        const float mn = fmaxf(m, sc);
-        const float a = exp2f(m - mn), b = exp2f(sc - mn);
-#pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            const int d = lane + 64 * i;
-            if (d < HD) o[i] = o[i] * a + to_f(Vb[(size_t)k * HD + d]) * b;
-        }
-        l = l * a + b;
-        m = mn;
-    };
-    if (c.fs) {
-        const int fs = c.fs[t], nsc = c.nsc[t];
-        const int sc_end = (t < fs + nsc) ? t : fs + nsc - 1;  // scaffold tokens up to itself
-        for (int k = fs; k <= sc_end; ++k) visit(k);
-        if (t >= fs + nsc)
-            for (int k = t; k >= 0; k = c.par[k]) visit(k);  // itself, then its trie ancestors
     }
     T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
     const float inv = 1.0f / l;
@@ -877,19 +1028,19 @@ __global__ __launch_bounds__(256) void k_attn_tail(TailCall c) {
     }
 }
 
-template <typename T> static void tail_t(const TailCall &c, hipStream_t st) {
+template <typename T> static void merge_t(const TailCall &c, hipStream_t st) {
     const int waves = c.n_tokens * c.n_heads;
     if (waves <= 0) return;
     const dim3 grid((waves + 3) / 4);
     switch (c.hd) {
-        case 32: hipLaunchKernelGGL((k_attn_tail<T, 32>), grid, dim3(256), 0, st, c); break;
-        case 64: hipLaunchKernelGGL((k_attn_tail<T, 64>), grid, dim3(256), 0, st, c); break;
-        case 128: hipLaunchKernelGGL((k_attn_tail<T, 128>), grid, dim3(256), 0, st, c); break;
+        case 32: hipLaunchKernelGGL((k_attn_merge<T, 32>), grid, dim3(256), 0, st, c); break;
+        case 64: hipLaunchKernelGGL((k_attn_merge<T, 64>), grid, dim3(256), 0, st, c); break;
+        case 128: hipLaunchKernelGGL((k_attn_merge<T, 128>), grid, dim3(256), 0, st, c); break;
     }
 }
-void attention_tail(const TailCall &c, hipStream_t st) {
-    if (c.dt == PCD_DT_F32) tail_t<float>(c, st);
-    else tail_t<bf16_t>(c, st);
+void attention_merge(const TailCall &c, hipStream_t st) {
+    if (c.dt == PCD_DT_F32) merge_t<float>(c, st);
+    else merge_t<bf16_t>(c, st);
 }
 
 // ---------------------------------------------------------------------------
