@@ -144,8 +144,17 @@ struct pcd_model {
     std::vector<const float *> an, mn;
     char *plan_host = nullptr;  // pinned staging for the plan upload
     char *outs_host = nullptr;  // pinned staging for the results
-    hipEvent_t ev[5] = {};
+    hipEvent_t ev[6] = {};  // branch start/end, readout end, prefill start/end, plan upload done
     pcd_stats stats{};
+    bool prefill_pending = false;  // last_prefill_ms not yet read from ev[3], ev[4]
+    // fold a finished prefill's event time into the stats (waits for it)
+    void settle_prefill() {
+        if (!prefill_pending) return;
+        prefill_pending = false;
+        float ms = 0.f;
+        if (hipEventSynchronize(ev[4]) == hipSuccess && hipEventElapsedTime(&ms, ev[3], ev[4]) == hipSuccess)
+            stats.last_prefill_ms = ms;
+    }
     int n_states = 0;
     // per-kernel-class timing
     bool timing = false;
@@ -420,8 +429,9 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
     const int32_t *d_len = pk.put(&n, 1);
     const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
     if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
+    m->settle_prefill();
     HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
-    m->tused = 0;
+    HIP_TRY(hipEventRecord(m->ev[5], st));
     HIP_TRY(hipEventRecord(m->ev[3], st));
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     m->tbegin(PCD_KC_OTHER, st);
@@ -474,11 +484,14 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
     }
     HIP_TRY(hipEventRecord(m->ev[4], st));
     HIP_TRY(hipGetLastError());
-    HIP_TRY(hipStreamSynchronize(st));
-    m->tcollect();
-    float ms = 0.f;
-    (void)hipEventElapsedTime(&ms, m->ev[3], m->ev[4]);
-    m->stats.last_prefill_ms = ms;
+    // The pass stays in flight: only the plan upload must have left the
+    // pinned staging buffer before the next call refills it.
+    HIP_TRY(hipEventSynchronize(m->ev[5]));
+    m->prefill_pending = true;
+    if (m->timing) {
+        HIP_TRY(hipStreamSynchronize(st));
+        m->tcollect();
+    }
     m->stats.prefill_passes += 1;
     pcd_state *s = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_buf, n};
     if (!s) return fail(PCD_E_NOMEM, "state allocation");
@@ -618,7 +631,6 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     if (oo > m->L.outs_bytes) return fail(PCD_E_CAP, "output staging overflow");
 
     HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
-    m->tused = 0;
     HIP_TRY(hipEventRecord(m->ev[0], st));
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     m->tbegin(PCD_KC_OTHER, st);
@@ -728,6 +740,7 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     HIP_TRY(hipMemcpyAsync(m->outs_host, ob, oo, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     m->tcollect();
+    m->settle_prefill();
 
     const char *oh = m->outs_host;
     for (int r = 0; r < n_req; ++r) {
@@ -765,6 +778,7 @@ int pcd_decide(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pc
 
 int pcd_get_stats(const pcd_model *m, pcd_stats *out) {
     if (!m || !out) return fail(PCD_E_ARG, "null argument");
+    const_cast<pcd_model *>(m)->settle_prefill();
     *out = m->stats;
     return PCD_OK;
 }
@@ -798,6 +812,7 @@ void pcd_free_state(pcd_state *s) {
 
 void pcd_free_model(pcd_model *m) {
     if (!m) return;
+    m->settle_prefill();
     if (m->plan_host) (void)hipHostFree(m->plan_host);
     if (m->outs_host) (void)hipHostFree(m->outs_host);
     for (auto &e : m->ev)

@@ -178,7 +178,13 @@ size_t pcd_state_bytes(const pcd_model *m, int32_t n_tokens);
  * caller's device buffer kv_buf (kv_bytes >= pcd_state_bytes).  No final norm
  * and no LM head are run ("The idea: parallel constrained decoding", step 1:
  * the shared prompt is read once).  On success *out is a new state handle
- * that borrows kv_buf. */
+ * that borrows kv_buf.  The call returns once the pass is enqueued on
+ * `stream` (it waits only for its small host-to-device plan upload), so the
+ * host can prepare the decide call while the device runs the prefill: kv_buf
+ * is complete when `stream` reaches the end of this call's work.  Decide
+ * calls on the same stream are ordered after it; other streams must wait on
+ * it first.  last_prefill_ms in pcd_get_stats is read when the pass has
+ * finished (pcd_get_stats waits for it). */
 int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n_tokens, void *kv_buf, size_t kv_bytes,
                 void *stream, pcd_state **out);
 
