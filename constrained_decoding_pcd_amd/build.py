@@ -11,9 +11,13 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpcd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# packed fp32 instructions stay off; the compiler would otherwise form them from float2 code
+# packed fp32 instructions stay off; the compiler would otherwise form them from float2 code.
+# Matrix-core accumulators live in ordinary VGPRs: with the accumulation
+# registers the allocator moved partial sums between them around every
+# matrix instruction of the unrolled loops, serialising them.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-variable"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall", "-Wno-unused-variable"]
 
 
 def _run(cmd):
