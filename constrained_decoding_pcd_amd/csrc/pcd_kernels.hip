@@ -514,11 +514,17 @@ template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
                 else if (c.K >= 4096) gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
                 else gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
                 return true;
-            case Epi::SwiGlu:
+            case Epi::SwiGlu: {
+                // the big 128-row tiles only when one round of workgroups covers the product:
+                // a second, mostly idle round costs as much as the first
+                const int rows = (c.M + 127) / 128;
                 if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
-                else if (rg == Reg::Medium) launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
+                else if (rows * (c.N / 128) <= 256) launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
+                else if (c.N % 160 == 0 && rows * (c.N / 160) <= 256)
+                    launch_gemm<T, 128, 160, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
                 else launch_gemm<T, 64, 64, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
                 return true;
+            }
             case Epi::Partial:
                 return false;  // chosen internally by Resid
         }
