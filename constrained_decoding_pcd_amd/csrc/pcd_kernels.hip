@@ -31,12 +31,9 @@ __device__ __forceinline__ float to_f(bf16_t v) { return __uint_as_float(((uint3
 
 template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
-template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;  // NaN stays NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                // round to nearest, ties to even
-    return (bf16_t)(u >> 16);
-}
+// round to nearest, ties to even: one v_cvt_pk_bf16_f32 on gfx950 (two values
+// per instruction where the compiler can pair them)
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return __builtin_bit_cast(bf16_t, (__bf16)v); }
 
 // 8 consecutive elements of one MFMA operand row/column
 template <typename T> struct Frag;
@@ -89,6 +86,27 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Reductions across the four 16-lane rows of a wave with gfx950's row swaps
+// (no LDS round trip): v_permlane16_swap pairs rows (0,1) and (2,3),
+// v_permlane32_swap pairs the two halves; combining a value with its swapped
+// copies leaves the result for its 16-lane column in every row.
+__device__ __forceinline__ float rows_max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(v);
+    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+    const uint32_t u = __float_as_uint(v);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __float_as_uint(v);
+    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -124,7 +142,7 @@ struct EpiArgs {
     float *g_logit;
 };
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // 16 bytes per lane from global memory into LDS at lds_addr + 16 * lane.
 // Issued from inline assembly so that the compiler does not add a wait for
@@ -862,17 +880,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
         const bool sfx = i >= n_pre;
         const int k0 = sfx ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
 
-        // S^T tile: sc[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r)
+        // S^T tile: sc[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r).  Every
+        // K fragment of the tile is read before the first multiply, and the
+        // multiplies interleave four independent accumulators.
         f32x4 sc[KT / 16];
+        {
+            Frag<T> kfr[KT / 16][HS];
 #pragma unroll
-        for (int kf = 0; kf < KT / 16; ++kf) {
-            sc[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kf = 0; kf < KT / 16; ++kf)
 #pragma unroll
-            for (int st = 0; st < HS; ++st) {
-                Frag<T> kf8;
-                ld8(kf8, Ks + (kf * 16 + lr) * LDKS + st * 32 + lg * 8);
-                mma(sc[kf], kf8, qf[st]);
-            }
+                for (int st = 0; st < HS; ++st) ld8(kfr[kf][st], Ks + (kf * 16 + lr) * LDKS + st * 32 + lg * 8);
+            __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the multiplies
+#pragma unroll
+            for (int kf = 0; kf < KT / 16; ++kf) sc[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < HS; ++st)
+#pragma unroll
+                for (int kf = 0; kf < KT / 16; ++kf) mma(sc[kf], kfr[kf][st], qf[st]);
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -887,22 +911,20 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
                 sc[kf][r] = v;
                 mx = fmaxf(mx, v);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = rows_max(mx);
         const float m_new = fmaxf(m_run, mx);
         const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_ref);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
         float psum = 0.f;
         float pr[KT / 16][4];
 #pragma unroll
         for (int kf = 0; kf < KT / 16; ++kf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[kf][r] = exp2f(sc[kf][r] - m_ref);
+                pr[kf][r] = __builtin_amdgcn_exp2f(sc[kf][r] - m_ref);
                 psum += pr[kf][r];
             }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
+        // this lane's share of the row sum; the four shares are added at the end
         l_run = l_run * alpha + psum;
         m_run = m_new;
 
@@ -913,23 +935,30 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
 #pragma unroll
             for (int j = 0; j < CF; ++j) o[j][r] *= a;
         }
-        // O += P V over two 32-key steps; A = P (row lr, keys {4lg..4lg+3} and {16+4lg..}), B = V
+        // O += P V over two 32-key steps; A = P (row lr, keys {4lg..4lg+3} and {16+4lg..}), B = V.
+        // All V fragments are read first.
+        {
+            Frag<T> vfr[KT / 32][CF];
 #pragma unroll
-        for (int st = 0; st < KT / 32; ++st) {
-            float pv[8];
+            for (int st = 0; st < KT / 32; ++st)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pv[r] = pr[2 * st][r];
-                pv[4 + r] = pr[2 * st + 1][r];
-            }
-            Frag<T> pa;
-            from8(pa, pv);
+                for (int j = 0; j < CF; ++j) {
+                    const T *vrow = Vt + (j * 16 + lr) * LDV + st * 32 + lg * 4;
+                    ld4x2(vfr[st][j], vrow, vrow + 16);
+                }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < CF; ++j) {
-                Frag<T> vb;
-                const T *vrow = Vt + (j * 16 + lr) * LDV + st * 32 + lg * 4;
-                ld4x2(vb, vrow, vrow + 16);
-                mma(o[j], pa, vb);
+            for (int st = 0; st < KT / 32; ++st) {
+                float pv[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pv[r] = pr[2 * st][r];
+                    pv[4 + r] = pr[2 * st + 1][r];
+                }
+                Frag<T> pa;
+                from8(pa, pv);
+#pragma unroll
+                for (int j = 0; j < CF; ++j) mma(o[j], pa, vfr[st][j]);
             }
         }
         // tile i+1 goes into the other buffer, last read during iteration i-1
@@ -937,6 +966,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
         __syncthreads();
     }
 
+    l_run = rows_sum(l_run);
     // write: O row 4*lg + r of this wave
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1016,7 +1046,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
         const size_t pi = ((size_t)s * c.n_tokens + t) * Hq + h;
         const float2 ml = c.part_ml[pi];
         const float mn = fmaxf(m, ml.x);
-        const float a = exp2f(m - mn), b = exp2f(ml.x - mn);
+        const float a = __builtin_amdgcn_exp2f(m - mn), b = __builtin_amdgcn_exp2f(ml.x - mn);
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
             const int d = lane + 64 * i;
