@@ -99,7 +99,7 @@ Layout layout(const pcd_config &c, const pcd_limits &l) {
     L.z = take((size_t)l.max_gathers * 4);
     L.outs_bytes = align_up((size_t)(2 * l.max_candidates + 3 * l.max_fields + l.max_readouts + l.max_gathers) * 4 + 8 * 256);
     L.outs = take(L.outs_bytes);
-    const int64_t ints = 6 * (int64_t)rows + 2 * (int64_t)l.max_readouts + 2 + 2 * (int64_t)l.max_gathers +
+    const int64_t ints = 6 * (int64_t)rows + 8 * (int64_t)l.max_branch_tokens + 2 * (int64_t)l.max_readouts + 2 + 2 * (int64_t)l.max_gathers +
                          2 * (int64_t)l.max_fields + 1 + (int64_t)l.max_candidates + 1 + path_cap(l) +
                          2 * (int64_t)l.max_requests;
     L.plan_bytes = align_up((size_t)ints * 4 + 20 * 256) + align_up((size_t)l.max_requests * 8) +
@@ -603,6 +603,18 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     const int32_t *d_fs = pk.put(p.fs.data(), Tb);
     const int32_t *d_nsc = pk.put(p.nsc.data(), Tb);
     const int32_t *d_par = pk.put(p.par.data(), Tb);
+    // the first 8 links of every trie token's chain (itself, parent, ...), so
+    // the attention kernel reads them with two independent loads
+    std::vector<int32_t> chain((size_t)8 * Tb, -1);
+    for (int t = 0; t < Tb; ++t) {
+        if (t < p.fs[t] + p.nsc[t]) continue;  // scaffold token: no chain
+        int a = t;
+        for (int i = 0; i < 8 && a >= 0; ++i) {
+            chain[(size_t)8 * t + i] = a;
+            a = p.par[a];
+        }
+    }
+    const int4 *d_chain = reinterpret_cast<const int4 *>(pk.put(chain.data(), chain.size()));
     const int32_t *d_ro = pk.put(p.ro_tok.data(), R);
     const int32_t *d_goff = pk.put(p.g_off.data(), R + 1);
     const int32_t *d_gtok = pk.put(p.g_tok.data(), G);
@@ -665,6 +677,7 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
             a.fs = d_fs;
             a.nsc = d_nsc;
             a.par = d_par;
+            a.chain = d_chain;
             m->tbegin(PCD_KC_BRANCH_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);

@@ -91,6 +91,7 @@ struct AttnCall {
     const void *kb, *vb;    // branch K/V of this layer, [Hkv][cap][hd] (branch pass only)
     int32_t cap;
     const int32_t *fs, *nsc, *par;  // per branch token: field start, scaffold length, trie parent
+    const int4 *chain;              // per branch token: 8 links of its trie chain (itself, parent, ...; -1 past the root)
 };
 bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
 

@@ -731,7 +731,8 @@ void resid_norm(int dt, const float *part, int32_t splits, int32_t M, int32_t N,
 // scaffold length ns and its trie chain (itself, parent, ...): a scaffold key
 // is seen by every trie token of its field and by the scaffold tokens after
 // it; a trie key only by itself and its descendants.  The first 8 links of
-// the chain sit in registers; longer chains continue through memory.
+// the chain come from the plan's chain table (two independent loads) and sit
+// in registers; longer chains continue through the parent links in memory.
 struct RowVis {
     int t, fs, ns, nch, tail;  // tail: parent of the last stored link (-1: chain complete)
     int chain[8];
@@ -745,16 +746,14 @@ __device__ __forceinline__ void row_vis_init(RowVis &v, const AttnCall &c, int t
     v.nch = 0;
     v.tail = -1;
     if (v.trie) {
-        int a = t;
+        const int4 a = c.chain[2 * t], b = c.chain[2 * t + 1];
+        const int ch[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            v.chain[i] = a;
-            if (a >= 0) {
-                v.nch = i + 1;
-                a = c.par[a];
-            }
+            v.chain[i] = ch[i];
+            if (ch[i] >= 0) v.nch = i + 1;
         }
-        v.tail = a;
+        v.tail = v.chain[7] >= 0 ? c.par[v.chain[7]] : -1;
     }
 }
 __device__ __forceinline__ bool row_vis_sees(const RowVis &v, const AttnCall &c, int k) {
