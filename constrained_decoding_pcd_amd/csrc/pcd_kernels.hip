@@ -769,6 +769,39 @@ __device__ __forceinline__ bool row_vis_sees(const RowVis &v, const AttnCall &c,
     return a == k;
 }
 
+// Output of one attention workgroup: O row 4*lg + r of wave w, normalised
+// when the row has no other split, else (unnormalised O, max, sum) partials
+// for the merge kernel.  l is the row's full sum (replicated over lg).
+template <typename T, int HD>
+__device__ __forceinline__ void attn_write(const AttnCall &c, const AttnBlock &blk, const f32x4 (&o)[HD / 16],
+                                           float m_run, float l_run, int w, int lr, int lg) {
+    constexpr int CF = HD / 16;
+    const int Hq = c.n_heads, grp = Hq / c.n_kv_heads;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int qi = lg * 4 + r;
+        const float lq = __shfl(l_run, qi);
+        const float mq = __shfl(m_run, qi);
+        if (w * 16 + qi >= blk.nrows) continue;
+        const int row = blk.row0 + w * 16 + qi;
+        const int t = row / grp, h = blk.g * grp + row % grp;
+        if (c.causal && t < blk.key0) continue;  // causal row with no key in this split
+        // a causal row whose keys all lie in split 0 has no partials to merge
+        if (blk.nsplit == 1 || (c.causal && blk.split == 0 && t < blk.key1)) {
+            T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
+            const float inv = 1.0f / lq;
+#pragma unroll
+            for (int j = 0; j < CF; ++j) out[j * 16 + lr] = from_f<T>(o[j][r] * inv);
+        } else {
+            const size_t pi = ((size_t)blk.split * c.n_tokens + t) * Hq + h;
+            float *po = c.part_o + pi * HD;
+#pragma unroll
+            for (int j = 0; j < CF; ++j) po[j * 16 + lr] = o[j][r];
+            if (lr == 0) c.part_ml[pi] = make_float2(mq, lq);
+        }
+    }
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     constexpr int KT = 64;
@@ -965,31 +998,259 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
         __syncthreads();
     }
 
-    l_run = rows_sum(l_run);
-    // write: O row 4*lg + r of this wave
+    attn_write<T, HD>(c, blk, o, m_run, rows_sum(l_run), w, lr, lg);
+}
+
+// ---------------------------------------------------------------------------
+// Attention for 16-bit types.  Same rows, keys, masks and outputs as k_attn,
+// but the operands never pass through registers on their way to LDS: the
+// 64 query rows and every (K, V) tile of 64 keys are copied by LDS-DMA
+// (global_load_lds_dwordx4), the key tiles through an S-stage ring so that
+// S-1 tiles are in flight while the matrix cores work on the current one.
+// A DMA instruction writes 1 KB linearly, so the LDS tiles are unpadded and
+// bank conflicts are avoided by permuting the 16-byte chunks of each row:
+// K and Q rows keep chunk c at c ^ (row % CPR), which spreads the 16 rows of
+// an MFMA fragment read over all banks; V rows keep chunk c at
+// c ^ (2*row % CPR), which does the same for the 4 rows of gfx950's LDS
+// transpose read (ds_read_b64_tr_b16) that delivers V's MFMA fragments.
+// ---------------------------------------------------------------------------
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+// Four 16-bit values by the LDS transpose read: within each 16-lane row of
+// the wave, lane j names 8 bytes (4 values); lane i receives value i % 4 of
+// the groups named by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12.
+__device__ __forceinline__ short4_t lds_tr4(const char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t *)(__attribute__((address_space(3))) const char *)p);
+}
+
+// A row's running maximum is raised (and its partial sums rescaled) only when
+// a tile's maximum exceeds it by more than this many powers of two; between
+// raises the exponentials stay below 2^RESCALE_LOG2, which bf16 holds at full
+// relative precision, and the normalised result is the same softmax.
+constexpr float RESCALE_LOG2 = 8.0f;
+#ifndef ATT_RING_STAGES
+#define ATT_RING_STAGES 3
+#endif
+
+template <int HD> struct RingLds {
+    static constexpr int KT = 64, RB = HD * 2, CPR = RB / 16, TILE = KT * RB;
+    static constexpr int Q_BYTES = TILE;  // 64 query rows
+    static int bytes(int S) { return Q_BYTES + S * 2 * TILE; }
+};
+
+template <int HD, int S>
+__global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
+    using T = bf16_t;
+    using L = RingLds<HD>;
+    constexpr int KT = L::KT, RB = L::RB, CPR = L::CPR, TILE = L::TILE, STAGE = 2 * TILE;
+    constexpr int INS = TILE / (4 * 1024);  // DMA instructions per wave per tile
+    constexpr int LPS = 2 * INS;            // per (K, V) stage
+    constexpr int HS = HD / 32, CF = HD / 16;
+    static_assert(INS >= 1 && INS * 4 * 1024 == TILE, "tile / DMA mapping");
+    static_assert(S >= 2 && (S - 1) * LPS + INS < 64, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) char attn_lds[];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)attn_lds;
+    const char *Qs = attn_lds;
+    const uint32_t ring_base = lds_base + L::Q_BYTES;
+
+    const AttnBlock blk = c.blocks[blockIdx.x];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
+    const int P = c.req_len[blk.req];
+    const char *kvbase = reinterpret_cast<const char *>(c.req_kv[blk.req]);
+    const char *Kg = kvbase + ((size_t)c.layer * 2 * Hkv + blk.g) * (size_t)P * RB;
+    const char *Vg = kvbase + ((size_t)c.layer * 2 * Hkv + Hkv + blk.g) * (size_t)P * RB;
+    const char *Kb = reinterpret_cast<const char *>(c.kb) + (size_t)blk.g * c.cap * RB;
+    const char *Vb = reinterpret_cast<const char *>(c.vb) + (size_t)blk.g * c.cap * RB;
+    const float qscale = LOG2E / sqrtf((float)HD);
+
+    // this lane's query row (B operand of S^T) and its token
+    const bool row_ok = (w * 16 + lr) < blk.nrows;
+    const int rr = row_ok ? blk.row0 + w * 16 + lr : blk.row0;
+    const int tq = rr / grp;
+    const int kend_row = c.causal ? min(tq + 1, blk.key1) : blk.key1;
+    int kmax = blk.key1;
+    if (c.causal) {
+        const int last = (blk.row0 + blk.nrows - 1) / grp + 1;
+        kmax = last < kmax ? last : kmax;
+    }
+    const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;
+    const int n_sfx = blk.sfx_hi > blk.sfx_lo ? (blk.sfx_hi - blk.sfx_lo + KT - 1) / KT : 0;
+    const int n_tiles = n_pre + n_sfx;
+    RowVis vis{};
+    if (n_sfx > 0) {
+        row_vis_init(vis, c, tq);
+        vm_wait<0>();  // its loads must not sit in the counter behind the DMA below
+    }
+
+    // DMA slots of this lane: 16-byte unit p = (i*4 + w)*64 + lane of a tile,
+    // row p / CPR, physical chunk p % CPR, logical chunk per the row permutation
+    int drow[INS], dck[INS], dcv[INS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int qi = lg * 4 + r;
-        const float lq = __shfl(l_run, qi);
-        const float mq = __shfl(m_run, qi);
-        if (w * 16 + qi >= blk.nrows) continue;
-        const int row = blk.row0 + w * 16 + qi;
-        const int t = row / grp, h = blk.g * grp + row % grp;
-        if (c.causal && t < blk.key0) continue;  // causal row with no key in this split
-        // a causal row whose keys all lie in split 0 has no partials to merge
-        if (blk.nsplit == 1 || (c.causal && blk.split == 0 && t < blk.key1)) {
-            T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
-            const float inv = 1.0f / lq;
+    for (int i = 0; i < INS; ++i) {
+        const int p = (i * 4 + w) * 64 + lane, pc = p % CPR;
+        drow[i] = p / CPR;
+        dck[i] = pc ^ (drow[i] & (CPR - 1));
+        dcv[i] = pc ^ ((2 * drow[i]) & (CPR - 1));
+    }
+    // query rows: (token, head) pairs of this block; rows past nrows re-read row0
+    {
+        const char *Q = reinterpret_cast<const char *>(c.q);
 #pragma unroll
-            for (int j = 0; j < CF; ++j) out[j * 16 + lr] = from_f<T>(o[j][r] * inv);
-        } else {
-            const size_t pi = ((size_t)blk.split * c.n_tokens + t) * Hq + h;
-            float *po = c.part_o + pi * HD;
-#pragma unroll
-            for (int j = 0; j < CF; ++j) po[j * 16 + lr] = o[j][r];
-            if (lr == 0) c.part_ml[pi] = make_float2(mq, lq);
+        for (int i = 0; i < INS; ++i) {
+            const int qr = drow[i] < blk.nrows ? blk.row0 + drow[i] : blk.row0;
+            const size_t qrow = (size_t)(qr / grp) * Hq + blk.g * grp + qr % grp;
+            dma16(Q + qrow * RB + dck[i] * 16, lds_base + (uint32_t)((i * 4 + w) * 1024));
         }
     }
+    auto issue = [&](int i) {
+        const bool sfx = i >= n_pre;
+        const int k0 = sfx ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
+        const int kl = sfx ? blk.sfx_hi : kmax;
+        const char *Ksrc = sfx ? Kb : Kg, *Vsrc = sfx ? Vb : Vg;
+        const uint32_t sb = ring_base + (uint32_t)((i % S) * STAGE);
+#pragma unroll
+        for (int u = 0; u < INS; ++u) {
+            const size_t key = (size_t)min(k0 + drow[u], kl - 1);  // keys past the range: a valid key, masked below
+            dma16(Ksrc + key * RB + dck[u] * 16, sb + (uint32_t)((u * 4 + w) * 1024));
+            dma16(Vsrc + key * RB + dcv[u] * 16, sb + (uint32_t)(TILE + (u * 4 + w) * 1024));
+        }
+    };
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s)
+        if (s < n_tiles) issue(s);
+
+    float m_run = -INFINITY, l_run = 0.f;  // reference max of query row lr (replicated over lg); this lane's share of the sum
+    f32x4 o[CF];
+#pragma unroll
+    for (int j = 0; j < CF; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag<T> qf[HS];
+    auto frag16 = [&](const char *tile, int row, int lc) {  // 16 bytes: logical chunk lc of a K or Q row
+        Frag<T> f;
+        f.v = *reinterpret_cast<const bf16x8_t *>(tile + row * RB + ((lc ^ (row & (CPR - 1))) * 16));
+        return f;
+    };
+
+    // One key tile from ring slot i % S: prefix keys (SFX false: visible below
+    // kend_row) or branch keys (SFX true: the row's scaffold and trie ancestors).
+    auto tile = [&](auto SFXC, int i) {
+        constexpr bool SFX = decltype(SFXC)::value;
+        const char *Kt = attn_lds + L::Q_BYTES + (i % S) * STAGE, *Vt = Kt + TILE;
+        const int k0 = SFX ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
+
+        // S^T tile: sc[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r)
+        f32x4 sc[KT / 16];
+        {
+            Frag<T> kfr[KT / 16][HS];
+#pragma unroll
+            for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+                for (int st = 0; st < HS; ++st) kfr[kf][st] = frag16(Kt, kf * 16 + lr, st * 4 + lg);
+            __builtin_amdgcn_sched_barrier(0);  // every read ahead of the multiplies
+#pragma unroll
+            for (int kf = 0; kf < KT / 16; ++kf) sc[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < HS; ++st)
+#pragma unroll
+                for (int kf = 0; kf < KT / 16; ++kf) mma(sc[kf], kfr[kf][st], qf[st]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = k0 + kf * 16 + lg * 4 + r;
+                bool see;
+                if constexpr (SFX) see = row_ok && key < blk.sfx_hi && row_vis_sees(vis, c, key);
+                else see = key < kend_row;
+                const float v = see ? sc[kf][r] * qscale : -INFINITY;
+                sc[kf][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = rows_max(mx);
+        if (__any(mx > m_run + RESCALE_LOG2)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            l_run *= alpha;
+            m_run = m_new;
+            // O rows are queries 4*lg + r, whose factor sits in lane 4*lg + r
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = __shfl(alpha, lg * 4 + r);
+#pragma unroll
+                for (int j = 0; j < CF; ++j) o[j][r] *= a;
+            }
+        }
+        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+        float psum = 0.f;
+        float pr[KT / 16][4];
+#pragma unroll
+        for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[kf][r] = __builtin_amdgcn_exp2f(sc[kf][r] - m_ref);
+                psum += pr[kf][r];
+            }
+        l_run += psum;
+
+        // O += P V over two 32-key steps; A = P (row lr, keys {4lg..4lg+3} and
+        // {16+4lg..16+4lg+3}), B = V with the same key order: lane (lr, lg)
+        // names key rows 32st + 4lg + lr/4 (and +16), columns 16j + 4(lr%4)..+3.
+        Frag<T> vfr[KT / 32][CF];
+#pragma unroll
+        for (int st = 0; st < KT / 32; ++st)
+#pragma unroll
+            for (int j = 0; j < CF; ++j) {
+                const int row = st * 32 + lg * 4 + (lr >> 2);
+                const int pc = (2 * j + ((lr & 3) >> 1)) ^ ((2 * row) & (CPR - 1));  // same for row + 16
+                const char *v0 = Vt + row * RB + pc * 16 + 8 * (lr & 1);
+                const short4_t lo = lds_tr4(v0), hi = lds_tr4(v0 + 16 * RB);
+                const short8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                vfr[st][j].v = __builtin_bit_cast(bf16x8_t, both);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < KT / 32; ++st) {
+            float pv[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pv[r] = pr[2 * st][r];
+                pv[4 + r] = pr[2 * st + 1][r];
+            }
+            Frag<T> pa;
+            from8(pa, pv);
+#pragma unroll
+            for (int j = 0; j < CF; ++j) mma(o[j], pa, vfr[st][j]);
+        }
+    };
+
+    for (int i = 0; i < n_tiles; ++i) {
+        // tile i (and the query rows) landed: later tiles issued so far may stay in flight
+        vm_wait_ahead<LPS, S - 2>(min(S - 2, n_tiles - 1 - i));
+        barrier_keep_loads();
+        if (i == 0) {
+#pragma unroll
+            for (int st = 0; st < HS; ++st) qf[st] = frag16(Qs, w * 16 + lr, st * 4 + lg);
+        }
+        // slot (i - 1) % S was read by every wave before the barrier
+        if (i + S - 1 < n_tiles) issue(i + S - 1);
+        if (i < n_pre) tile(std::false_type{}, i);
+        else tile(std::true_type{}, i);
+        lds_reads_done();
+    }
+    attn_write<T, HD>(c, blk, o, m_run, rows_sum(l_run), w, lr, lg);
+}
+
+template <int HD, int S> static void launch_attn_ring(const AttnCall &c, hipStream_t st) {
+    const int shmem = RingLds<HD>::bytes(S);
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_attn_ring<HD, S>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_attn_ring<HD, S>), dim3(c.n_blocks), dim3(256), shmem, st, c);
 }
 
 template <typename T, int HD> static int attn_lds_bytes() {
@@ -1010,15 +1271,17 @@ template <typename T, int HD> static void launch_attn(const AttnCall &c, hipStre
 
 template <typename T> static bool attention_t(const AttnCall &c, hipStream_t st) {
     if (c.n_blocks <= 0) return true;
-    switch (c.hd) {
-        case 32: launch_attn<T, 32>(c, st); return true;
-        case 64: launch_attn<T, 64>(c, st); return true;
-        case 128:
-            if constexpr (sizeof(T) == 2) {
-                launch_attn<T, 128>(c, st);
-                return true;
-            }
-            return false;
+    if constexpr (sizeof(T) == 2) {
+        switch (c.hd) {
+            case 32: launch_attn_ring<32, ATT_RING_STAGES>(c, st); return true;
+            case 64: launch_attn_ring<64, ATT_RING_STAGES>(c, st); return true;
+            case 128: launch_attn_ring<128, ATT_RING_STAGES>(c, st); return true;
+        }
+    } else {
+        switch (c.hd) {
+            case 32: launch_attn<T, 32>(c, st); return true;
+            case 64: launch_attn<T, 64>(c, st); return true;
+        }
     }
     return false;
 }

@@ -137,6 +137,30 @@ def test_tiny_ragged_multi_request_deep_tries(tiny_w, tiny_dec):
     _run_case("tiny-multi", pi.SHAPES["tiny"], tiny_w, reqs, dec=tiny_dec)
 
 
+def _deep_chain_fields(seed, V):
+    """Two fields whose candidates share long lead runs, so trie tokens sit 11
+    and 15 levels below the scaffold: their visibility chains run past the 8
+    links held in registers and continue through the parent links."""
+    rng = np.random.default_rng(seed)
+    tok = lambda n: [int(t) for t in rng.choice(V, size=n, replace=False)]
+    b, x = tok(10), tok(8)
+    a = pi.Field(tok(4), [b + [x[0]], b + [x[1], x[2]], b + [x[3], x[4], x[5]], [x[6]]], kind="trie")
+    d, z = tok(14), tok(3)
+    f = pi.Field(tok(3), [d + [z[0]], d + [z[1]], d[:6] + [z[2]]], kind="trie")
+    return [a, f]
+
+
+def test_tiny_deep_chains(tiny_w, tiny_dec):
+    """Trie chains deeper than 8 links, three requests (prefixes 3, 64, 100)."""
+    V = pi.SHAPES["tiny"].vocab_size
+    rng = np.random.default_rng(9)
+    reqs = []
+    for k, P in enumerate((3, 64, 100)):
+        prefix = [int(t) for t in rng.integers(0, V, size=P)]
+        reqs.append((prefix, _deep_chain_fields(900 + k, V) + pi.random_trie_fields(910 + k, V, 2)))
+    _run_case("tiny-deep", pi.SHAPES["tiny"], tiny_w, reqs, dec=tiny_dec)
+
+
 def test_tiny_prefill_kv(tiny_w, tiny_dec):
     """The state's KV buffer holds every layer's K (after RoPE) and V of the
     prefix, [layer][K|V][kv head][token][head_dim]."""
@@ -228,3 +252,16 @@ def test_bf16_two_layer_batched_requests(q15_l2):
     sh, w, dec = q15_l2
     wl = pi.make_workload("cfg3")
     _run_case("q15-L2-cfg3x4", sh, w, [(r.prefix, r.fields) for r in wl.requests[:4]], dec=dec)
+
+
+def test_bf16_two_layer_deep_chains(q15_l2):
+    """Trie chains deeper than 8 links at the 1.5B widths (head_dim 128),
+    three requests with prefixes of 1, 65 and 130 tokens in one branch pass."""
+    sh, w, dec = q15_l2
+    rng = np.random.default_rng(11)
+    reqs = []
+    for k, P in enumerate((1, 65, 130)):
+        prefix = [int(t) for t in rng.integers(0, sh.vocab_size, size=P)]
+        reqs.append((prefix, _deep_chain_fields(920 + k, sh.vocab_size) +
+                     pi.random_trie_fields(930 + k, sh.vocab_size, 2, max_len=6)))
+    _run_case("q15-L2-deep", sh, w, reqs, dec=dec)
