@@ -22,9 +22,10 @@ ERROR_NAMES = {-1: "ARG", -2: "TOKEN", -3: "NCAND", -4: "EMPTY", -5: "DUP", -6: 
                -8: "STATE", -9: "DEVICE", -10: "NOMEM"}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_decide",
-           "pcd_decide_many", "pcd_debug_plan", "pcd_get_stats", "pcd_free_state", "pcd_free_model",
-           "pcd_last_error", "pcd_set_kernel_timing", "pcd_get_kernel_times")
+EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_extend",
+           "pcd_fork", "pcd_state_tokens", "pcd_decide", "pcd_decide_sequenced", "pcd_decide_many",
+           "pcd_debug_plan", "pcd_get_stats",
+           "pcd_free_state", "pcd_free_model", "pcd_last_error", "pcd_set_kernel_timing", "pcd_get_kernel_times")
 
 KERNEL_CLASSES = ("prefill_qkv", "prefill_attn", "prefill_o", "prefill_gateup", "prefill_down", "branch_qkv",
                   "branch_attn", "branch_tail", "branch_o", "branch_gateup", "branch_down", "readout_lmhead",
@@ -113,6 +114,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        P(c_void_p)]),
         "pcd_state_bytes": (c_size_t, [c_void_p, c_int32]),
         "pcd_prefill": (c_int32, [c_void_p, P(c_int32), c_int32, c_void_p, c_size_t, c_void_p, P(c_void_p)]),
+        "pcd_extend": (c_int32, [c_void_p, P(c_int32), c_int32, c_void_p]),
+        "pcd_fork": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p, P(c_void_p)]),
+        "pcd_state_tokens": (c_int32, [c_void_p]),
+        "pcd_decide_sequenced": (c_int32, [c_void_p, P(pcd_field), c_int32, P(pcd_candidate), c_int32, c_int32,
+                                           c_float, P(pcd_outputs), c_void_p]),
         "pcd_decide": (c_int32, [c_void_p, P(pcd_field), c_int32, P(pcd_candidate), c_int32, c_float,
                                  P(pcd_outputs), c_void_p]),
         "pcd_decide_many": (c_int32, [P(c_void_p), P(pcd_request), c_int32, c_float, P(pcd_outputs), c_void_p]),
@@ -237,8 +243,28 @@ def upload_weights(mats: Dict[str, np.ndarray], n_layers: int, d_model: int, dev
 
 
 class PcdState:
+    """A prefilled prefix over a torch-allocated KV buffer (`kv`)."""
+
     def __init__(self, model: "PcdModel", handle: c_void_p, kv, n_tokens: int):
         self.model, self.handle, self.kv, self.n_tokens = model, handle, kv, n_tokens
+
+    def extend(self, tokens: Sequence[int]) -> "PcdState":
+        """pcd_extend: append tokens (the buffer must have the capacity)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(self.model.lib.pcd_extend(self.handle, _i32p(t), t.size, _stream_handle(self.model.torch)))
+        self.n_tokens = int(self.model.lib.pcd_state_tokens(self.handle))
+        return self
+
+    def fork(self, capacity: Optional[int] = None, kv=None) -> "PcdState":
+        """pcd_fork: a copy of this state's tokens in a new buffer of `capacity` tokens."""
+        m = self.model
+        if kv is None:
+            kv = m.torch.empty(max(m.state_bytes(capacity or self.n_tokens), 1), dtype=m.torch.uint8,
+                               device=m.workspace.device)
+        h = c_void_p()
+        _check(m.lib.pcd_fork(self.handle, c_void_p(kv.data_ptr()), kv.numel(), _stream_handle(m.torch),
+                              ctypes.byref(h)))
+        return PcdState(m, h, kv, self.n_tokens)
 
     def close(self):
         if self.handle:
@@ -287,10 +313,11 @@ class PcdModel:
     def state_bytes(self, n_tokens: int) -> int:
         return self.lib.pcd_state_bytes(self.handle, n_tokens)
 
-    def prefill(self, tokens: Sequence[int], kv=None) -> PcdState:
+    def prefill(self, tokens: Sequence[int], kv=None, capacity: Optional[int] = None) -> PcdState:
+        """pcd_prefill into `kv` (or a new buffer of `capacity` tokens, default the prefix length)."""
         torch = self.torch
         t = np.ascontiguousarray(tokens, dtype=np.int32)
-        nb = self.state_bytes(t.size)
+        nb = self.state_bytes(max(t.size, capacity or 0))
         if kv is None:
             kv = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.workspace.device)
         h = c_void_p()
@@ -300,6 +327,23 @@ class PcdModel:
 
     def decide(self, state: PcdState, fields, temperature: float = 1.0, debug: bool = False) -> dict:
         return self.decide_many([state], [fields], temperature, debug)[0]
+
+    def decide_sequenced(self, state: PcdState, fields, n_first: int, temperature: float = 1.0) -> dict:
+        """pcd_decide_sequenced: the first n_first fields, their answers appended
+        to the state, then the rest; results indexed as for decide()."""
+        mr = _Marshalled([fields])
+        d = {"prob": np.zeros(mr.n_cands[0], np.float32), "logscore": np.zeros(mr.n_cands[0], np.float32),
+             "mass": np.zeros(mr.n_fields[0], np.float32), "margin": np.zeros(mr.n_fields[0], np.float32),
+             "argmax": np.zeros(mr.n_fields[0], np.int32)}
+        o = pcd_outputs()
+        o.cand_prob, o.cand_logscore = _f32p(d["prob"]), _f32p(d["logscore"])
+        o.field_mass, o.field_margin = _f32p(d["mass"]), _f32p(d["margin"])
+        o.field_argmax = _i32p(d["argmax"])
+        rq = mr.reqs[0]
+        _check(self.lib.pcd_decide_sequenced(state.handle, rq.fields, rq.n_fields, rq.candidates, rq.n_candidates,
+                                             n_first, temperature, ctypes.byref(o), _stream_handle(self.torch)))
+        state.n_tokens = int(self.lib.pcd_state_tokens(state.handle))
+        return d
 
     def decide_many(self, states: Sequence[PcdState], requests, temperature: float = 1.0,
                     debug: bool = False) -> List[dict]:

@@ -198,7 +198,8 @@ struct pcd_state {
     uint64_t magic;
     pcd_model *m;
     void *kv;
-    int32_t P;
+    int32_t P;    // tokens held
+    int32_t cap;  // tokens per (layer, K|V, KV head) slab of the buffer: its layout stride
 };
 
 namespace {
@@ -392,41 +393,47 @@ size_t pcd_state_bytes(const pcd_model *m, int32_t n) {
     return (size_t)n * m->cfg.n_layers * 2 * m->cfg.n_kv_heads * m->cfg.head_dim * esize(m);
 }
 
-int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, size_t kv_bytes, void *stream,
-                pcd_state **out) {
-    if (!m || !tokens || !kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+namespace {
+
+size_t per_token_bytes(const pcd_model *m) {
+    return (size_t)m->cfg.n_layers * 2 * m->cfg.n_kv_heads * m->cfg.head_dim * esize(m);
+}
+
+// One causal pass over tokens[0..n) at positions P0..P0+n-1, appending their
+// K and V to a KV buffer with `cap` tokens per slab that holds P0 tokens
+// already: prefill (P0 = 0) and extend.  Attention of each new token covers
+// keys 0..P0+t, split over workgroups when the row blocks alone do not fill
+// the chip (split k covers [k*slen, (k+1)*slen); only row blocks that reach
+// key k*slen get a workgroup for it), then merged.
+int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32_t *tokens, int32_t n,
+                hipStream_t st) {
     const pcd_config &c = m->cfg;
-    if (n <= 0) return fail(PCD_E_ARG, "empty prefix");
-    if (n > m->lim.max_prefill_tokens || n > c.max_seq)
-        return fail(PCD_E_CAP, "prefix of " + std::to_string(n) + " tokens exceeds the model's limits");
-    if (kv_bytes < pcd_state_bytes(m, n)) return fail(PCD_E_CAP, "KV buffer too small");
-    for (int i = 0; i < n; ++i)
-        if (tokens[i] < 0 || tokens[i] >= c.vocab_size)
-            return fail(PCD_E_TOKEN, "token id " + std::to_string(tokens[i]) + " outside the vocabulary");
-    hipStream_t st = static_cast<hipStream_t>(stream);
     const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim;
-    // device tables: tokens, one request (this KV buffer), attention blocks:
-    // per KV head, 64 query rows each, causal keys 0..t of every row.  With
-    // too few row blocks for the chip the keys are split: split k covers
-    // [k*slen, (k+1)*slen), only row blocks that reach key k*slen get a
-    // workgroup for it, and a merge kernel combines the partials.
+    const int keys = P0 + n;
     std::vector<AttnBlock> blocks;
     const int rows = n * grp;
     const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + ATT_ROWS - 1) / ATT_ROWS);
-    int ns = att_splits(row_blocks, (n + 63) / 64);
-    const int slen = ((n + ns - 1) / ns + 63) / 64 * 64;
-    ns = (n + slen - 1) / slen;
+    int ns = att_splits(row_blocks, (keys + 63) / 64);
+    const int slen = ((keys + ns - 1) / ns + 63) / 64 * 64;
+    ns = (keys + slen - 1) / slen;
     for (int g = 0; g < c.n_kv_heads; ++g)
         for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
-            const int nr = std::min(ATT_ROWS, rows - r0), t_last = (r0 + nr - 1) / grp;
+            const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
             for (int k = 0; k < ns && k * slen <= t_last; ++k)
-                blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(n, (k + 1) * slen), k, ns, 0, 0});
+                blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0});
         }
+    if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
+    std::vector<int32_t> pos;
+    if (P0 > 0) {
+        pos.resize(n);
+        for (int i = 0; i < n; ++i) pos[i] = P0 + i;
+    }
     Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
     const int32_t *d_tok = pk.put(tokens, n);
+    const int32_t *d_pos = P0 > 0 ? pk.put(pos.data(), n) : nullptr;
     const uint64_t kvaddr = reinterpret_cast<uint64_t>(kv_buf);
     const uint64_t *d_kv = pk.put(&kvaddr, 1);
-    const int32_t *d_len = pk.put(&n, 1);
+    const int32_t *d_stride = pk.put(&cap, 1);
     const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
     if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
     m->settle_prefill();
@@ -437,10 +444,14 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
     m->tbegin(PCD_KC_OTHER, st);
     embed(c.dtype, d_tok, n, m->embed, c.d_model, x, m->an[0], c.rms_eps, m->ws + m->L.h, st);
     m->tend(st);
-    const size_t layer_elems = (size_t)2 * c.n_kv_heads * n * hd;
+    const size_t es = esize(m);
+    const size_t slab = (size_t)cap * hd;  // elements of one (layer, K|V, KV head) slab
+    float *part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
+    float2 *part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
     for (int l = 0; l < c.n_layers; ++l) {
-        char *kc = static_cast<char *>(kv_buf) + (size_t)l * layer_elems * esize(m);
-        char *vc = kc + layer_elems / 2 * esize(m);
+        // this layer's K and V slabs, at the first new token's row
+        char *kc = static_cast<char *>(kv_buf) + ((size_t)l * 2 * c.n_kv_heads * slab + (size_t)P0 * hd) * es;
+        char *vc = kc + (size_t)c.n_kv_heads * slab * es;
         auto attn = [&](void *q, void *ao) {
             AttnCall a{};
             a.dt = c.dtype;
@@ -450,13 +461,14 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
             a.layer = l;
             a.q = q;
             a.req_kv = d_kv;
-            a.req_len = d_len;
+            a.req_stride = d_stride;
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
             a.causal = true;
+            a.q_pos0 = P0;
             a.out = ao;
-            a.part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
-            a.part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
+            a.part_o = part_o;
+            a.part_ml = part_ml;
             a.n_tokens = n;
             m->tbegin(PCD_KC_PREFILL_ATTN, st);
             const bool ok = attention(a, st);
@@ -469,9 +481,10 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
                 t.n_heads = c.n_heads;
                 t.n_kv_heads = c.n_kv_heads;
                 t.n_tokens = n;
-                t.part_o = a.part_o;
-                t.part_ml = a.part_ml;
+                t.part_o = part_o;
+                t.part_ml = part_ml;
                 t.split_len = slen;
+                t.q_pos0 = P0;
                 t.out = ao;
                 m->tbegin(PCD_KC_PREFILL_ATTN, st);
                 attention_merge(t, st);
@@ -479,7 +492,7 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
             }
             return PCD_OK;
         };
-        int rc = layer(m, l, n, nullptr, kc, vc, n, false, attn, st);
+        int rc = layer(m, l, n, d_pos, kc, vc, cap, false, attn, st);
         if (rc != PCD_OK) return rc;
     }
     HIP_TRY(hipEventRecord(m->ev[4], st));
@@ -493,11 +506,82 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, si
         m->tcollect();
     }
     m->stats.prefill_passes += 1;
-    pcd_state *s = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_buf, n};
+    return PCD_OK;
+}
+
+int check_tokens(const pcd_model *m, const int32_t *tokens, int32_t n) {
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab_size)
+            return fail(PCD_E_TOKEN, "token id " + std::to_string(tokens[i]) + " outside the vocabulary");
+    return PCD_OK;
+}
+
+}  // namespace
+
+int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, size_t kv_bytes, void *stream,
+                pcd_state **out) {
+    if (!m || !tokens || !kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+    const pcd_config &c = m->cfg;
+    if (n <= 0) return fail(PCD_E_ARG, "empty prefix");
+    if (n > m->lim.max_prefill_tokens || n > c.max_seq)
+        return fail(PCD_E_CAP, "prefix of " + std::to_string(n) + " tokens exceeds the model's limits");
+    if (kv_bytes < pcd_state_bytes(m, n)) return fail(PCD_E_CAP, "KV buffer too small");
+    const size_t cap_tokens = kv_bytes / per_token_bytes(m);
+    const int32_t cap = (int32_t)std::min<size_t>(cap_tokens, (size_t)c.max_seq);
+    int rc = check_tokens(m, tokens, n);
+    if (rc != PCD_OK) return rc;
+    pcd_state *s = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_buf, 0, cap};
     if (!s) return fail(PCD_E_NOMEM, "state allocation");
+    rc = causal_pass(m, kv_buf, cap, 0, tokens, n, static_cast<hipStream_t>(stream));
+    if (rc != PCD_OK) {
+        delete s;
+        return rc;
+    }
+    s->P = n;
     m->n_states++;
     *out = s;
     return PCD_OK;
+}
+
+int pcd_extend(pcd_state *s, const int32_t *tokens, int32_t n, void *stream) {
+    if (!s || s->magic != STATE_MAGIC) return fail(PCD_E_STATE, "invalid state handle");
+    if (!tokens) return fail(PCD_E_ARG, "null argument");
+    if (n <= 0) return fail(PCD_E_ARG, "nothing to append");
+    pcd_model *m = s->m;
+    if (n > m->lim.max_prefill_tokens || s->P + n > m->cfg.max_seq)
+        return fail(PCD_E_CAP, "appending " + std::to_string(n) + " tokens exceeds the model's limits");
+    if (s->P + n > s->cap)
+        return fail(PCD_E_CAP, "the state's KV buffer holds " + std::to_string(s->cap) + " tokens, " +
+                                   std::to_string(s->P + n) + " needed");
+    int rc = check_tokens(m, tokens, n);
+    if (rc != PCD_OK) return rc;
+    rc = causal_pass(m, s->kv, s->cap, s->P, tokens, n, static_cast<hipStream_t>(stream));
+    if (rc != PCD_OK) return rc;
+    s->P += n;
+    return PCD_OK;
+}
+
+int pcd_fork(const pcd_state *s, void *kv_buf, size_t kv_bytes, void *stream, pcd_state **out) {
+    if (!s || s->magic != STATE_MAGIC) return fail(PCD_E_STATE, "invalid state handle");
+    if (!kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+    pcd_model *m = s->m;
+    if (kv_bytes < pcd_state_bytes(m, s->P)) return fail(PCD_E_CAP, "KV buffer too small");
+    const int32_t cap = (int32_t)std::min<size_t>(kv_bytes / per_token_bytes(m), (size_t)m->cfg.max_seq);
+    const size_t row = (size_t)m->cfg.head_dim * esize(m);
+    // every (layer, K|V, KV head) slab: the first P rows, from stride s->cap to stride cap
+    HIP_TRY(hipMemcpy2DAsync(kv_buf, (size_t)cap * row, s->kv, (size_t)s->cap * row, (size_t)s->P * row,
+                             (size_t)m->cfg.n_layers * 2 * m->cfg.n_kv_heads, hipMemcpyDeviceToDevice,
+                             static_cast<hipStream_t>(stream)));
+    pcd_state *f = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_buf, s->P, cap};
+    if (!f) return fail(PCD_E_NOMEM, "state allocation");
+    m->n_states++;
+    *out = f;
+    return PCD_OK;
+}
+
+int pcd_state_tokens(const pcd_state *s) {
+    if (!s || s->magic != STATE_MAGIC) return fail(PCD_E_STATE, "invalid state handle");
+    return s->P;
 }
 
 int pcd_debug_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_lens, const pcd_request *reqs,
@@ -623,7 +707,9 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     const int32_t *d_fcand = pk.put(p.f_cand_off.data(), F + 1);
     const int32_t *d_cpo = pk.put(p.c_path_off.data(), C + 1);
     const int32_t *d_cp = pk.put(p.c_path.data(), NP);
-    const int32_t *d_len = pk.put(lens.data(), n_req);
+    std::vector<int32_t> strides(n_req);
+    for (int r = 0; r < n_req; ++r) strides[r] = states[r]->cap;
+    const int32_t *d_stride = pk.put(strides.data(), n_req);
     const int32_t *d_rsp = pk.put(req_splits.data(), n_req);
     const uint64_t *d_kv = pk.put(req_kv.data(), n_req);
     const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
@@ -663,7 +749,7 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
             a.layer = l;
             a.q = q;
             a.req_kv = d_kv;
-            a.req_len = d_len;
+            a.req_stride = d_stride;
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
             a.causal = false;
@@ -787,6 +873,65 @@ int pcd_decide(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pc
                int32_t n_candidates, float temperature, pcd_outputs *out, void *stream) {
     pcd_request r{fields, n_fields, candidates, n_candidates};
     return pcd_decide_many(&s, &r, 1, temperature, out, stream);
+}
+
+int pcd_decide_sequenced(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pcd_candidate *candidates,
+                         int32_t n_candidates, int32_t n_first, float temperature, pcd_outputs *out, void *stream) {
+    if (!s || s->magic != STATE_MAGIC) return fail(PCD_E_STATE, "invalid state handle");
+    if (!fields || !out) return fail(PCD_E_ARG, "null argument");
+    if (n_first < 1 || n_first >= n_fields) return fail(PCD_E_ARG, "n_first must be in [1, n_fields)");
+    if (out->readout_lse || out->gather_logit) return fail(PCD_E_ARG, "readout_lse / gather_logit must be NULL here");
+    if (!out->cand_prob || !out->field_mass || !out->field_margin || !out->field_argmax)
+        return fail(PCD_E_ARG, "null output array");
+    pcd_model *m = s->m;
+    // Longest possible answer of the first fields: each scaffold plus its longest candidate.
+    int64_t ans_max = 0, c1 = 0;
+    for (int f = 0; f < n_first; ++f) {
+        const pcd_field &fd = fields[f];
+        if (fd.cand_offset < 0 || fd.n_cands < 0 || (int64_t)fd.cand_offset + fd.n_cands > n_candidates || !candidates)
+            return fail(PCD_E_ARG, "field " + std::to_string(f) + ": candidates outside the candidate array");
+        int lmax = 0;
+        for (int k = 0; k < fd.n_cands; ++k) lmax = std::max(lmax, candidates[fd.cand_offset + k].n_tokens);
+        ans_max += std::max(0, fd.n_scaffold) + lmax;
+        c1 += fd.n_cands;
+    }
+    // Validate the whole request before any device work: the plan at the
+    // longest extended prefix, the buffer's capacity and the pass size.
+    const int64_t P_max = (int64_t)s->P + ans_max;
+    if (P_max > s->cap || P_max > m->cfg.max_seq || ans_max > m->lim.max_prefill_tokens)
+        return fail(PCD_E_CAP, "the first fields' answers may need " + std::to_string(ans_max) +
+                                   " more tokens than the state's buffer or the model's limits allow");
+    {
+        const int32_t Pc = (int32_t)P_max;
+        pcd_request all{fields, n_fields, candidates, n_candidates};
+        Plan p;
+        std::string err;
+        const int rc = build_plan(m->cfg.vocab_size, m->cfg.max_seq, 1, &Pc, &all, p, err);
+        if (rc != PCD_OK) return fail(rc, err);
+    }
+    pcd_request r1{fields, n_first, candidates, n_candidates};
+    pcd_outputs o1 = *out;
+    int rc = pcd_decide_many(&s, &r1, 1, temperature, &o1, stream);
+    if (rc != PCD_OK) return rc;
+    // write the answers in: each first field's scaffold, then its chosen candidate
+    std::vector<int32_t> ans;
+    ans.reserve((size_t)ans_max);
+    for (int f = 0; f < n_first; ++f) {
+        const pcd_field &fd = fields[f];
+        ans.insert(ans.end(), fd.scaffold, fd.scaffold + fd.n_scaffold);
+        const pcd_candidate &cd = candidates[fd.cand_offset + out->field_argmax[f]];
+        ans.insert(ans.end(), cd.tokens, cd.tokens + cd.n_tokens);
+    }
+    rc = pcd_extend(s, ans.data(), (int32_t)ans.size(), stream);
+    if (rc != PCD_OK) return rc;
+    pcd_request r2{fields + n_first, n_fields - n_first, candidates, n_candidates};
+    pcd_outputs o2 = *out;
+    o2.cand_prob += c1;
+    if (o2.cand_logscore) o2.cand_logscore += c1;
+    o2.field_mass += n_first;
+    o2.field_margin += n_first;
+    o2.field_argmax += n_first;
+    return pcd_decide_many(&s, &r2, 1, temperature, &o2, stream);
 }
 
 int pcd_get_stats(const pcd_model *m, pcd_stats *out) {

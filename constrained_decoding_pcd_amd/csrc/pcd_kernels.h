@@ -80,10 +80,11 @@ struct AttnCall {
     int32_t hd, n_heads, n_kv_heads, layer;
     const void *q;          // [tokens][Hq][hd]
     const uint64_t *req_kv; // per request: device address of its KV buffer ([L][2][Hkv][P][hd])
-    const int32_t *req_len; // per request: P
+    const int32_t *req_stride; // per request: tokens per (layer, K|V, KV head) slab of its KV buffer
     const AttnBlock *blocks;
     int32_t n_blocks;
-    bool causal;            // prefill: row token t sees prefix keys <= t (rows with t < key0 are skipped)
+    bool causal;            // prefill / extend: row token t sees keys <= q_pos0 + t (rows with q_pos0 + t < key0 are skipped)
+    int32_t q_pos0;         // causal: position of the call's first token (the state's length before it)
     void *out;              // [tokens][Hq][hd] (dt)
     float *part_o;          // [split][tokens][Hq][hd] unnormalised
     float2 *part_ml;        // [split][tokens][Hq] (max in log2 units, sum)
@@ -103,7 +104,8 @@ struct TailCall {
     const float *part_o;
     const float2 *part_ml;
     const int32_t *tok_req, *req_splits;  // branch: splits used by each request
-    int32_t split_len;                    // prefill (> 0): token t has splits 0..t/split_len
+    int32_t split_len;                    // causal (> 0): token t has splits 0..(q_pos0 + t)/split_len
+    int32_t q_pos0;
     void *out;                            // [tokens][Hq][hd]
 };
 void attention_merge(const TailCall &c, hipStream_t st);

@@ -785,9 +785,10 @@ __device__ __forceinline__ void attn_write(const AttnCall &c, const AttnBlock &b
         if (w * 16 + qi >= blk.nrows) continue;
         const int row = blk.row0 + w * 16 + qi;
         const int t = row / grp, h = blk.g * grp + row % grp;
-        if (c.causal && t < blk.key0) continue;  // causal row with no key in this split
+        const int ta = c.q_pos0 + t;            // causal: the row's position
+        if (c.causal && ta < blk.key0) continue;  // causal row with no key in this split
         // a causal row whose keys all lie in split 0 has no partials to merge
-        if (blk.nsplit == 1 || (c.causal && blk.split == 0 && t < blk.key1)) {
+        if (blk.nsplit == 1 || (c.causal && blk.split == 0 && ta < blk.key1)) {
             T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
             const float inv = 1.0f / lq;
 #pragma unroll
@@ -823,7 +824,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     const AttnBlock blk = c.blocks[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
-    const int P = c.req_len[blk.req];
+    const int P = c.req_stride[blk.req];  // slab stride (the buffer's token capacity)
     const T *kvbase = reinterpret_cast<const T *>(c.req_kv[blk.req]);
     const T *Kg = kvbase + ((size_t)c.layer * 2 * Hkv + blk.g) * (size_t)P * HD;
     const T *Vg = kvbase + ((size_t)c.layer * 2 * Hkv + Hkv + blk.g) * (size_t)P * HD;
@@ -839,11 +840,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     Frag<T> qf[HS];
 #pragma unroll
     for (int s = 0; s < HS; ++s) ld8(qf[s], Q + ((size_t)tq * Hq + hq) * HD + s * 32 + lg * 8);
-    const int kend_row = c.causal ? min(tq + 1, blk.key1) : blk.key1;
+    const int kend_row = c.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
 
     int kmax = blk.key1;
     if (c.causal) {
-        const int last = (blk.row0 + blk.nrows - 1) / grp + 1;
+        const int last = c.q_pos0 + (blk.row0 + blk.nrows - 1) / grp + 1;
         kmax = last < kmax ? last : kmax;
     }
     const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;
@@ -1057,7 +1058,7 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     const AttnBlock blk = c.blocks[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
-    const int P = c.req_len[blk.req];
+    const int P = c.req_stride[blk.req];  // slab stride (the buffer's token capacity)
     const char *kvbase = reinterpret_cast<const char *>(c.req_kv[blk.req]);
     const char *Kg = kvbase + ((size_t)c.layer * 2 * Hkv + blk.g) * (size_t)P * RB;
     const char *Vg = kvbase + ((size_t)c.layer * 2 * Hkv + Hkv + blk.g) * (size_t)P * RB;
@@ -1069,10 +1070,10 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     const bool row_ok = (w * 16 + lr) < blk.nrows;
     const int rr = row_ok ? blk.row0 + w * 16 + lr : blk.row0;
     const int tq = rr / grp;
-    const int kend_row = c.causal ? min(tq + 1, blk.key1) : blk.key1;
+    const int kend_row = c.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
     int kmax = blk.key1;
     if (c.causal) {
-        const int last = (blk.row0 + blk.nrows - 1) / grp + 1;
+        const int last = c.q_pos0 + (blk.row0 + blk.nrows - 1) / grp + 1;
         kmax = last < kmax ? last : kmax;
     }
     const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;
@@ -1299,7 +1300,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
     const int Hq = c.n_heads;
     if (id >= c.n_tokens * Hq) return;
     const int t = id / Hq, h = id % Hq;
-    const int ns = c.split_len > 0 ? t / c.split_len + 1 : c.req_splits[c.tok_req[t]];
+    const int ns = c.split_len > 0 ? (c.q_pos0 + t) / c.split_len + 1 : c.req_splits[c.tok_req[t]];
     if (ns <= 1) return;  // written directly by the attention kernel
     float m = -INFINITY, l = 0.f, o[PL];
 #pragma unroll

@@ -170,7 +170,11 @@ int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_wei
 /* Bytes of the KV buffer a state of n_tokens needs:
  * n_tokens x n_layers x 2 (K, V) x n_kv_heads x head_dim x element size
  * ("Parallel Constrained Decoding from Scratch", "the KV cache").
- * Layout: [layer][K|V][kv head][token][head_dim], K after RoPE. */
+ * Layout: [layer][K|V][kv head][cap][head_dim], K after RoPE, where the
+ * buffer's capacity cap = min(kv_bytes / pcd_state_bytes(m, 1), max_seq)
+ * tokens is fixed when the state is created (equal to the token count for a
+ * buffer of exactly pcd_state_bytes(m, n) bytes).  A state may grow by
+ * pcd_extend up to its capacity. */
 size_t pcd_state_bytes(const pcd_model *m, int32_t n_tokens);
 
 /* Prefill: one causal pass of the decoder over tokens[0..n_tokens) (host
@@ -188,6 +192,30 @@ size_t pcd_state_bytes(const pcd_model *m, int32_t n_tokens);
 int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n_tokens, void *kv_buf, size_t kv_bytes,
                 void *stream, pcd_state **out);
 
+/* Append tokens[0..n_tokens) (host array) to a state: one causal pass of the
+ * decoder at positions P..P+n_tokens-1 whose attention covers the state's P
+ * cached tokens and the new ones before each token, writing the new tokens'
+ * K and V into the state's buffer after the cached ones.  The result equals a
+ * prefill of the concatenated tokens.  This is how a cached prompt head is
+ * completed by a per-request input, and how a decided field's answer is
+ * written in before the remaining fields are decided ("Parallel Constrained
+ * Decoding from Scratch", "The idea: parallel constrained decoding": the
+ * prompt and the first field's answer).  PCD_E_CAP if P + n_tokens exceeds
+ * the buffer's capacity, max_seq or max_prefill_tokens; PCD_E_TOKEN for an id
+ * outside the vocabulary; on error the state is unchanged.  Asynchronous
+ * like pcd_prefill; counted as a prefill pass. */
+int pcd_extend(pcd_state *s, const int32_t *tokens, int32_t n_tokens, void *stream);
+
+/* A new state holding a copy of s's cached tokens in the caller's device
+ * buffer kv_buf (kv_bytes >= pcd_state_bytes of s's token count; its
+ * capacity as for pcd_prefill), so that one cached prompt head can be
+ * extended by many requests.  The copy is enqueued on `stream`; s must not be
+ * extended before the stream has passed it.  s is unchanged. */
+int pcd_fork(const pcd_state *s, void *kv_buf, size_t kv_bytes, void *stream, pcd_state **out);
+
+/* Tokens a state holds (P); negative (PCD_E_STATE) for an invalid handle. */
+int pcd_state_tokens(const pcd_state *s);
+
 /* Decide every field of one request against a prefilled state in ONE batched
  * decoder pass.  Each field's row is its scaffold, placed right after the
  * state's prefix (positions P, P+1, ...).  Candidates whose leading tokens
@@ -201,6 +229,20 @@ int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n_tokens, void *kv_
  * written, so any number of decide calls may share one state. */
 int pcd_decide(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pcd_candidate *candidates,
                int32_t n_candidates, float temperature, pcd_outputs *out, void *stream);
+
+/* The first-field round: decide fields[0..n_first) in one batched pass,
+ * append each of them (its scaffold followed by its argmax candidate's
+ * tokens, in field order) to the state with pcd_extend, then decide the
+ * remaining fields in a second batched pass against the extended prefix, so
+ * that their rows see the earlier answers ("Parallel Constrained Decoding
+ * from Scratch", "The idea: parallel constrained decoding": decide the first
+ * field, write its answer in, decide the rest).  Outputs are indexed as for
+ * pcd_decide over the whole request; readout_lse and gather_logit must be
+ * NULL.  The whole request is validated first (plans at the longest possible
+ * extended prefix, the buffer's capacity); the state then ends holding the
+ * prefix plus the answers.  Passes: 2 branch passes and 1 extend. */
+int pcd_decide_sequenced(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pcd_candidate *candidates,
+                         int32_t n_candidates, int32_t n_first, float temperature, pcd_outputs *out, void *stream);
 
 /* Several requests, each on its own state, in ONE batched pass; outs[i]
  * receives request i's results (arrays indexed within that request). */

@@ -158,6 +158,23 @@ def decide(dec: Decoder, requests, temperature: float = 1.0, prefix_kv=None,
     return DecideResult(plan, lse, z, res, {"prefill": 1, "branch": 1}, steps)
 
 
+def decide_sequenced(dec: Decoder, prefix: Sequence[int], fields, n_first: int, temperature: float = 1.0,
+                     n_layers: Optional[int] = None):
+    """The first-field round ([Scratch] "The idea: parallel constrained
+    decoding": the first field is decided, its answer written into the
+    prompt, and the remaining fields decided against it).  Reading taken: the
+    answer of a field is its scaffold followed by its argmax candidate, the
+    first n_first fields' answers are appended in field order, and the rest
+    are decided against that extended prefix.  Returns (first result, rest
+    result, extended prefix)."""
+    first = decide(dec, [(list(prefix), fields[:n_first])], temperature, n_layers=n_layers)
+    ext = list(prefix)
+    for f, r in zip(fields[:n_first], first.fields):
+        ext += list(f.scaffold) + list(f.candidates[r.argmax])
+    rest = decide(dec, [(ext, fields[n_first:])], temperature, n_layers=n_layers)
+    return first, rest, ext
+
+
 # ----------------------------------------------------------------------------
 # independent references built on plain causal runs (no cache, no batching)
 # ----------------------------------------------------------------------------

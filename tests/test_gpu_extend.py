@@ -1,0 +1,181 @@
+"""GPU parity of growing a state through the C ABI against the fp64 oracle:
+pcd_extend (a causal pass over new tokens after the cached ones), pcd_fork
+(one cached prompt head, many requests) and pcd_decide_sequenced (the
+first-field round: decide the first field, write its answer in, decide the
+rest).  An extended state must equal a prefill of the concatenated tokens;
+tolerances as in test_gpu_parity.py.
+"""
+import numpy as np
+import pytest
+
+import pcd_inputs as pi
+from oracle import decoder as odec
+from oracle import pcd as opcd
+from test_gpu_parity import TOL, MARGIN_WAIVER, _compare
+
+cpd = pytest.importorskip("constrained_decoding_pcd_amd")
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny_w():
+    return pi.make_weights(pi.SHAPES["tiny"], 1000)
+
+
+@pytest.fixture(scope="module")
+def tiny_dec(tiny_w):
+    return odec.Decoder(tiny_w, np.float64)
+
+
+def _model(shape, weights, lens, requests, max_prefill):
+    dev = cpd.upload_weights(weights.mats, shape.n_layers, shape.d_model, "cuda:0")
+    lim = cpd.limits_for(shape.vocab_size, shape.max_seq, lens, requests, max_prefill)
+    return cpd.PcdModel(cpd.config_of(shape), dev, lim)
+
+
+def _kv(state, shape, cap, np_dtype):
+    a = state.kv.view(torch.float32 if np_dtype == np.float32 else torch.int16).cpu().numpy()
+    return a.reshape(shape.n_layers, 2, shape.n_kv_heads, cap, shape.head_dim)[:, :, :, :state.n_tokens]
+
+
+def _tokens(rng, V, n):
+    return [int(t) for t in rng.integers(0, V, size=n)]
+
+
+def _compare_fields(name, got, ref_fields, dtype):
+    """Per-candidate probabilities and log-scores, per-field mass and argmax."""
+    tol = TOL[dtype]
+    prob = np.concatenate([f.prob for f in ref_fields])
+    ls = np.concatenate([f.logscore for f in ref_fields])
+    mass = np.array([f.mass for f in ref_fields])
+    d = {"prob": float(np.max(np.abs(got["prob"] - prob))), "ls": float(np.max(np.abs(got["logscore"] - ls))),
+         "mass_rel": float(np.max(np.abs(got["mass"] - mass) / mass))}
+    print(f"[{name}] max errors: " + ", ".join(f"{k} {v:.3e}" for k, v in d.items()), flush=True)
+    # log-scores sum at most 4 conditionals here (trie depth of the workloads)
+    assert d["prob"] <= tol["prob"] and d["mass_rel"] <= tol["mass"] and d["ls"] <= tol["ls"] * 4
+    for i, f in enumerate(ref_fields):
+        if f.margin >= MARGIN_WAIVER:
+            assert int(got["argmax"][i]) == f.argmax, (name, i, f.margin)
+
+
+def test_tiny_extend_kv_matches_prefill(tiny_w, tiny_dec):
+    """prefill(A) + extend(B) + extend(C) leaves the KV of prefill(A+B+C);
+    the pieces (50, 30, 70 tokens) straddle the 64-key tiles."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(21)
+    A, B, C = _tokens(rng, sh.vocab_size, 50), _tokens(rng, sh.vocab_size, 30), _tokens(rng, sh.vocab_size, 70)
+    fields = pi.make_workload("cfg0").requests[0].fields
+    m = _model(sh, tiny_w, [150], [fields], 70)
+    st = m.prefill(A, capacity=150)
+    st.extend(B)
+    st.extend(C)
+    assert st.n_tokens == 150
+    kv = _kv(st, sh, 150, np.float32)
+    ref = opcd.prefill(tiny_dec, A + B + C)
+    err = max(float(np.max(np.abs(kv[l, i] - ref[l][i]))) for l in range(sh.n_layers) for i in range(2))
+    print(f"[extend-kv] max abs error {err:.3e}", flush=True)
+    assert err < 1e-4
+    assert m.stats()["prefill_passes"] == 3
+    # decide against the grown state equals decide against the concatenation
+    got = [m.decide(st, fields, debug=True)]
+    ref = opcd.decide(tiny_dec, [(A + B + C, fields)])
+    _compare("tiny-extend", got, ref, ref.plan.c_path_off, "f32")
+    st.close()
+    m.close()
+
+
+def test_tiny_fork_serves_two_requests(tiny_w, tiny_dec):
+    """One cached head (60 tokens) forked twice and extended by two different
+    inputs (20 and 45 tokens): each equals its own concatenation, and the
+    head's KV is untouched."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(22)
+    head = _tokens(rng, sh.vocab_size, 60)
+    inputs = [_tokens(rng, sh.vocab_size, 20), _tokens(rng, sh.vocab_size, 45)]
+    fields = pi.make_workload("cfg0t").requests[0].fields
+    m = _model(sh, tiny_w, [105], [fields], 60)
+    hs = m.prefill(head)
+    kv0 = hs.kv.clone()
+    for k, inp in enumerate(inputs):
+        st = hs.fork(capacity=len(head) + len(inp))
+        st.extend(inp)
+        got = [m.decide(st, fields, debug=True)]
+        ref = opcd.decide(tiny_dec, [(head + inp, fields)])
+        _compare(f"tiny-fork{k}", got, ref, ref.plan.c_path_off, "f32")
+        st.close()
+    assert torch.equal(kv0, hs.kv) and hs.n_tokens == len(head)
+    hs.close()
+    m.close()
+
+
+def test_tiny_first_field_round(tiny_w, tiny_dec):
+    """pcd_decide_sequenced: field 0 decided, its scaffold and chosen
+    candidate appended, the other fields decided against that."""
+    sh = pi.SHAPES["tiny"]
+    wl = pi.make_workload("cfg0t")
+    prefix, fields = wl.requests[0].prefix, wl.requests[0].fields
+    ans_max = len(fields[0].scaffold) + max(len(c) for c in fields[0].candidates)
+    m = _model(sh, tiny_w, [len(prefix) + ans_max], [fields], len(prefix) + ans_max)
+    st = m.prefill(prefix, capacity=len(prefix) + ans_max)
+    got = m.decide_sequenced(st, fields, 1)
+    first, rest, ext = opcd.decide_sequenced(tiny_dec, prefix, fields, 1)
+    assert st.n_tokens == len(ext)
+    _compare_fields("tiny-sequenced", got, first.fields + rest.fields, "f32")
+    s = m.stats()
+    assert s["prefill_passes"] == 2 and s["branch_passes"] == 2
+    st.close()
+    m.close()
+
+
+def test_tiny_extend_errors_leave_state(tiny_w):
+    """Past the buffer's capacity or outside the vocabulary: the call fails
+    before any device work and the state keeps its tokens."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(23)
+    fields = pi.make_workload("cfg0").requests[0].fields
+    m = _model(sh, tiny_w, [40], [fields], 40)
+    st = m.prefill(_tokens(rng, sh.vocab_size, 30), capacity=40)
+    with pytest.raises(cpd.PcdError) as e:
+        st.extend(_tokens(rng, sh.vocab_size, 11))
+    assert e.value.name == "CAP" and st.n_tokens == 30
+    with pytest.raises(cpd.PcdError) as e:
+        st.extend([1, 2, sh.vocab_size])
+    assert e.value.name == "TOKEN" and st.n_tokens == 30
+    st.extend(_tokens(rng, sh.vocab_size, 10))
+    assert st.n_tokens == 40
+    st.close()
+    m.close()
+
+
+@pytest.fixture(scope="module")
+def q15_l2():
+    sh = pi.SHAPES["qwen2.5-1.5b"]
+    w = pi.make_weights(sh, 1001, n_layers=2)
+    return w.shape, w, odec.Decoder(w, np.float64)
+
+
+def test_bf16_two_layer_warm_head_and_first_field_round(q15_l2):
+    """The 28-field workload at the 1.5B widths (2 layers): its 512-token
+    prefix as a cached 400-token head plus a 112-token request input (fork +
+    extend), then the first-field round on the grown state."""
+    sh, w, dec = q15_l2
+    wl = pi.make_workload("cfg1")
+    prefix, fields = wl.requests[0].prefix, wl.requests[0].fields
+    ans_max = len(fields[0].scaffold) + max(len(c) for c in fields[0].candidates)
+    cap = len(prefix) + ans_max
+    m = _model(sh, w, [cap], [fields], cap)
+    hs = m.prefill(prefix[:400])
+    st = hs.fork(capacity=cap)
+    st.extend(prefix[400:])
+    got = [m.decide(st, fields, debug=True)]
+    ref = opcd.decide(dec, [(list(prefix), fields)])
+    _compare("q15-L2-warm", got, ref, ref.plan.c_path_off, "bf16")
+    seq = m.decide_sequenced(st, fields, 1)
+    first, rest, ext = opcd.decide_sequenced(dec, prefix, fields, 1)
+    assert st.n_tokens == len(ext)
+    _compare_fields("q15-L2-sequenced", seq, first.fields + rest.fields, "bf16")
+    st.close()
+    hs.close()
+    m.close()

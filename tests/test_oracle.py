@@ -225,6 +225,20 @@ def test_trie_scores_equal_enumeration(tiny, cfg0t):
         assert np.max(np.abs(fr.logscore - ref)) < 1e-10
 
 
+def test_sequenced_rest_sees_the_answers(tiny, cfg0t):
+    """The first-field round: the remaining fields' scores equal from-scratch
+    conditionals after prefix + the first field's scaffold and chosen
+    candidate, and differ from scores taken against the bare prefix."""
+    prefix, fields = _reqs(cfg0t)[0]
+    first, rest, ext = opcd.decide_sequenced(tiny, prefix, fields, 1)
+    f0 = fields[0]
+    assert ext == list(prefix) + list(f0.scaffold) + list(f0.candidates[first.fields[0].argmax])
+    for f, fr in zip(fields[1:], rest.fields):
+        assert np.max(np.abs(fr.logscore - opcd.enumerate_scores(tiny, ext, f))) < 1e-10
+    bare = opcd.decide(tiny, [(prefix, fields[1:])])
+    assert max(float(np.max(np.abs(a.logscore - b.logscore))) for a, b in zip(rest.fields, bare.fields)) > 1e-6
+
+
 def test_subset_softmax_identity(tiny, cfg0):
     """First Principles, "The subset softmax is exact": for single-token
     candidates q = p_S / sum(p_S) = p_S / mass, and the argmax does not depend
