@@ -157,6 +157,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cfg1", help="cfg0 (tiny) or cfg1 (1.5B, 512-token prefix, 28 fields)")
     ap.add_argument("--cpu-layers", type=int, default=28, help="layers of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--warm-input", type=int, default=100,
+                    help="warm request: the prefix minus this many tokens is a cached head (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -214,6 +216,40 @@ def main():
     stats = model.stats()
     dev_ms = stats["last_prefill_ms"] + stats["last_branch_ms"] + stats["last_readout_ms"]
 
+    # Warm requests: the prefix's first tokens are a cached head; each request
+    # forks it, appends its own input tokens and decides (one extend + one
+    # branch pass), or runs the first-field round on top (decide field 0,
+    # append its answer, decide the rest: two extends + two branch passes).
+    warm = None
+    if 0 < args.warm_input < len(req.prefix):
+        head_n = len(req.prefix) - args.warm_input
+        f0 = req.fields[0]
+        cap = len(req.prefix) + len(f0.scaffold) + max(len(c) for c in f0.candidates)
+        head = model.prefill(req.prefix[:head_n])
+        kv_w = torch.empty(model.state_bytes(cap), dtype=torch.uint8, device="cuda:0")
+
+        def warm_step(first_field_round):
+            st = head.fork(kv=kv_w)
+            st.extend(req.prefix[head_n:])
+            if first_field_round:
+                model.decide_sequenced(st, req.fields, 1)
+            else:
+                model.decide(st, req.fields)
+            st.close()
+
+        warm = {"head_tokens": head_n, "input_tokens": args.warm_input}
+        for key, ffr in (("p50_request_ms", False), ("first_field_round_p50_ms", True)):
+            for _ in range(args.warmup):
+                warm_step(ffr)
+            torch.cuda.synchronize()
+            lw = []
+            for _ in range(args.steps):
+                s0 = time.perf_counter()
+                warm_step(ffr)
+                lw.append(time.perf_counter() - s0)
+            warm[key] = round(float(np.percentile(np.array(lw) * 1e3, 50)), 4)
+        head.close()
+
     # the same steps again with every kernel launch bracketed by hipEvents on the library's stream
     model.set_kernel_timing(True)
     for _ in range(args.steps):
@@ -261,6 +297,8 @@ def main():
                                                             "launches", "bound")} for c, e in kernels.items()},
         "kernel_timed_ms_per_step": round(timed_ms_per_step, 4),
     }
+    if warm is not None:
+        res["warm"] = warm
     if args.cpu_layers > 0:
         print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(weights, wl, min(args.cpu_layers, sh.n_layers))
