@@ -23,7 +23,8 @@ ERROR_NAMES = {-1: "ARG", -2: "TOKEN", -3: "NCAND", -4: "EMPTY", -5: "DUP", -6: 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_extend",
-           "pcd_fork", "pcd_state_tokens", "pcd_decide", "pcd_decide_sequenced", "pcd_decide_many",
+           "pcd_fork", "pcd_state_tokens", "pcd_new_state", "pcd_decide", "pcd_extend_decide",
+           "pcd_decide_sequenced", "pcd_decide_many",
            "pcd_debug_plan", "pcd_get_stats",
            "pcd_free_state", "pcd_free_model", "pcd_last_error", "pcd_set_kernel_timing", "pcd_get_kernel_times")
 
@@ -117,6 +118,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pcd_extend": (c_int32, [c_void_p, P(c_int32), c_int32, c_void_p]),
         "pcd_fork": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p, P(c_void_p)]),
         "pcd_state_tokens": (c_int32, [c_void_p]),
+        "pcd_new_state": (c_int32, [c_void_p, c_void_p, c_size_t, P(c_void_p)]),
+        "pcd_extend_decide": (c_int32, [c_void_p, P(c_int32), c_int32, P(pcd_field), c_int32, P(pcd_candidate),
+                                        c_int32, c_float, P(pcd_outputs), c_void_p]),
         "pcd_decide_sequenced": (c_int32, [c_void_p, P(pcd_field), c_int32, P(pcd_candidate), c_int32, c_int32,
                                            c_float, P(pcd_outputs), c_void_p]),
         "pcd_decide": (c_int32, [c_void_p, P(pcd_field), c_int32, P(pcd_candidate), c_int32, c_float,
@@ -327,6 +331,45 @@ class PcdModel:
 
     def decide(self, state: PcdState, fields, temperature: float = 1.0, debug: bool = False) -> dict:
         return self.decide_many([state], [fields], temperature, debug)[0]
+
+    def new_state(self, capacity: int, kv=None) -> PcdState:
+        """pcd_new_state: an empty state whose buffer holds `capacity` tokens."""
+        torch = self.torch
+        if kv is None:
+            kv = torch.empty(max(self.state_bytes(capacity), 1), dtype=torch.uint8, device=self.workspace.device)
+        h = c_void_p()
+        _check(self.lib.pcd_new_state(self.handle, c_void_p(kv.data_ptr()), kv.numel(), ctypes.byref(h)))
+        return PcdState(self, h, kv, 0)
+
+    def extend_decide(self, state: PcdState, tokens: Sequence[int], fields, temperature: float = 1.0,
+                      debug: bool = False) -> dict:
+        """pcd_extend_decide: append tokens and decide the fields in one pass."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        mr = _Marshalled([fields])
+        d, o = self._outputs(mr, 0, [fields], state.n_tokens + t.size if debug else None)
+        rq = mr.reqs[0]
+        _check(self.lib.pcd_extend_decide(state.handle, _i32p(t), t.size, rq.fields, rq.n_fields, rq.candidates,
+                                          rq.n_candidates, temperature, ctypes.byref(o),
+                                          _stream_handle(self.torch)))
+        state.n_tokens = int(self.lib.pcd_state_tokens(state.handle))
+        return d
+
+    def _outputs(self, mr, r, requests, debug_prefix):
+        """Result arrays of request r and their pcd_outputs view (debug: sized
+        from the plan at a prefix of debug_prefix tokens)."""
+        d = {"prob": np.zeros(mr.n_cands[r], np.float32), "logscore": np.zeros(mr.n_cands[r], np.float32),
+             "mass": np.zeros(mr.n_fields[r], np.float32), "margin": np.zeros(mr.n_fields[r], np.float32),
+             "argmax": np.zeros(mr.n_fields[r], np.int32)}
+        o = pcd_outputs()
+        o.cand_prob, o.cand_logscore = _f32p(d["prob"]), _f32p(d["logscore"])
+        o.field_mass, o.field_margin = _f32p(d["mass"]), _f32p(d["margin"])
+        o.field_argmax = _i32p(d["argmax"])
+        if debug_prefix is not None:
+            plan = debug_plan(self.cfg.vocab_size, self.cfg.max_seq, [debug_prefix], [requests[r]])
+            d["lse"] = np.zeros(max(1, len(plan["ro_tok"])), np.float32)
+            d["z"] = np.zeros(max(1, len(plan["g_tok"])), np.float32)
+            o.readout_lse, o.gather_logit = _f32p(d["lse"]), _f32p(d["z"])
+        return d, o
 
     def decide_sequenced(self, state: PcdState, fields, n_first: int, temperature: float = 1.0) -> dict:
         """pcd_decide_sequenced: the first n_first fields, their answers appended

@@ -60,7 +60,7 @@ int64_t plan_block_cap(const pcd_config &c, const pcd_limits &l) {
         (int64_t)c.n_kv_heads * (((int64_t)l.max_prefill_tokens * grp + ATT_ROWS - 1) / ATT_ROWS) * MAX_SPLITS;
     const int64_t br = (int64_t)c.n_kv_heads *
                        (((int64_t)l.max_branch_tokens * grp + ATT_ROWS - 1) / ATT_ROWS + l.max_requests) * MAX_SPLITS;
-    return std::max(pre, br);
+    return pre + br;  // a fused pass has both kinds of blocks
 }
 
 int64_t path_cap(const pcd_limits &l) { return 8 * (int64_t)l.max_candidates + l.max_gathers; }
@@ -99,7 +99,7 @@ Layout layout(const pcd_config &c, const pcd_limits &l) {
     L.z = take((size_t)l.max_gathers * 4);
     L.outs_bytes = align_up((size_t)(2 * l.max_candidates + 3 * l.max_fields + l.max_readouts + l.max_gathers) * 4 + 8 * 256);
     L.outs = take(L.outs_bytes);
-    const int64_t ints = 6 * (int64_t)rows + 8 * (int64_t)l.max_branch_tokens + 2 * (int64_t)l.max_readouts + 2 + 2 * (int64_t)l.max_gathers +
+    const int64_t ints = 8 * (int64_t)rows + 8 * (int64_t)l.max_branch_tokens + 2 * (int64_t)l.max_readouts + 2 + 2 * (int64_t)l.max_gathers +
                          2 * (int64_t)l.max_fields + 1 + (int64_t)l.max_candidates + 1 + path_cap(l) +
                          2 * (int64_t)l.max_requests;
     L.plan_bytes = align_up((size_t)ints * 4 + 20 * 256) + align_up((size_t)l.max_requests * 8) +
@@ -232,7 +232,7 @@ bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W,
 // KV head, and whose attention is run by `attn` (prefill or branch)
 template <class Attn>
 int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, int cap, bool branch, Attn attn,
-          hipStream_t st) {
+          hipStream_t st, void *kc2 = nullptr, void *vc2 = nullptr, int cap2 = 0, int kv_split = 0) {
     const int K_QKV = branch ? PCD_KC_BRANCH_QKV : PCD_KC_PREFILL_QKV;
     const int K_O = branch ? PCD_KC_BRANCH_O : PCD_KC_PREFILL_O;
     const int K_GU = branch ? PCD_KC_BRANCH_GATEUP : PCD_KC_PREFILL_GATEUP;
@@ -260,6 +260,10 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     g.kc = kc;
     g.vc = vc;
     g.cap = cap;
+    g.kc2 = kc2;  // rows from kv_split on (the branch tokens of a fused pass)
+    g.vc2 = vc2;
+    g.cap2 = cap2;
+    g.kv_split = kv_split;
     g.pos = pos;
     g.rope = reinterpret_cast<const float2 *>(m->ws + m->L.rope);
     g.n_q = nq;
@@ -420,9 +424,11 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
         for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
             const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
             for (int k = 0; k < ns && k * slen <= t_last; ++k)
-                blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0});
+                blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0, 1});
         }
     if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
+    std::vector<int32_t> tok_splits(n);
+    for (int t = 0; t < n; ++t) tok_splits[t] = (P0 + t) / slen + 1;
     std::vector<int32_t> pos;
     if (P0 > 0) {
         pos.resize(n);
@@ -434,6 +440,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     const uint64_t kvaddr = reinterpret_cast<uint64_t>(kv_buf);
     const uint64_t *d_kv = pk.put(&kvaddr, 1);
     const int32_t *d_stride = pk.put(&cap, 1);
+    const int32_t *d_tsp = pk.put(tok_splits.data(), n);
     const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
     if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
     m->settle_prefill();
@@ -464,8 +471,8 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
             a.req_stride = d_stride;
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
-            a.causal = true;
             a.q_pos0 = P0;
+            a.tok_splits = d_tsp;
             a.out = ao;
             a.part_o = part_o;
             a.part_ml = part_ml;
@@ -483,8 +490,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
                 t.n_tokens = n;
                 t.part_o = part_o;
                 t.part_ml = part_ml;
-                t.split_len = slen;
-                t.q_pos0 = P0;
+                t.tok_splits = d_tsp;
                 t.out = ao;
                 m->tbegin(PCD_KC_PREFILL_ATTN, st);
                 attention_merge(t, st);
@@ -618,8 +624,17 @@ int pcd_debug_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *pre
     return PCD_OK;
 }
 
-int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float T, pcd_outputs *outs,
-                    void *stream) {
+namespace {
+
+// One batched branch pass over the fields of n_req requests, each on its own
+// state.  With n_new > 0 (one request) the pass also carries new_tok, which
+// are appended to the state: its first rows are those tokens, causal over the
+// state's cached tokens and each other, their K/V written into the state's
+// buffer; the branch rows then see the whole extended prefix.  One pass thus
+// does the work of pcd_extend followed by pcd_decide, streaming every weight
+// matrix once.
+int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float T, pcd_outputs *outs,
+                void *stream, const int32_t *new_tok, int32_t n_new) {
     if (!states || !reqs || !outs || n_req <= 0) return fail(PCD_E_ARG, "null argument or no requests");
     if (!(T > 0.f) || !std::isfinite(T)) return fail(PCD_E_ARG, "temperature must be positive and finite");
     for (int r = 0; r < n_req; ++r)
@@ -633,8 +648,20 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     const pcd_config &c = m->cfg;
     const pcd_limits &lim = m->lim;
     if (n_req > lim.max_requests) return fail(PCD_E_CAP, "more requests than max_requests");
+    if (n_new > 0) {
+        if (n_req != 1) return fail(PCD_E_ARG, "new tokens go with exactly one request");
+        if (!new_tok) return fail(PCD_E_ARG, "null argument");
+        const pcd_state *s0 = states[0];
+        if (s0->P + n_new > s0->cap)
+            return fail(PCD_E_CAP, "the state's KV buffer holds " + std::to_string(s0->cap) + " tokens, " +
+                                       std::to_string(s0->P + n_new) + " needed");
+        for (int i = 0; i < n_new; ++i)
+            if (new_tok[i] < 0 || new_tok[i] >= c.vocab_size)
+                return fail(PCD_E_TOKEN, "token id " + std::to_string(new_tok[i]) + " outside the vocabulary");
+    }
+    const int P0 = n_new > 0 ? states[0]->P : 0;  // cached tokens before the new ones
     std::vector<int32_t> lens(n_req);
-    for (int r = 0; r < n_req; ++r) lens[r] = states[r]->P;
+    for (int r = 0; r < n_req; ++r) lens[r] = states[r]->P + (r == 0 ? n_new : 0);
     Plan p;
     std::string err;
     int rc = build_plan(c.vocab_size, c.max_seq, n_req, lens.data(), reqs, p, err);
@@ -646,44 +673,81 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
         return fail(PCD_E_CAP, "decide call of " + std::to_string(Tb) + " branch tokens, " + std::to_string(R) +
                                    " readouts, " + std::to_string(G) + " gathers exceeds the model's limits");
     const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim, d = c.d_model;
+    const int M = n_new + Tb;  // rows of the pass: new tokens, then branch tokens
+    const int64_t ws_rows = std::max(lim.max_prefill_tokens, lim.max_branch_tokens);
+    if (M > ws_rows)
+        return fail(PCD_E_CAP, std::to_string(n_new) + " new tokens and " + std::to_string(Tb) +
+                                   " branch tokens exceed the workspace's " + std::to_string(ws_rows) + " rows");
 
-    // attention blocks: per request, KV head and 64-row block; with too few
-    // row blocks for the chip the prefix keys are split over workgroups (the
-    // partials are then merged by a second kernel).  The last split of a row
-    // block also covers the branch keys of the fields its rows belong to.
-    std::vector<int32_t> req_splits(n_req);
+    // attention blocks, per KV head and 64-row block; with too few row blocks
+    // for the chip the keys are split over workgroups (the partials are then
+    // merged by a second kernel).  New tokens: causal over the extended
+    // prefix.  Branch tokens: the prefix of their request, split; the last
+    // split also covers the branch keys of the fields its rows belong to.
+    std::vector<int32_t> tok_splits(M, 1);
     std::vector<uint64_t> req_kv(n_req);
     std::vector<AttnBlock> blocks;
     bool any_split = false;
-    int64_t row_blocks = 0;
+    int64_t row_blocks = (int64_t)c.n_kv_heads * (((int64_t)n_new * grp + ATT_ROWS - 1) / ATT_ROWS);
     for (int r = 0; r < n_req; ++r)
         row_blocks += (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
+    auto split_keys = [&](int keys, int &s, int &slen) {
+        s = att_splits(row_blocks, (keys + 63) / 64);
+        if (keys == 0) {
+            s = 1;
+            slen = 0;
+            return;
+        }
+        slen = ((keys + s - 1) / s + 63) / 64 * 64;
+        s = (keys + slen - 1) / slen;
+    };
+    if (n_new > 0) {
+        int s, slen;
+        split_keys(P0 + n_new, s, slen);
+        any_split |= s > 1;
+        for (int t = 0; t < n_new; ++t) tok_splits[t] = (P0 + t) / slen + 1;
+        const int rows = n_new * grp;
+        for (int g = 0; g < c.n_kv_heads; ++g)
+            for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
+                const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
+                for (int k = 0; k < s && k * slen <= t_last; ++k)
+                    blocks.push_back(
+                        AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1});
+            }
+    }
     for (int r = 0; r < n_req; ++r) {
         const int P = lens[r];
-        const int tiles = (P + 63) / 64;
-        int s = att_splits(row_blocks, tiles);
-        const int slen = ((P + s - 1) / s + 63) / 64 * 64;
-        s = (P + slen - 1) / slen;
+        int s, slen;
+        split_keys(P, s, slen);
         any_split |= s > 1;
-        req_splits[r] = s;
+        for (int t = p.r_tok[r]; t < p.r_tok[r + 1]; ++t) tok_splits[n_new + t] = s;
         req_kv[r] = reinterpret_cast<uint64_t>(states[r]->kv);
-        const int row_beg = p.r_tok[r] * grp, row_end = p.r_tok[r + 1] * grp;
+        const int row_beg = (n_new + p.r_tok[r]) * grp, row_end = (n_new + p.r_tok[r + 1]) * grp;
         for (int g = 0; g < c.n_kv_heads; ++g)
             for (int r0 = row_beg; r0 < row_end; r0 += ATT_ROWS) {
                 const int nr = std::min(ATT_ROWS, row_end - r0);
-                const int t_first = r0 / grp, t_last = (r0 + nr - 1) / grp;
+                const int b_first = r0 / grp - n_new, b_last = (r0 + nr - 1) / grp - n_new;  // plan indices
                 for (int k = 0; k < s; ++k)
                     blocks.push_back(AttnBlock{r, g, r0, nr, k * slen, std::min(P, (k + 1) * slen), k, s,
-                                               k == s - 1 ? p.fs[t_first] : 0, k == s - 1 ? t_last + 1 : 0});
+                                               k == s - 1 ? p.fs[b_first] : 0, k == s - 1 ? b_last + 1 : 0, 0});
             }
     }
     if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
-    const int32_t *d_tok = pk.put(p.tok.data(), Tb);
-    const int32_t *d_pos = pk.put(p.pos.data(), Tb);
-    const int32_t *d_req = pk.put(p.req.data(), Tb);
+    std::vector<int32_t> toks(M), poss(M);
+    for (int i = 0; i < n_new; ++i) {
+        toks[i] = new_tok[i];
+        poss[i] = P0 + i;
+    }
+    std::copy(p.tok.begin(), p.tok.end(), toks.begin() + n_new);
+    std::copy(p.pos.begin(), p.pos.end(), poss.begin() + n_new);
+    std::vector<int32_t> ro_rows(p.ro_tok);
+    for (auto &v : ro_rows) v += n_new;
+    const int32_t *d_tok = pk.put(toks.data(), M);
+    const int32_t *d_pos = pk.put(poss.data(), M);
+    const int32_t *d_tsp = pk.put(tok_splits.data(), M);
     const int32_t *d_fs = pk.put(p.fs.data(), Tb);
     const int32_t *d_nsc = pk.put(p.nsc.data(), Tb);
     const int32_t *d_par = pk.put(p.par.data(), Tb);
@@ -699,7 +763,7 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
         }
     }
     const int4 *d_chain = reinterpret_cast<const int4 *>(pk.put(chain.data(), chain.size()));
-    const int32_t *d_ro = pk.put(p.ro_tok.data(), R);
+    const int32_t *d_ro = pk.put(ro_rows.data(), R);
     const int32_t *d_goff = pk.put(p.g_off.data(), R + 1);
     const int32_t *d_gtok = pk.put(p.g_tok.data(), G);
     const int32_t *d_gro = pk.put(p.g_ro.data(), G);
@@ -710,7 +774,6 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     std::vector<int32_t> strides(n_req);
     for (int r = 0; r < n_req; ++r) strides[r] = states[r]->cap;
     const int32_t *d_stride = pk.put(strides.data(), n_req);
-    const int32_t *d_rsp = pk.put(req_splits.data(), n_req);
     const uint64_t *d_kv = pk.put(req_kv.data(), n_req);
     const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
     if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
@@ -732,14 +795,20 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     HIP_TRY(hipEventRecord(m->ev[0], st));
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     m->tbegin(PCD_KC_OTHER, st);
-    embed(c.dtype, d_tok, Tb, m->embed, d, x, m->an[0], c.rms_eps, m->ws + m->L.h, st);
+    embed(c.dtype, d_tok, M, m->embed, d, x, m->an[0], c.rms_eps, m->ws + m->L.h, st);
     m->tend(st);
     const size_t layer_elems = (size_t)2 * c.n_kv_heads * Tb * hd;
+    const size_t es = esize(m), sslab = n_new > 0 ? (size_t)states[0]->cap * hd : 0;
     float *part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
     float2 *part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
     for (int l = 0; l < c.n_layers; ++l) {
-        char *kc = m->ws + m->L.kvb + (size_t)l * layer_elems * esize(m);
-        char *vc = kc + layer_elems / 2 * esize(m);
+        char *kc = m->ws + m->L.kvb + (size_t)l * layer_elems * es;
+        char *vc = kc + layer_elems / 2 * es;
+        // new tokens' K/V: the state's slabs of this layer, at row P0
+        char *skc = n_new > 0 ? static_cast<char *>(states[0]->kv) +
+                                    ((size_t)l * 2 * c.n_kv_heads * sslab + (size_t)P0 * hd) * es
+                              : nullptr;
+        char *svc = n_new > 0 ? skc + (size_t)c.n_kv_heads * sslab * es : nullptr;
         auto attn = [&](void *q, void *ao) {
             AttnCall a{};
             a.dt = c.dtype;
@@ -752,11 +821,13 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
             a.req_stride = d_stride;
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
-            a.causal = false;
+            a.q_pos0 = P0;
+            a.branch0 = n_new;
+            a.tok_splits = d_tsp;
             a.out = ao;
             a.part_o = part_o;
             a.part_ml = part_ml;
-            a.n_tokens = Tb;
+            a.n_tokens = M;
             a.kb = kc;
             a.vb = vc;
             a.cap = Tb;
@@ -774,11 +845,10 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
                 t.hd = hd;
                 t.n_heads = c.n_heads;
                 t.n_kv_heads = c.n_kv_heads;
-                t.n_tokens = Tb;
+                t.n_tokens = M;
                 t.part_o = part_o;
                 t.part_ml = part_ml;
-                t.tok_req = d_req;
-                t.req_splits = d_rsp;
+                t.tok_splits = d_tsp;
                 t.out = ao;
                 m->tbegin(PCD_KC_BRANCH_TAIL, st);
                 attention_merge(t, st);
@@ -786,7 +856,8 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
             }
             return PCD_OK;
         };
-        rc = layer(m, l, Tb, d_pos, kc, vc, Tb, true, attn, st);
+        rc = n_new > 0 ? layer(m, l, M, d_pos, skc, svc, states[0]->cap, true, attn, st, kc, vc, Tb, n_new)
+                       : layer(m, l, M, d_pos, kc, vc, Tb, true, attn, st);
         if (rc != PCD_OK) return rc;
     }
     HIP_TRY(hipEventRecord(m->ev[1], st));
@@ -859,6 +930,7 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     float ms_b = 0.f, ms_r = 0.f;
     (void)hipEventElapsedTime(&ms_b, m->ev[0], m->ev[1]);
     (void)hipEventElapsedTime(&ms_r, m->ev[1], m->ev[2]);
+    if (n_new > 0) states[0]->P += n_new;
     m->stats.branch_passes += 1;
     m->stats.last_branch_ms = ms_b;
     m->stats.last_readout_ms = ms_r;
@@ -866,6 +938,32 @@ int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n
     m->stats.last_readouts = R;
     m->stats.last_gathers = G;
     m->stats.last_requests = n_req;
+    return PCD_OK;
+}
+
+}  // namespace
+
+int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float T, pcd_outputs *outs,
+                    void *stream) {
+    return decide_impl(states, reqs, n_req, T, outs, stream, nullptr, 0);
+}
+
+int pcd_extend_decide(pcd_state *s, const int32_t *tokens, int32_t n_tokens, const pcd_field *fields,
+                      int32_t n_fields, const pcd_candidate *candidates, int32_t n_candidates, float temperature,
+                      pcd_outputs *out, void *stream) {
+    if (n_tokens < 0) return fail(PCD_E_ARG, "negative token count");
+    pcd_request r{fields, n_fields, candidates, n_candidates};
+    return decide_impl(&s, &r, 1, temperature, out, stream, tokens, n_tokens);
+}
+
+int pcd_new_state(pcd_model *m, void *kv_buf, size_t kv_bytes, pcd_state **out) {
+    if (!m || !kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+    if (kv_bytes < per_token_bytes(m)) return fail(PCD_E_CAP, "KV buffer smaller than one token");
+    const int32_t cap = (int32_t)std::min<size_t>(kv_bytes / per_token_bytes(m), (size_t)m->cfg.max_seq);
+    pcd_state *s = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_buf, 0, cap};
+    if (!s) return fail(PCD_E_NOMEM, "state allocation");
+    m->n_states++;
+    *out = s;
     return PCD_OK;
 }
 

@@ -43,6 +43,8 @@ struct GemmCall {
     void *out;       // SwiGlu: [M][N] of dt;  Qkv: q buffer [M][Hq][hd]
     void *kc, *vc;   // Qkv: K and V cache of this layer, [Hkv][cap][hd] each
     int32_t cap;     // Qkv: tokens per KV head in the cache
+    void *kc2, *vc2; // Qkv (optional): rows m >= kv_split go to row m - kv_split of this cache instead
+    int32_t cap2, kv_split;
     const int32_t *pos;  // Qkv: position of each row (NULL: row index)
     const float2 *rope;  // Qkv: [max_seq][hd/2] (cos, sin)
     int32_t n_q, n_k, hd;    // Qkv: columns of q and of k; head dim
@@ -74,6 +76,7 @@ void resid_norm(int dt, const float *part, int32_t splits, int32_t M, int32_t N,
 // partials for attention_merge.
 struct AttnBlock {
     int32_t req, g, row0, nrows, key0, key1, split, nsplit, sfx_lo, sfx_hi;
+    int32_t causal;  // rows see keys up to their own position (q_pos0 + token); else the whole key range
 };
 struct AttnCall {
     int dt;
@@ -83,8 +86,10 @@ struct AttnCall {
     const int32_t *req_stride; // per request: tokens per (layer, K|V, KV head) slab of its KV buffer
     const AttnBlock *blocks;
     int32_t n_blocks;
-    bool causal;            // prefill / extend: row token t sees keys <= q_pos0 + t (rows with q_pos0 + t < key0 are skipped)
-    int32_t q_pos0;         // causal: position of the call's first token (the state's length before it)
+    int32_t q_pos0;         // causal blocks: row token t is at position q_pos0 + t and sees keys <= q_pos0 + t
+                            // (rows with q_pos0 + t < key0 are skipped)
+    int32_t branch0;        // first row token of the branch tokens (their plan index is token - branch0)
+    const int32_t *tok_splits;  // per row token: key splits covering it (<= 1: written directly)
     void *out;              // [tokens][Hq][hd] (dt)
     float *part_o;          // [split][tokens][Hq][hd] unnormalised
     float2 *part_ml;        // [split][tokens][Hq] (max in log2 units, sum)
@@ -103,10 +108,8 @@ struct TailCall {
     int32_t hd, n_heads, n_kv_heads, n_tokens;
     const float *part_o;
     const float2 *part_ml;
-    const int32_t *tok_req, *req_splits;  // branch: splits used by each request
-    int32_t split_len;                    // causal (> 0): token t has splits 0..(q_pos0 + t)/split_len
-    int32_t q_pos0;
-    void *out;                            // [tokens][Hq][hd]
+    const int32_t *tok_splits;  // per token: its splits are 0..tok_splits[t]-1 (<= 1: nothing to merge)
+    void *out;                  // [tokens][Hq][hd]
 };
 void attention_merge(const TailCall &c, hipStream_t st);
 

@@ -132,8 +132,8 @@ template <int NB> struct GemmArgs {
 
 struct EpiArgs {
     float *x, *part;
-    void *out, *kc, *vc;
-    int32_t cap, n_q, n_k, hd;
+    void *out, *kc, *vc, *kc2, *vc2;
+    int32_t cap, cap2, kv_split, n_q, n_k, hd;
     const int32_t *pos;
     const float2 *rope;
     float2 *ro_part;
@@ -391,12 +391,17 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
                 T *dst;
                 if (n < e.n_q) {
                     dst = reinterpret_cast<T *>(e.out) + (size_t)m * e.n_q + (n - j);
-                } else if (n < e.n_q + e.n_k) {
-                    const int kh = (n - e.n_q) / hd;
-                    dst = reinterpret_cast<T *>(e.kc) + ((size_t)kh * e.cap + m) * hd;
                 } else {
-                    const int vh = (n - e.n_q - e.n_k) / hd;
-                    dst = reinterpret_cast<T *>(e.vc) + ((size_t)vh * e.cap + m) * hd;
+                    // rows from kv_split on go to the second cache (the branch tokens of a fused pass)
+                    const bool second = m >= e.kv_split;
+                    const int mr = second ? m - e.kv_split : m, cap = second ? e.cap2 : e.cap;
+                    if (n < e.n_q + e.n_k) {
+                        const int kh = (n - e.n_q) / hd;
+                        dst = reinterpret_cast<T *>(second ? e.kc2 : e.kc) + ((size_t)kh * cap + mr) * hd;
+                    } else {
+                        const int vh = (n - e.n_q - e.n_k) / hd;
+                        dst = reinterpret_cast<T *>(second ? e.vc2 : e.vc) + ((size_t)vh * cap + mr) * hd;
+                    }
                 }
                 dst[j] = from_f<T>(v1);
                 dst[j + half] = from_f<T>(v2);
@@ -446,6 +451,10 @@ static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     e.kc = c.kc;
     e.vc = c.vc;
     e.cap = c.cap;
+    e.kc2 = c.kc2;
+    e.vc2 = c.vc2;
+    e.cap2 = c.cap2;
+    e.kv_split = c.kc2 ? c.kv_split : c.M;
     e.n_q = c.n_q;
     e.n_k = c.n_k;
     e.hd = c.hd;
@@ -785,10 +794,8 @@ __device__ __forceinline__ void attn_write(const AttnCall &c, const AttnBlock &b
         if (w * 16 + qi >= blk.nrows) continue;
         const int row = blk.row0 + w * 16 + qi;
         const int t = row / grp, h = blk.g * grp + row % grp;
-        const int ta = c.q_pos0 + t;            // causal: the row's position
-        if (c.causal && ta < blk.key0) continue;  // causal row with no key in this split
-        // a causal row whose keys all lie in split 0 has no partials to merge
-        if (blk.nsplit == 1 || (c.causal && blk.split == 0 && ta < blk.key1)) {
+        if (blk.causal && c.q_pos0 + t < blk.key0) continue;  // causal row with no key in this split
+        if (c.tok_splits[t] <= 1) {
             T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
             const float inv = 1.0f / lq;
 #pragma unroll
@@ -840,10 +847,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     Frag<T> qf[HS];
 #pragma unroll
     for (int s = 0; s < HS; ++s) ld8(qf[s], Q + ((size_t)tq * Hq + hq) * HD + s * 32 + lg * 8);
-    const int kend_row = c.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
+    const int kend_row = blk.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
 
     int kmax = blk.key1;
-    if (c.causal) {
+    if (blk.causal) {
         const int last = c.q_pos0 + (blk.row0 + blk.nrows - 1) / grp + 1;
         kmax = last < kmax ? last : kmax;
     }
@@ -851,7 +858,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     const int n_sfx = blk.sfx_hi > blk.sfx_lo ? (blk.sfx_hi - blk.sfx_lo + KT - 1) / KT : 0;
     const int n_tiles = n_pre + n_sfx;
     RowVis vis{};
-    if (n_sfx > 0) row_vis_init(vis, c, tq);
+    if (n_sfx > 0) row_vis_init(vis, c, tq - c.branch0);
 
     // K chunks: 16 consecutive threads cover one key row (coalesced, row-major
     // LDS store).  V chunks: the 64 lanes of a wave hold 64 consecutive keys of
@@ -1070,9 +1077,9 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     const bool row_ok = (w * 16 + lr) < blk.nrows;
     const int rr = row_ok ? blk.row0 + w * 16 + lr : blk.row0;
     const int tq = rr / grp;
-    const int kend_row = c.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
+    const int kend_row = blk.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
     int kmax = blk.key1;
-    if (c.causal) {
+    if (blk.causal) {
         const int last = c.q_pos0 + (blk.row0 + blk.nrows - 1) / grp + 1;
         kmax = last < kmax ? last : kmax;
     }
@@ -1081,7 +1088,7 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     const int n_tiles = n_pre + n_sfx;
     RowVis vis{};
     if (n_sfx > 0) {
-        row_vis_init(vis, c, tq);
+        row_vis_init(vis, c, tq - c.branch0);
         vm_wait<0>();  // its loads must not sit in the counter behind the DMA below
     }
 
@@ -1300,7 +1307,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
     const int Hq = c.n_heads;
     if (id >= c.n_tokens * Hq) return;
     const int t = id / Hq, h = id % Hq;
-    const int ns = c.split_len > 0 ? (c.q_pos0 + t) / c.split_len + 1 : c.req_splits[c.tok_req[t]];
+    const int ns = c.tok_splits[t];
     if (ns <= 1) return;  // written directly by the attention kernel
     float m = -INFINITY, l = 0.f, o[PL];
 #pragma unroll

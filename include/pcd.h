@@ -230,6 +230,28 @@ int pcd_state_tokens(const pcd_state *s);
 int pcd_decide(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pcd_candidate *candidates,
                int32_t n_candidates, float temperature, pcd_outputs *out, void *stream);
 
+/* Single-pass mode: append tokens[0..n_tokens) to the state AND decide the
+ * request's fields against the extended prefix, in ONE batched decoder pass
+ * whose first rows are the new tokens (causal over the cached ones and each
+ * other, their K/V written into the state's buffer) and whose remaining rows
+ * are the fields' branch tokens ("Parallel Constrained Decoding", the Java +
+ * llama.cpp engine page, "Java engine details": its optional single-pass
+ * mode, prefill and field suffixes in one forward pass).  The results equal
+ * pcd_extend followed by pcd_decide, with every weight matrix streamed once.
+ * n_tokens may be 0 (then this is pcd_decide).  The pass needs n_tokens plus
+ * the branch tokens within the workspace's rows (the larger of
+ * max_prefill_tokens and max_branch_tokens).  Errors as for pcd_extend and
+ * pcd_decide, all before any device work; on error the state is unchanged.
+ * Counted as one branch pass. */
+int pcd_extend_decide(pcd_state *s, const int32_t *tokens, int32_t n_tokens, const pcd_field *fields,
+                      int32_t n_fields, const pcd_candidate *candidates, int32_t n_candidates, float temperature,
+                      pcd_outputs *out, void *stream);
+
+/* An empty state (0 tokens) over the caller's device buffer kv_buf (capacity
+ * as for pcd_prefill), for pcd_extend / pcd_extend_decide to fill: a cold
+ * request in single-pass mode is pcd_new_state + pcd_extend_decide. */
+int pcd_new_state(pcd_model *m, void *kv_buf, size_t kv_bytes, pcd_state **out);
+
 /* The first-field round: decide fields[0..n_first) in one batched pass,
  * append each of them (its scaffold followed by its argmax candidate's
  * tokens, in field order) to the state with pcd_extend, then decide the

@@ -179,3 +179,77 @@ def test_bf16_two_layer_warm_head_and_first_field_round(q15_l2):
     st.close()
     hs.close()
     m.close()
+
+
+# ---------------------------------------------------------------------------
+# single-pass mode: new tokens and branch tokens in one decoder pass
+# ---------------------------------------------------------------------------
+
+def _fused_model(shape, weights, prefix_len, fields):
+    """Limits with room for the prefix rows and the branch rows in one pass."""
+    plan = cpd.debug_plan(shape.vocab_size, shape.max_seq, [prefix_len], [fields])
+    return _model(shape, weights, [prefix_len], [fields], prefix_len + len(plan["tok"]))
+
+
+def test_tiny_fused_cold_request(tiny_w, tiny_dec):
+    """An empty state + extend_decide(prefix, fields): the decisions of
+    prefill + decide, and the state's KV that prefill would leave, from one
+    pass (150-token prefix across three 64-key tiles, trie fields)."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(31)
+    prefix = _tokens(rng, sh.vocab_size, 150)
+    fields = pi.make_workload("cfg0t").requests[0].fields
+    m = _fused_model(sh, tiny_w, len(prefix), fields)
+    st = m.new_state(len(prefix))
+    got = [m.extend_decide(st, prefix, fields, debug=True)]
+    assert st.n_tokens == len(prefix)
+    ref = opcd.decide(tiny_dec, [(prefix, fields)])
+    _compare("tiny-fused-cold", got, ref, ref.plan.c_path_off, "f32")
+    kv = _kv(st, sh, len(prefix), np.float32)
+    rkv = opcd.prefill(tiny_dec, prefix)
+    err = max(float(np.max(np.abs(kv[l, i] - rkv[l][i]))) for l in range(sh.n_layers) for i in range(2))
+    assert err < 1e-4
+    s = m.stats()
+    assert s["branch_passes"] == 1 and s["prefill_passes"] == 0
+    # the state serves later decides as a prefilled one would
+    again = [m.decide(st, fields, debug=True)]
+    _compare("tiny-fused-then-decide", again, ref, ref.plan.c_path_off, "f32")
+    st.close()
+    m.close()
+
+
+def test_tiny_fused_warm_request(tiny_w, tiny_dec):
+    """A cached head (70 tokens) forked, then extend_decide(input of 40
+    tokens, fields); and extend_decide with no new tokens is decide."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(32)
+    head, inp = _tokens(rng, sh.vocab_size, 70), _tokens(rng, sh.vocab_size, 40)
+    fields = pi.random_trie_fields(940, sh.vocab_size, 3)
+    m = _fused_model(sh, tiny_w, len(head) + len(inp), fields)
+    hs = m.prefill(head)
+    st = hs.fork(capacity=len(head) + len(inp))
+    got = [m.extend_decide(st, inp, fields, debug=True)]
+    ref = opcd.decide(tiny_dec, [(head + inp, fields)])
+    _compare("tiny-fused-warm", got, ref, ref.plan.c_path_off, "f32")
+    got0 = [m.extend_decide(st, [], fields, debug=True)]
+    _compare("tiny-fused-none", got0, ref, ref.plan.c_path_off, "f32")
+    st.close()
+    hs.close()
+    m.close()
+
+
+def test_bf16_two_layer_fused_cold(q15_l2):
+    """The 28-field workload (512-token prefix) and the 255-option ID
+    workload (2048-token prefix) at the 1.5B widths, 2 layers, each as one
+    fused pass on an empty state."""
+    sh, w, dec = q15_l2
+    for name in ("cfg1", "cfg2"):
+        wl = pi.make_workload(name)
+        prefix, fields = wl.requests[0].prefix, wl.requests[0].fields
+        m = _fused_model(sh, w, len(prefix), fields)
+        st = m.new_state(len(prefix))
+        got = [m.extend_decide(st, prefix, fields, debug=True)]
+        ref = opcd.decide(dec, [(list(prefix), fields)])
+        _compare(f"q15-L2-fused-{name}", got, ref, ref.plan.c_path_off, "bf16")
+        st.close()
+        m.close()

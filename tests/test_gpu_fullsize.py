@@ -119,6 +119,25 @@ def test_bench_request_full_depth(q15_full):
     _full_case("cfg1-full", sh, w, "cfg1")
 
 
+def test_bench_request_full_depth_fused(q15_full):
+    """The bench's request in single-pass mode (empty state, the 512 prefix
+    tokens and the 287 branch tokens in one 28-layer pass)."""
+    sh, w = q15_full
+    wl = pi.make_workload("cfg1")
+    prefix, fields = wl.requests[0].prefix, wl.requests[0].fields
+    plan = cpd.debug_plan(sh.vocab_size, sh.max_seq, [len(prefix)], [fields])
+    dev = cpd.upload_weights(w.mats, sh.n_layers, sh.d_model, "cuda:0")
+    lim = cpd.limits_for(sh.vocab_size, sh.max_seq, [len(prefix)], [fields], len(prefix) + len(plan["tok"]))
+    m = cpd.PcdModel(cpd.config_of(sh), dev, lim)
+    st = m.new_state(len(prefix))
+    got = [m.extend_decide(st, prefix, fields, debug=True)]
+    ref = opcd.decide(odec.Decoder(w, np.float64), [(list(prefix), fields)])
+    _check("cfg1-full-fused", got, ref)
+    _field_sums_to_one(got, [fields])
+    st.close()
+    m.close()
+
+
 def test_id_field_full_depth(q15_full):
     """2048-token prefix; one 255-option ID field resolved by trie
     continuation rows, plus 3 booleans; 28 layers."""
