@@ -49,12 +49,21 @@ def algorithmic_work(sh, P, Tb, R):
     # prefix part of the shared-prefix attention: the prefix K/V of a layer read once
     w["branch_attn"] = (4.0 * sh.n_heads * hd * Tb * P, float(P * kv_tok + Tb * nq * e))
     w["readout_lmhead"] = gemm(R, V, d, 0)
+    # single-pass mode: the prefix rows and the branch rows in one pass
+    Mf = P + Tb
+    w["fused_qkv"] = gemm(Mf, nq + 2 * nk, d, e)
+    w["fused_o"] = gemm(Mf, d, nq, 4)
+    w["fused_gateup"] = gemm(Mf, 2 * F, d, 0)
+    w["fused_gateup"] = (w["fused_gateup"][0], w["fused_gateup"][1] + Mf * F * e)
+    w["fused_down"] = gemm(Mf, d, F, 4)
+    w["fused_attn"] = (w["prefill_attn"][0] + w["branch_attn"][0], w["prefill_attn"][1] + Tb * nq * e)
     return w
 
 
 BOUND = {"prefill_qkv": "mfma", "prefill_o": "mfma", "prefill_gateup": "mfma", "prefill_down": "mfma",
          "prefill_attn": "mfma", "branch_qkv": "hbm", "branch_o": "hbm", "branch_gateup": "hbm",
-         "branch_down": "hbm", "branch_attn": "hbm", "readout_lmhead": "hbm"}
+         "branch_down": "hbm", "branch_attn": "hbm", "readout_lmhead": "hbm", "fused_qkv": "mfma",
+         "fused_o": "mfma", "fused_gateup": "mfma", "fused_down": "mfma", "fused_attn": "mfma"}
 
 
 def roofline_entry(cls, total_ms, launches, work, peak_mfma):
@@ -186,35 +195,57 @@ def main():
     weights = pi.make_weights(sh, wl.weight_seed)
     print(f"# weights drawn in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
     dev = cpd.upload_weights(weights.mats, sh.n_layers, sh.d_model, "cuda:0")
-    lim = cpd.limits_for(sh.vocab_size, sh.max_seq, [len(req.prefix)], [req.fields])
+    plan = cpd.debug_plan(sh.vocab_size, sh.max_seq, [len(req.prefix)], [req.fields])
+    Tb, R = len(plan["tok"]), len(plan["ro_tok"])
+    # room for the single-pass mode: the prefix rows and the branch rows in one pass
+    lim = cpd.limits_for(sh.vocab_size, sh.max_seq, [len(req.prefix)], [req.fields], len(req.prefix) + Tb)
     model = cpd.PcdModel(cpd.config_of(sh), dev, lim)
     kv = torch.empty(model.state_bytes(len(req.prefix)), dtype=torch.uint8, device="cuda:0")
 
-    def step():
+    def step_two_pass():  # prefill pass, then the branch pass
         st = model.prefill(req.prefix, kv)
         out = model.decide(st, req.fields)
         st.close()
         return out
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    lat = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        s0 = time.perf_counter()
-        out = step()
-        lat.append(time.perf_counter() - s0)
-    torch.cuda.synchronize()
-    total = time.perf_counter() - t0
-    ms_per_step = total / args.steps * 1e3
-    p50 = float(np.percentile(np.array(lat) * 1e3, 50))
-    p90 = float(np.percentile(np.array(lat) * 1e3, 90))
+    def step_single_pass():  # an empty state; the prefix rows and the branch rows in one pass
+        st = model.new_state(len(req.prefix), kv)
+        out = model.extend_decide(st, req.prefix, req.fields)
+        st.close()
+        return out
+
+    def timed(step):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        lat = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            s0 = time.perf_counter()
+            out = step()
+            lat.append(time.perf_counter() - s0)
+        torch.cuda.synchronize()
+        r = {"ms_per_step": (time.perf_counter() - t0) / args.steps * 1e3,
+             "p50_request_ms": float(np.percentile(np.array(lat) * 1e3, 50)),
+             "p90_request_ms": float(np.percentile(np.array(lat) * 1e3, 90)), "out": out}
+        st = model.stats()
+        r["phases_ms"] = {k: round(st[f"last_{k}_ms"], 4) for k in ("prefill", "branch", "readout")}
+        return r
+
     nf = len(req.fields)
-    print(f"# {args.steps} steps: {ms_per_step:.3f} ms/step, p50 {p50:.3f} ms, p90 {p90:.3f} ms",
-          file=sys.stderr, flush=True)
-    stats = model.stats()
-    dev_ms = stats["last_prefill_ms"] + stats["last_branch_ms"] + stats["last_readout_ms"]
+    modes = {"two-pass": timed(step_two_pass), "single-pass": timed(step_single_pass)}
+    mode = min(modes, key=lambda k: modes[k]["ms_per_step"])
+    head = modes[mode]
+    step, out = (step_single_pass if mode == "single-pass" else step_two_pass), head["out"]
+    ms_per_step, p50, p90 = head["ms_per_step"], head["p50_request_ms"], head["p90_request_ms"]
+    for k, r in modes.items():
+        print(f"# {k}: {args.steps} steps: {r['ms_per_step']:.3f} ms/step, p50 {r['p50_request_ms']:.3f} ms, "
+              f"p90 {r['p90_request_ms']:.3f} ms", file=sys.stderr, flush=True)
+    if mode == "single-pass":
+        phases = {"fused": head["phases_ms"]["branch"], "readout": head["phases_ms"]["readout"]}
+    else:
+        phases = dict(head["phases_ms"])
+    dev_ms = sum(phases.values())
 
     # Warm requests: the prefix's first tokens are a cached head; each request
     # forks it, appends its own input tokens and decides (one extend + one
@@ -225,30 +256,33 @@ def main():
         head_n = len(req.prefix) - args.warm_input
         f0 = req.fields[0]
         cap = len(req.prefix) + len(f0.scaffold) + max(len(c) for c in f0.candidates)
-        head = model.prefill(req.prefix[:head_n])
+        head_st = model.prefill(req.prefix[:head_n])
         kv_w = torch.empty(model.state_bytes(cap), dtype=torch.uint8, device="cuda:0")
 
-        def warm_step(first_field_round):
-            st = head.fork(kv=kv_w)
-            st.extend(req.prefix[head_n:])
-            if first_field_round:
-                model.decide_sequenced(st, req.fields, 1)
+        def warm_step(kind):
+            st = head_st.fork(kv=kv_w)
+            if kind == "single_pass_p50_ms":
+                model.extend_decide(st, req.prefix[head_n:], req.fields)
             else:
-                model.decide(st, req.fields)
+                st.extend(req.prefix[head_n:])
+                if kind == "first_field_round_p50_ms":
+                    model.decide_sequenced(st, req.fields, 1)
+                else:
+                    model.decide(st, req.fields)
             st.close()
 
         warm = {"head_tokens": head_n, "input_tokens": args.warm_input}
-        for key, ffr in (("p50_request_ms", False), ("first_field_round_p50_ms", True)):
+        for key in ("single_pass_p50_ms", "two_pass_p50_ms", "first_field_round_p50_ms"):
             for _ in range(args.warmup):
-                warm_step(ffr)
+                warm_step(key)
             torch.cuda.synchronize()
             lw = []
             for _ in range(args.steps):
                 s0 = time.perf_counter()
-                warm_step(ffr)
+                warm_step(key)
                 lw.append(time.perf_counter() - s0)
             warm[key] = round(float(np.percentile(np.array(lw) * 1e3, 50)), 4)
-        head.close()
+        head_st.close()
 
     # the same steps again with every kernel launch bracketed by hipEvents on the library's stream
     model.set_kernel_timing(True)
@@ -257,8 +291,6 @@ def main():
     torch.cuda.synchronize()
     kt = model.kernel_times()
     model.set_kernel_timing(False)
-    plan = cpd.debug_plan(sh.vocab_size, sh.max_seq, [len(req.prefix)], [req.fields])
-    Tb, R = len(plan["tok"]), len(plan["ro_tok"])
     work = algorithmic_work(sh, len(req.prefix), Tb, R)
     peak_mfma = BF16_PEAK_TFLOPS if sh.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernels = {c: roofline_entry(c, ms, n, work, peak_mfma) for c, (ms, n) in kt.items() if n > 0 and c in work}
@@ -285,13 +317,14 @@ def main():
         "config": {"workload": f"{args.workload}: {sh.name} random-init {sh.dtype}, {len(req.prefix)}-token "
                                f"prefix, {nf} fields, {Tb} branch tokens, {R} readouts, batch 1",
                    "layers": sh.n_layers, "prefix_tokens": len(req.prefix), "fields": nf,
-                   "branch_tokens": Tb, "readouts": R},
-        "phases_ms": {"prefill": round(stats["last_prefill_ms"], 4), "branch": round(stats["last_branch_ms"], 4),
-                      "readout": round(stats["last_readout_ms"], 4)},
+                   "branch_tokens": Tb, "readouts": R, "mode": mode},
+        "phases_ms": phases,
         "device_fields_per_s": round(nf / (dev_ms / 1e3), 2),
-        "passes": {"prefill": 1, "branch": 1,
-                   "token_by_token_equivalent": int(sum(len(f.scaffold) + len(f.candidates[int(a)])
-                                                        for f, a in zip(req.fields, out["argmax"])))},
+        "passes": dict({"fused": 1} if mode == "single-pass" else {"prefill": 1, "branch": 1},
+                       token_by_token_equivalent=int(sum(len(f.scaffold) + len(f.candidates[int(a)])
+                                                         for f, a in zip(req.fields, out["argmax"])))),
+        "modes": {k: {"ms_per_step": round(r["ms_per_step"], 4), "p50_request_ms": round(r["p50_request_ms"], 4),
+                      "phases_ms": r["phases_ms"]} for k, r in modes.items()},
         "roofline": kernels[dominant],
         "kernels": {c: {k: v for k, v in e.items() if k in ("achieved", "unit", "frac", "avg_launch_us",
                                                             "launches", "bound")} for c, e in kernels.items()},

@@ -30,7 +30,7 @@ EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_pr
 
 KERNEL_CLASSES = ("prefill_qkv", "prefill_attn", "prefill_o", "prefill_gateup", "prefill_down", "branch_qkv",
                   "branch_attn", "branch_tail", "branch_o", "branch_gateup", "branch_down", "readout_lmhead",
-                  "other")
+                  "other", "fused_qkv", "fused_attn", "fused_o", "fused_gateup", "fused_down")
 
 
 class PcdError(RuntimeError):

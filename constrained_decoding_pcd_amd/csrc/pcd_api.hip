@@ -230,13 +230,16 @@ bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W,
 
 // one decoder layer over M rows whose K/V go to (kc, vc) with `cap` tokens per
 // KV head, and whose attention is run by `attn` (prefill or branch)
+enum class Pass { Prefill, Branch, Fused };  // which timing classes a layer's kernels count under
+
 template <class Attn>
-int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, int cap, bool branch, Attn attn,
+int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, int cap, Pass kind, Attn attn,
           hipStream_t st, void *kc2 = nullptr, void *vc2 = nullptr, int cap2 = 0, int kv_split = 0) {
-    const int K_QKV = branch ? PCD_KC_BRANCH_QKV : PCD_KC_PREFILL_QKV;
-    const int K_O = branch ? PCD_KC_BRANCH_O : PCD_KC_PREFILL_O;
-    const int K_GU = branch ? PCD_KC_BRANCH_GATEUP : PCD_KC_PREFILL_GATEUP;
-    const int K_DN = branch ? PCD_KC_BRANCH_DOWN : PCD_KC_PREFILL_DOWN;
+    const bool br = kind == Pass::Branch, fu = kind == Pass::Fused;
+    const int K_QKV = fu ? PCD_KC_FUSED_QKV : br ? PCD_KC_BRANCH_QKV : PCD_KC_PREFILL_QKV;
+    const int K_O = fu ? PCD_KC_FUSED_O : br ? PCD_KC_BRANCH_O : PCD_KC_PREFILL_O;
+    const int K_GU = fu ? PCD_KC_FUSED_GATEUP : br ? PCD_KC_BRANCH_GATEUP : PCD_KC_PREFILL_GATEUP;
+    const int K_DN = fu ? PCD_KC_FUSED_DOWN : br ? PCD_KC_BRANCH_DOWN : PCD_KC_PREFILL_DOWN;
     const pcd_config &c = m->cfg;
     const int d = c.d_model, hd = c.head_dim, nq = c.n_heads * hd, nk = c.n_kv_heads * hd;
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
@@ -498,7 +501,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
             }
             return PCD_OK;
         };
-        int rc = layer(m, l, n, d_pos, kc, vc, cap, false, attn, st);
+        int rc = layer(m, l, n, d_pos, kc, vc, cap, Pass::Prefill, attn, st);
         if (rc != PCD_OK) return rc;
     }
     HIP_TRY(hipEventRecord(m->ev[4], st));
@@ -835,7 +838,7 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
             a.nsc = d_nsc;
             a.par = d_par;
             a.chain = d_chain;
-            m->tbegin(PCD_KC_BRANCH_ATTN, st);
+            m->tbegin(n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);
             if (!ok) return fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
@@ -850,14 +853,14 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                 t.part_ml = part_ml;
                 t.tok_splits = d_tsp;
                 t.out = ao;
-                m->tbegin(PCD_KC_BRANCH_TAIL, st);
+                m->tbegin(n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_TAIL, st);
                 attention_merge(t, st);
                 m->tend(st);
             }
             return PCD_OK;
         };
-        rc = n_new > 0 ? layer(m, l, M, d_pos, skc, svc, states[0]->cap, true, attn, st, kc, vc, Tb, n_new)
-                       : layer(m, l, M, d_pos, kc, vc, Tb, true, attn, st);
+        rc = n_new > 0 ? layer(m, l, M, d_pos, skc, svc, states[0]->cap, Pass::Fused, attn, st, kc, vc, Tb, n_new)
+                       : layer(m, l, M, d_pos, kc, vc, Tb, Pass::Branch, attn, st);
         if (rc != PCD_OK) return rc;
     }
     HIP_TRY(hipEventRecord(m->ev[1], st));

@@ -296,7 +296,12 @@ int pcd_get_stats(const pcd_model *m, pcd_stats *out);
 #define PCD_KC_BRANCH_DOWN 10
 #define PCD_KC_READOUT_LMHEAD 11 /* LM head with online log-sum-exp and candidate gather */
 #define PCD_KC_OTHER 12          /* embedding, RMSNorm, log-sum-exp merge, combine */
-#define PCD_KC_COUNT 13
+#define PCD_KC_FUSED_QKV 13      /* single-pass mode (pcd_extend_decide): new and branch rows together */
+#define PCD_KC_FUSED_ATTN 14     /* single-pass mode: causal and shared-prefix attention + split merge */
+#define PCD_KC_FUSED_O 15
+#define PCD_KC_FUSED_GATEUP 16
+#define PCD_KC_FUSED_DOWN 17
+#define PCD_KC_COUNT 18
 
 int pcd_set_kernel_timing(pcd_model *m, int32_t enable);
 /* total_ms[PCD_KC_COUNT] and launches[PCD_KC_COUNT], host arrays. */
