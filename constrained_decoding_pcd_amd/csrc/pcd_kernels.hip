@@ -538,18 +538,22 @@ template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
                 return true;
             case Epi::Resid:
                 if (rg == Reg::Small) gemm_resid_cfg<T, 32, 128, 1, 4, 4>(c, st);
-                else if (c.K >= 4096) gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
-                else gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
+                else if (c.K < 4096) gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
+                // 160-row tiles where they need fewer row tiles than 128-row ones
+                // (799 rows: 5 instead of 7, so the split-K grid fits one round)
+                else if (rg == Reg::Big && c.M <= 1024 && (c.M + 159) / 160 < (c.M + 127) / 128)
+                    gemm_resid_cfg<T, 160, 128, 2, 2, 4>(c, st);
+                else gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
                 return true;
             case Epi::SwiGlu: {
-                // the big 128-row tiles only when one round of workgroups covers the product:
-                // a second, mostly idle round costs as much as the first
+                // 128x160 (gate/up pair) when it covers the product in one round of
+                // workgroups and 128x128 does not; 128x128 otherwise, whose second
+                // round is still cheaper per tile than any smaller tile's rounds
                 const int rows = (c.M + 127) / 128;
                 if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
-                else if (rows * (c.N / 128) <= 256) launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
-                else if (c.N % 160 == 0 && rows * (c.N / 160) <= 256)
+                else if (rows * (c.N / 128) > 256 && c.N % 160 == 0 && rows * (c.N / 160) <= 256)
                     launch_gemm<T, 128, 160, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
-                else launch_gemm<T, 64, 64, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
+                else launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
                 return true;
             }
             case Epi::Partial:
