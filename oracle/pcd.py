@@ -13,7 +13,8 @@ Steps, in the order the pages give them ([TechRef] section 4 "The algorithm";
      path, a softmax over the field's candidates at temperature T, and the
      candidate mass.
 
-Combine, written out:
+Combine, written out (the default "path" scoring; plan.py lists the other
+modes and the spelling sets):
   logscore(c) = sum_{i=0}^{u(c)} log p(c[i] | prefix + scaffold + c[<i])
   q           = softmax(logscore / T)           ([TechRef] section 4, stage 4)
   mass        = sum over distinct first tokens t of p(t | prefix + scaffold)
@@ -25,6 +26,8 @@ Combine, written out:
 For single-token candidates, q is the subset softmax of the logits, which
 equals p_S / mass: the full-vocabulary normaliser cancels ([FirstPr], "The
 subset softmax is exact").
+With spelling sets, a label's logscore is log of the sum over its spellings
+of exp(spelling score); q, argmax and margin are taken over labels.
 """
 from __future__ import annotations
 
@@ -34,7 +37,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 from .decoder import Decoder, causal_mask
-from .plan import Plan, build_plan, build_trie
+from .plan import MODES, Plan, build_plan, build_trie, field_mode, field_spellings
 
 
 @dataclasses.dataclass
@@ -98,16 +101,19 @@ def readout(dec: Decoder, plan: Plan, x: np.ndarray):
 
 
 def combine_field(edge_logp: np.ndarray, paths: List[Sequence[int]], root_edges: Sequence[int],
-                  temperature: float = 1.0, labels: Optional[Sequence[int]] = None) -> FieldResult:
-    """Step 5 for one field.  edge_logp[g] = z[g] - lse[readout of g];
-    paths[c] lists the gather indices scored for candidate c; root_edges lists
-    the gathers of the root readout (its distinct first tokens).
+                  temperature: float = 1.0, labels: Optional[Sequence[int]] = None,
+                  mean: bool = False) -> FieldResult:
+    """Step 5 for one field.  edge_logp[g] is the log-probability of gather g
+    under the field's scoring mode; paths[c] lists the gather indices scored
+    for spelling c; root_edges lists the gathers of the root readout (its
+    distinct first tokens), whose probabilities must be full-vocabulary ones.
 
-    ``labels`` (optional) groups candidates that are spellings of one label: a
-    label's probability sums its spellings' path products ([Scratch], "Small
-    models quote their booleans").  With labels given, ``prob``/``logscore``
-    are per label."""
-    ls = np.array([sum(edge_logp[g] for g in p) for p in paths], dtype=np.float64)
+    ``mean``: a spelling's score is the mean of its edge log-probabilities.
+    ``labels`` (optional) groups spellings that write one label: a label's
+    probability sums its spellings' path products ([Scratch], "Small models
+    quote their booleans").  With labels given, ``prob``/``logscore`` are per
+    label."""
+    ls = np.array([sum(edge_logp[g] for g in p) / (len(p) if mean else 1) for p in paths], dtype=np.float64)
     if labels is not None:
         nl = max(labels) + 1
         ls = np.array([np.log(sum(np.exp(ls[c]) for c in range(len(ls)) if labels[c] == k)) for k in range(nl)])
@@ -123,14 +129,30 @@ def combine_field(edge_logp: np.ndarray, paths: List[Sequence[int]], root_edges:
 
 def combine(plan: Plan, lse: np.ndarray, z: np.ndarray, temperature: float = 1.0) -> List[FieldResult]:
     ro_of_g = np.repeat(np.arange(plan.n_readouts), np.diff(plan.g_off))
-    edge_logp = z - lse[ro_of_g]
+    edge_full = z - lse[ro_of_g]
+    # "level": each readout's child logits softmaxed among themselves
+    sub = np.array([Decoder.logsumexp(z[plan.g_off[r]:plan.g_off[r + 1]][None])[0] if plan.g_off[r + 1] > plan.g_off[r]
+                    else 0.0 for r in range(plan.n_readouts)])
+    edge_level = z - sub[ro_of_g]
     out = []
     for f in range(len(plan.f_ro_root)):
+        mode = MODES[plan.f_mode[f]]
         c0, c1 = plan.f_cand_off[f], plan.f_cand_off[f + 1]
-        paths = [plan.c_path[plan.c_path_off[c]:plan.c_path_off[c + 1]] for c in range(c0, c1)]
+        s0, s1 = plan.c_spell_off[c0], plan.c_spell_off[c1]
+        paths = [plan.s_path[plan.s_path_off[k]:plan.s_path_off[k + 1]] for k in range(s0, s1)]
+        labels = [c - c0 for c in range(c0, c1) for _ in range(plan.c_spell_off[c], plan.c_spell_off[c + 1])]
         r = plan.f_ro_root[f]
-        out.append(combine_field(edge_logp, paths, range(plan.g_off[r], plan.g_off[r + 1]), temperature))
+        res = combine_field(edge_level if mode == "level" else edge_full, paths,
+                            range(plan.g_off[r], plan.g_off[r + 1]), temperature, labels, mean=mode == "mean")
+        # mass is a full-vocabulary quantity in every mode
+        res.mass = float(sum(np.exp(edge_full[g]) for g in range(plan.g_off[r], plan.g_off[r + 1])))
+        out.append(res)
     return out
+
+
+def answer_tokens(f, label: int) -> List[int]:
+    """The tokens written for a field's label: its first spelling."""
+    return field_spellings(f)[label][0]
 
 
 def token_by_token_steps(requests, results: List[FieldResult]) -> int:
@@ -140,7 +162,7 @@ def token_by_token_steps(requests, results: List[FieldResult]) -> int:
     n, i = 0, 0
     for _, fields in requests:
         for f in fields:
-            n += len(f.scaffold) + len(f.candidates[results[i].argmax])
+            n += len(f.scaffold) + len(answer_tokens(f, results[i].argmax))
             i += 1
     return n
 
@@ -170,7 +192,7 @@ def decide_sequenced(dec: Decoder, prefix: Sequence[int], fields, n_first: int, 
     first = decide(dec, [(list(prefix), fields[:n_first])], temperature, n_layers=n_layers)
     ext = list(prefix)
     for f, r in zip(fields[:n_first], first.fields):
-        ext += list(f.scaffold) + list(f.candidates[r.argmax])
+        ext += list(f.scaffold) + answer_tokens(f, r.argmax)
     rest = decide(dec, [(ext, fields[n_first:])], temperature, n_layers=n_layers)
     return first, rest, ext
 
@@ -197,9 +219,10 @@ def scratch_readouts(dec: Decoder, requests, n_layers: Optional[int] = None):
     r = 0
     for prefix, fields in requests:
         for f in fields:
-            nodes = build_trie(f.candidates)
+            to_end = field_mode(f) in ("exact", "mean")
+            nodes = build_trie([c for lab in field_spellings(f) for c in lab])
             for i, n in enumerate(nodes):
-                if not (i == 0 or len(n.cands) >= 2):
+                if not (i == 0 or (len(n.children) > 0 if to_end else len(n.cands) >= 2)):
                     continue
                 path = []
                 a = i
@@ -229,18 +252,35 @@ def greedy_first_token(dec: Decoder, prefix, field, n_layers: Optional[int] = No
     return best
 
 
-def enumerate_scores(dec: Decoder, prefix, field, n_layers: Optional[int] = None) -> np.ndarray:
-    """Brute force: each candidate's score as a sum of separately computed
-    from-scratch conditionals log p(c[i] | prefix + scaffold + c[<i]) for
-    i = 0..u(c), with u(c) found by comparing token prefixes directly."""
-    cands = [list(c) for c in field.candidates]
+def enumerate_scores(dec: Decoder, prefix, field, n_layers: Optional[int] = None, mode: Optional[str] = None,
+                     spellings=None) -> np.ndarray:
+    """Brute force, per label: each spelling scored from separately computed
+    from-scratch conditionals log p(c[i] | prefix + scaffold + c[<i]), with no
+    trie: u(c) is found by comparing token prefixes of the spellings directly,
+    and (mode "level") a level's sub-vocabulary is the set of next tokens of
+    the spellings that share c[<i].  A label's score is log of the sum of
+    exp(spelling score) over its spellings."""
+    mode = mode or field_mode(field)
+    labels = spellings if spellings is not None else field_spellings(field)
+    allsp = [list(c) for lab in labels for c in lab]
+    ctx = list(prefix) + list(field.scaffold)
     out = []
-    for c in cands:
-        s = 0.0
-        for i in range(len(c)):
-            s += next_token_logp(dec, list(prefix) + list(field.scaffold) + c[:i], n_layers)[c[i]]
-            shared = any(o[:i + 1] == c[:i + 1] for o in cands if o is not c)
-            if not shared:
-                break
-        out.append(s)
+    for lab in labels:
+        tot = []
+        for c in lab:
+            c = list(c)
+            s = 0.0
+            for i in range(len(c)):
+                lp = next_token_logp(dec, ctx + c[:i], n_layers)
+                if mode == "level":
+                    sibs = sorted({o[i] for o in allsp if len(o) > i and o[:i] == c[:i]})
+                    s += lp[c[i]] - np.log(sum(np.exp(lp[t]) for t in sibs))
+                else:
+                    s += lp[c[i]]
+                if mode in ("path", "level") and not any(o[:i + 1] == c[:i + 1] for o in allsp if o != c):
+                    break
+            if mode == "mean":
+                s /= len(c)
+            tot.append(s)
+        out.append(np.log(sum(np.exp(v) for v in tot)))
     return np.array(out)

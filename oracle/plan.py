@@ -25,11 +25,34 @@ Token positions are those a from-scratch run of prefix + scaffold + path would
 give: P + offset.  Each branch token sees the whole prefix of its request plus
 the branch tokens listed as its ancestors (itself included).
 
+Spellings ([Scratch], "Small models quote their booleans"): a label may be
+written several ways (a bare and a quoted boolean); a label is the set of its
+spellings, and its probability is the sum of its spellings' path products.
+The trie is built over every spelling of every label of the field, inserted
+label by label and, within a label, in the order given; u(c) is taken over
+spellings, so a spelling is followed until no other spelling (of any label)
+shares its tokens.  A field without explicit spellings has one spelling per
+candidate.
+
+Scoring modes (the rules the pages describe for multi-token labels):
+  path  - the default: full-vocabulary log p of c[0..u(c)] summed
+          ([Scratch], "When one token is not enough");
+  exact - every token of the spelling, to its end ([Scratch], same section:
+          scoring a label to the end of its line); each non-leaf trie node is
+          then a readout;
+  level - per level, a softmax over the node's child tokens only, multiplied
+          down to u(c) ([README], "The technique" and "Caveats": confidence
+          as the product of per-level probabilities);
+  mean  - the exact sum divided by the spelling's token count ([FirstPr],
+          "Multi-token candidates": length normalisation).
+
 Validation (a reading of the pages' limits): every field needs a non-empty
 scaffold and 2..255 candidates ([TechRef], "At a glance" and the schema
 checklist); candidates must be non-empty, distinct, and no candidate may be a
 proper prefix of another (with token ids only, the end of a label is unknown,
-so callers end each label with an explicit terminator token).
+so callers end each label with an explicit terminator token).  With
+spellings, the same holds for all spellings of a field taken together, each
+label needs at least one spelling, and a field has at most 1024 spellings.
 """
 from __future__ import annotations
 
@@ -39,6 +62,21 @@ from typing import List, Sequence
 import numpy as np
 
 MAX_CANDIDATES = 255
+MAX_SPELLINGS = 1024
+MODES = ("path", "exact", "level", "mean")
+
+
+def field_spellings(f) -> List[List[List[int]]]:
+    """Per label, its spellings (token lists): the field's ``spellings`` when
+    given, else one spelling per candidate."""
+    sp = getattr(f, "spellings", None)
+    if sp is None:
+        return [[[int(t) for t in c]] for c in f.candidates]
+    return [[[int(t) for t in c] for c in lab] for lab in sp]
+
+
+def field_mode(f) -> str:
+    return getattr(f, "mode", None) or "path"
 
 
 class PlanError(ValueError):
@@ -86,11 +124,19 @@ def build_trie(cands: Sequence[Sequence[int]]) -> List[TrieNode]:
     return out
 
 
-def validate_field(scaffold, cands, vocab_size: int):
+def validate_field(scaffold, labels, vocab_size: int, mode: str = "path"):
+    """labels: per label, its spellings (token lists)."""
+    if mode not in MODES:
+        raise PlanError("ARG", f"unknown scoring mode {mode!r}")
     if len(scaffold) == 0:
         raise PlanError("EMPTY", "empty scaffold")
-    if not (2 <= len(cands) <= MAX_CANDIDATES):
-        raise PlanError("NCAND", f"{len(cands)} candidates (allowed 2..{MAX_CANDIDATES})")
+    if not (2 <= len(labels) <= MAX_CANDIDATES):
+        raise PlanError("NCAND", f"{len(labels)} candidates (allowed 2..{MAX_CANDIDATES})")
+    if any(len(lab) == 0 for lab in labels):
+        raise PlanError("EMPTY", "a label without spellings")
+    cands = [c for lab in labels for c in lab]
+    if len(cands) > MAX_SPELLINGS:
+        raise PlanError("NCAND", f"{len(cands)} spellings (allowed up to {MAX_SPELLINGS})")
     for t in list(scaffold) + [t for c in cands for t in c]:
         if not (0 <= int(t) < vocab_size):
             raise PlanError("TOKEN", f"token id {t} outside [0, {vocab_size})")
@@ -122,9 +168,11 @@ class Plan:
     g_off: np.ndarray      # [R+1]
     g_tok: np.ndarray      # [G] child token ids gathered at each readout
     f_ro_root: np.ndarray  # [F] readout index of each field's root
-    f_cand_off: np.ndarray  # [F+1] candidate range of each field (global candidate index)
-    c_path_off: np.ndarray  # [C+1]
-    c_path: np.ndarray     # gather indices scored for each candidate, depth order
+    f_cand_off: np.ndarray  # [F+1] candidate (label) range of each field (global candidate index)
+    f_mode: np.ndarray     # [F] scoring mode, an index into MODES
+    c_spell_off: np.ndarray  # [C+1] spelling range of each candidate
+    s_path_off: np.ndarray  # [S+1]
+    s_path: np.ndarray     # gather indices scored for each spelling, depth order
     n_requests: int
 
     @property
@@ -142,30 +190,36 @@ class Plan:
     def arrays(self):
         return {k: getattr(self, k) for k in (
             "tok", "pos", "req", "tfield", "anc_off", "anc", "ro_tok", "ro_field", "g_off", "g_tok",
-            "f_ro_root", "f_cand_off", "c_path_off", "c_path")}
+            "f_ro_root", "f_cand_off", "f_mode", "c_spell_off", "s_path_off", "s_path")}
 
 
 def build_plan(requests, vocab_size: int) -> Plan:
     """requests: list of (prefix_len, fields) with fields a list of objects
-    carrying ``scaffold`` and ``candidates``."""
+    carrying ``scaffold`` and ``candidates`` (and optionally ``spellings``,
+    per label a list of token lists, and ``mode``, one of MODES)."""
     tok, pos, req, tfield, anc_off, anc = [], [], [], [], [0], []
     ro_tok, ro_field, g_off, g_tok = [], [], [0], []
-    f_ro_root, f_cand_off, c_path_off, c_path = [], [0], [0], []
+    f_ro_root, f_cand_off, f_mode, c_spell_off, s_path_off, s_path = [], [0], [], [0], [0], []
     gf = 0
     for r, (P, fields) in enumerate(requests):
         for f in fields:
             sc = [int(t) for t in f.scaffold]
-            cands = [[int(t) for t in c] for c in f.candidates]
-            validate_field(sc, cands, vocab_size)
-            nodes = build_trie(cands)
+            labels = field_spellings(f)
+            mode = field_mode(f)
+            validate_field(sc, labels, vocab_size, mode)
+            spells = [c for lab in labels for c in lab]
+            to_end = mode in ("exact", "mean")
+            nodes = build_trie(spells)
             base = len(tok)
             # scaffold tokens
             for j, t in enumerate(sc):
                 tok.append(t); pos.append(P + j); req.append(r); tfield.append(gf)
                 anc.extend(range(base, base + j + 1)); anc_off.append(len(anc))
             last_scaffold = base + len(sc) - 1
-            # non-root readout nodes, BFS order
-            is_ro = [i == 0 or len(n.cands) >= 2 for i, n in enumerate(nodes)]
+            # non-root readout nodes, BFS order: nodes the labels still share, or
+            # (scoring to the end) every node some spelling continues from
+            is_ro = [i == 0 or (len(n.children) > 0 if to_end else len(n.cands) >= 2)
+                     for i, n in enumerate(nodes)]
             branch_of = {0: last_scaffold}
             for i, n in enumerate(nodes):
                 if i == 0 or not is_ro[i]:
@@ -192,19 +246,22 @@ def build_plan(requests, vocab_size: int) -> Plan:
                     gidx[(i, nodes[ch].token)] = len(g_tok)
                     g_tok.append(nodes[ch].token)
                 g_off.append(len(g_tok))
-            # candidate paths: edges c[0..u(c)]
-            for c in cands:
-                cur = 0
-                for t in c:
-                    c_path.append(gidx[(cur, t)])
-                    nxt = [ch for ch in nodes[cur].children if nodes[ch].token == t][0]
-                    if len(nodes[nxt].cands) == 1:
-                        break
-                    cur = nxt
-                c_path_off.append(len(c_path))
-            f_cand_off.append(f_cand_off[-1] + len(cands))
+            # spelling paths: edges c[0..u(c)], or every edge when scoring to the end
+            for lab in labels:
+                for c in lab:
+                    cur = 0
+                    for t in c:
+                        s_path.append(gidx[(cur, t)])
+                        nxt = [ch for ch in nodes[cur].children if nodes[ch].token == t][0]
+                        if len(nodes[nxt].cands) == 1 and not to_end:
+                            break
+                        cur = nxt
+                    s_path_off.append(len(s_path))
+                c_spell_off.append(c_spell_off[-1] + len(lab))
+            f_cand_off.append(f_cand_off[-1] + len(labels))
+            f_mode.append(MODES.index(mode))
             gf += 1
     i32 = lambda a: np.asarray(a, dtype=np.int32)
     return Plan(i32(tok), i32(pos), i32(req), i32(tfield), i32(anc_off), i32(anc), i32(ro_tok), i32(ro_field),
-                i32(g_off), i32(g_tok), i32(f_ro_root), i32(f_cand_off), i32(c_path_off), i32(c_path),
-                len(requests))
+                i32(g_off), i32(g_tok), i32(f_ro_root), i32(f_cand_off), i32(f_mode), i32(c_spell_off),
+                i32(s_path_off), i32(s_path), len(requests))

@@ -184,9 +184,15 @@ def make_weights(shape: ModelShape, seed: int, n_layers: Optional[int] = None) -
 
 @dataclasses.dataclass
 class Field:
+    """One field of a request.  ``candidates`` holds one token list per label;
+    ``spellings``, when given, holds per label every way of writing it (its
+    first spelling is the candidate itself); ``mode`` names the scoring rule:
+    "path", "exact", "level" or "mean"."""
     scaffold: List[int]
     candidates: List[List[int]]
     kind: str = "enum"
+    spellings: Optional[List[List[List[int]]]] = None
+    mode: str = "path"
 
 
 @dataclasses.dataclass
@@ -335,3 +341,40 @@ def random_trie_fields(seed: int, V: int, n_fields: int, max_cands: int = 12, ma
             cands = [[alphabet[0]], [alphabet[1]]]
         out.append(Field(sc, cands, kind="trie"))
     return out
+
+
+def random_spelling_fields(seed: int, V: int, n_fields: int, max_labels: int = 5, max_spellings: int = 3,
+                           max_len: int = 3, scaffold_len=(1, 6), small_alphabet: int = 5,
+                           mode: str = "path") -> List[Field]:
+    """Random fields whose labels each have 1..max_spellings spellings over a
+    small alphabet (so spellings of different labels share prefixes, as a
+    quoted and a bare boolean share the quote).  No two spellings of a field
+    are equal, and none is a proper prefix of another."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    alphabet = _distinct(rng, V, small_alphabet)
+    out = []
+    for _ in range(n_fields):
+        sc = _scaffold(rng, V, *scaffold_len)
+        k = int(rng.integers(2, max_labels + 1))
+        used: List[List[int]] = []
+        labels: List[List[List[int]]] = []
+        tries = 0
+        while len(labels) < k and tries < 2000:
+            tries += 1
+            want = int(rng.integers(1, max_spellings + 1))
+            lab: List[List[int]] = []
+            for _ in range(50):
+                if len(lab) == want:
+                    break
+                L = int(rng.integers(1, max_len + 1))
+                c = [alphabet[int(i)] for i in rng.integers(0, small_alphabet, size=L)]
+                if not any(c == o or c[:len(o)] == o or o[:len(c)] == c for o in used + lab):
+                    lab.append(c)
+            if lab:
+                labels.append(lab)
+                used += lab
+        if len(labels) < 2:
+            labels = [[[alphabet[0]]], [[alphabet[1]]]]
+        out.append(Field(sc, [lab[0] for lab in labels], kind="spellings", spellings=labels, mode=mode))
+    return out
+

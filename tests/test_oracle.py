@@ -84,7 +84,7 @@ def test_quoted_boolean_path_products():
     for r in range(plan.n_readouts):
         for gi in range(plan.g_off[r], plan.g_off[r + 1]):
             edge[gi] = math.log(p_of[r][int(plan.g_tok[gi])])
-    paths = [plan.c_path[plan.c_path_off[c]:plan.c_path_off[c + 1]] for c in range(4)]
+    paths = [plan.s_path[plan.s_path_off[c]:plan.s_path_off[c + 1]] for c in range(4)]
     root = range(plan.g_off[0], plan.g_off[1])
     res = opcd.combine_field(edge, paths, root, 1.0, labels=[0, 1, 1, 0])
     pr = g["printed"]
@@ -94,6 +94,32 @@ def test_quoted_boolean_path_products():
     assert abs(math.exp(res.logscore[1]) - pr["quoted_false_plus_bare"]) < tol
     assert abs(res.prob[0] - pr["True_renormalised"]) < tol
     assert res.argmax == 0
+
+
+def test_quoted_boolean_spelling_sets():
+    """The same worked numbers through the plan of a field whose two labels
+    are each a set of spellings (bare, quoted): True 0.812 against 0.137,
+    renormalised 0.855; the exact value of the printed rounding is
+    0.811424 / 0.948656."""
+    g = _golden("quoted_boolean_paths.json")
+    Q, BF, BT, T, F = 100, 101, 102, 103, 104
+    field = pi.Field([7, 8], [[BT], [BF]], spellings=[[[BT], [Q, T]], [[BF], [Q, F]]])
+    plan = oplan.build_plan([(20, [field])], 256)
+    assert plan.n_readouts == 2 and list(plan.c_spell_off) == [0, 2, 4]
+    p_of = {0: {Q: g["root"]["quote"], BF: g["root"]["false"], BT: g["root"]["true"]},
+            1: {T: g["after_quote"]["true"], F: g["after_quote"]["false"]}}
+    # logits equal to log p and a zero log-sum-exp make every edge exactly log p
+    z = np.array([math.log(p_of[r][int(plan.g_tok[gi])]) for r in range(plan.n_readouts)
+                  for gi in range(plan.g_off[r], plan.g_off[r + 1])])
+    res = opcd.combine(plan, np.zeros(plan.n_readouts), z)[0]
+    pr, tol = g["printed"], g["printed_abs_tolerance"]
+    assert abs(math.exp(res.logscore[0]) - pr["True_total"]) < tol
+    assert abs(math.exp(res.logscore[1]) - pr["quoted_false_plus_bare"]) < tol
+    assert abs(res.prob[0] - pr["True_renormalised"]) < tol
+    t = 0.868 * 0.868 + 0.058
+    f = 0.073 + 0.868 * 0.074
+    assert abs(res.prob[0] - t / (t + f)) < 1e-12 and res.argmax == 0
+    assert abs(res.mass - (0.868 + 0.073 + 0.058)) < 1e-12
 
 
 def test_kv_pile_size():
@@ -225,6 +251,74 @@ def test_trie_scores_equal_enumeration(tiny, cfg0t):
         assert np.max(np.abs(fr.logscore - ref)) < 1e-10
 
 
+@pytest.mark.parametrize("mode", ["path", "exact", "level", "mean"])
+def test_spelling_scores_equal_enumeration(tiny, mode):
+    """Labels with several spellings sharing prefixes, under each scoring
+    mode: every label's score equals the brute-force enumeration (from-scratch
+    conditionals per spelling, no trie), and the cached pass equals
+    from-scratch runs at every readout node of the mode's trie."""
+    V = tiny.sh.vocab_size
+    prefix = [int(t) for t in np.random.default_rng(5).integers(0, V, size=21)]
+    fields = pi.random_spelling_fields(71, V, 4, mode=mode)
+    assert any(len(lab) > 1 for f in fields for lab in f.spellings)
+    res = opcd.decide(tiny, [(prefix, fields)])
+    for f, fr in zip(fields, res.fields):
+        assert np.max(np.abs(fr.logscore - opcd.enumerate_scores(tiny, prefix, f))) < 1e-10
+        assert abs(fr.prob.sum() - 1.0) < 1e-12 and 0.0 < fr.mass <= 1.0
+    plan, edge, lse = opcd.scratch_readouts(tiny, [(prefix, fields)])
+    ro_of_g = np.repeat(np.arange(res.plan.n_readouts), np.diff(res.plan.g_off))
+    assert np.max(np.abs(res.lse - lse)) < 1e-10
+    assert np.max(np.abs((res.z - res.lse[ro_of_g]) - edge)) < 1e-10
+
+
+def test_level_mode_is_a_distribution(tiny):
+    """Per-level probabilities multiplied down a trie: every level's child
+    probabilities sum to one, so the label probabilities exp(logscore) sum to
+    one before any renormalisation, and q equals them at T = 1."""
+    V = tiny.sh.vocab_size
+    prefix = [int(t) for t in np.random.default_rng(6).integers(0, V, size=15)]
+    fields = pi.random_trie_fields(41, V, 4, max_cands=7, max_len=3)
+    for f in fields:
+        f.mode = "level"
+    res = opcd.decide(tiny, [(prefix, fields)])
+    for fr in res.fields:
+        assert abs(np.exp(fr.logscore).sum() - 1.0) < 1e-12
+        assert np.max(np.abs(fr.prob - np.exp(fr.logscore))) < 1e-12
+
+
+def test_modes_on_single_token_labels(tiny, cfg0):
+    """With one token per label, scoring to the end is the path rule, the mean
+    divides by one, and the per-level softmax is the subset softmax: every
+    mode gives the same q."""
+    prefix, fields = _reqs(cfg0)[0]
+    base = opcd.decide(tiny, [(prefix, fields)])
+    for mode in ("exact", "mean", "level"):
+        fm = [pi.Field(f.scaffold, f.candidates, mode=mode) for f in fields]
+        res = opcd.decide(tiny, [(prefix, fm)])
+        assert res.plan.n_readouts == base.plan.n_readouts
+        for a, b in zip(res.fields, base.fields):
+            assert np.max(np.abs(a.prob - b.prob)) < 1e-12 and a.argmax == b.argmax
+            if mode != "level":
+                assert np.max(np.abs(a.logscore - b.logscore)) < 1e-12
+
+
+def test_exact_mode_scores_every_token(tiny, cfg0t):
+    """Exact scoring reads out at every node a label continues from: the
+    tiny-trie field's six 3-token IDs get a readout at the lead token and at
+    both second-level nodes (the path rule already does), and each label's
+    score sums three conditionals; the mean divides it by three."""
+    prefix, fields = _reqs(cfg0t)[0]
+    f = fields[-1]
+    assert all(len(c) == 3 for c in f.candidates)
+    ex = opcd.decide(tiny, [(prefix, [pi.Field(f.scaffold, f.candidates, mode="exact")])])
+    mn = opcd.decide(tiny, [(prefix, [pi.Field(f.scaffold, f.candidates, mode="mean")])])
+    assert np.all(np.diff(ex.plan.s_path_off) == 3)
+    assert np.max(np.abs(ex.fields[0].logscore - 3 * mn.fields[0].logscore)) < 1e-12
+    ref = [sum(opcd.next_token_logp(tiny, list(prefix) + list(f.scaffold) + c[:i])[c[i]] for i in range(3))
+           for c in f.candidates]
+    assert np.max(np.abs(ex.fields[0].logscore - np.array(ref))) < 1e-10
+
+
 def test_sequenced_rest_sees_the_answers(tiny, cfg0t):
     """The first-field round: the remaining fields' scores equal from-scratch
     conditionals after prefix + the first field's scaffold and chosen
@@ -354,6 +448,11 @@ def test_plan_positions_and_ancestors_bruteforce():
     (pi.Field([3], [[1], [1, 2]]), "PREFIX"),
     (pi.Field([3], [[1], [5000]]), "TOKEN"),
     (pi.Field([-1], [[1], [2]]), "TOKEN"),
+    (pi.Field([3], [[1], [2]], mode="greedy"), "ARG"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1]], []]), "EMPTY"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1], [7, 2]], [[2], [7, 2]]]), "DUP"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1], [7]], [[2], [7, 2]]]), "PREFIX"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1]], [[2]] + [[9, i] for i in range(1023)]]), "NCAND"),
 ])
 def test_plan_rejects(bad, code):
     with pytest.raises(oplan.PlanError) as e:
@@ -418,11 +517,45 @@ def test_planted_separation_point_is_caught(monkeypatch, tiny, cfg0t):
     brute-force enumeration pin."""
     orig = opcd.combine_field
 
-    def bad(edge_logp, paths, root_edges, temperature=1.0, labels=None):
-        return orig(edge_logp, [p[:max(1, len(p) - 1)] for p in paths], root_edges, temperature, labels)
+    def bad(edge_logp, paths, root_edges, temperature=1.0, labels=None, mean=False):
+        return orig(edge_logp, [p[:max(1, len(p) - 1)] for p in paths], root_edges, temperature, labels, mean)
     monkeypatch.setattr(opcd, "combine_field", bad)
     reqs = _reqs(cfg0t)
     res = opcd.decide(tiny, reqs)
     prefix, fields = reqs[0]
     f, fr = fields[-1], res.fields[-1]
     assert np.max(np.abs(fr.logscore - opcd.enumerate_scores(tiny, prefix, f))) > 1e-6
+
+
+def test_planted_spelling_max_is_caught(monkeypatch):
+    """Taking a label's best spelling instead of the sum of its spellings
+    breaks the quoted-boolean worked numbers."""
+    orig = opcd.combine_field
+
+    def bad(edge_logp, paths, root_edges, temperature=1.0, labels=None, mean=False):
+        if labels is None:
+            return orig(edge_logp, paths, root_edges, temperature, None, mean)
+        best = {}
+        for c, k in enumerate(labels):
+            sc = sum(edge_logp[g] for g in paths[c])
+            if k not in best or sc > best[k][0]:
+                best[k] = (sc, c)
+        keep = sorted(c for _, c in best.values())
+        return orig(edge_logp, [paths[c] for c in keep], root_edges, temperature, None, mean)
+    monkeypatch.setattr(opcd, "combine_field", bad)
+    with pytest.raises(AssertionError):
+        test_quoted_boolean_spelling_sets()
+
+
+def test_planted_level_normaliser_is_caught(monkeypatch, tiny):
+    """Normalising a level over the full vocabulary instead of its child
+    tokens breaks the level-mode distribution pin."""
+    orig = opcd.combine
+
+    def bad(plan, lse, z, temperature=1.0):
+        plan.f_mode = np.zeros_like(plan.f_mode)
+        return orig(plan, lse, z, temperature)
+    monkeypatch.setattr(opcd, "combine", bad)
+    with pytest.raises(AssertionError):
+        test_level_mode_is_a_distribution(tiny)
+
