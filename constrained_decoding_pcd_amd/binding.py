@@ -57,16 +57,21 @@ class pcd_weights(ctypes.Structure):
 class pcd_limits(ctypes.Structure):
     _fields_ = [("max_prefill_tokens", c_int32), ("max_branch_tokens", c_int32), ("max_readouts", c_int32),
                 ("max_gathers", c_int32), ("max_fields", c_int32), ("max_candidates", c_int32),
-                ("max_requests", c_int32)]
+                ("max_requests", c_int32), ("max_spellings", c_int32)]
 
 
 class pcd_candidate(ctypes.Structure):
-    _fields_ = [("tokens", POINTER(c_int32)), ("n_tokens", c_int32)]
+    _fields_ = [("tokens", POINTER(c_int32)), ("n_tokens", c_int32), ("spell_len", POINTER(c_int32)),
+                ("n_spellings", c_int32)]
 
 
 class pcd_field(ctypes.Structure):
     _fields_ = [("scaffold", POINTER(c_int32)), ("n_scaffold", c_int32), ("cand_offset", c_int32),
-                ("n_cands", c_int32)]
+                ("n_cands", c_int32), ("score_mode", c_int32)]
+
+
+# PCD_SCORE_* by name
+SCORE_MODES = {"path": 0, "exact": 1, "level": 2, "mean": 3}
 
 
 class pcd_request(ctypes.Structure):
@@ -89,12 +94,13 @@ class pcd_stats(ctypes.Structure):
 
 
 _PLAN_ARRAYS = ("tok", "pos", "req", "field", "anc_off", "anc", "ro_tok", "ro_field", "g_off", "g_tok",
-                "f_ro_root", "f_cand_off", "c_path_off", "c_path")
+                "f_ro_root", "f_cand_off", "f_mode", "c_spell_off", "s_path_off", "s_path")
 
 
 class pcd_plan_info(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("n_branch", "n_readouts", "n_gathers", "n_fields", "n_candidates",
-                                        "n_paths", "n_anc")] + [(n, POINTER(c_int32)) for n in _PLAN_ARRAYS]
+                                        "n_paths", "n_anc", "n_spellings")] + \
+               [(n, POINTER(c_int32)) for n in _PLAN_ARRAYS]
 
 
 _lib = None
@@ -164,12 +170,23 @@ class _Marshalled:
         self.reqs = (pcd_request * len(requests))()
         self.n_cands, self.n_fields = [], []
         for r, fields in enumerate(requests):
-            cands = [c for f in fields for c in f.candidates]
-            ca = (pcd_candidate * max(1, len(cands)))()
+            # per label: None (one spelling: the candidate) or its list of spellings
+            labels = []
+            for f in fields:
+                sp = getattr(f, "spellings", None)
+                labels += [(c, None if sp is None else sp[k]) for k, c in enumerate(f.candidates)]
+            ca = (pcd_candidate * max(1, len(labels)))()
             fa = (pcd_field * max(1, len(fields)))()
             off = 0
-            for i, c in enumerate(cands):
-                a = np.ascontiguousarray(c, dtype=np.int32)
+            for i, (c, spell) in enumerate(labels):
+                if spell is None:
+                    a = np.ascontiguousarray(c, dtype=np.int32)
+                else:
+                    a = np.ascontiguousarray([t for x in spell for t in x], dtype=np.int32)
+                    ln = np.ascontiguousarray([len(x) for x in spell], dtype=np.int32)
+                    self.keep.append(ln)
+                    ca[i].spell_len = _i32p(ln)
+                    ca[i].n_spellings = ln.size
                 self.keep.append(a)
                 ca[i].tokens = _i32p(a)
                 ca[i].n_tokens = a.size
@@ -180,13 +197,15 @@ class _Marshalled:
                 fa[i].n_scaffold = s.size
                 fa[i].cand_offset = off
                 fa[i].n_cands = len(f.candidates)
+                mode = getattr(f, "mode", None) or "path"
+                fa[i].score_mode = SCORE_MODES.get(mode, -1)
                 off += len(f.candidates)
             self.keep += [ca, fa]
             self.reqs[r].fields = fa
             self.reqs[r].n_fields = len(fields)
             self.reqs[r].candidates = ca
-            self.reqs[r].n_candidates = len(cands)
-            self.n_cands.append(len(cands))
+            self.reqs[r].n_candidates = len(labels)
+            self.n_cands.append(len(labels))
             self.n_fields.append(len(fields))
 
 
@@ -200,8 +219,8 @@ def debug_plan(vocab_size: int, max_seq: int, prefix_lens: Sequence[int], reques
     sizes = {"tok": info.n_branch, "pos": info.n_branch, "req": info.n_branch, "field": info.n_branch,
              "anc_off": info.n_branch + 1, "anc": info.n_anc, "ro_tok": info.n_readouts,
              "ro_field": info.n_readouts, "g_off": info.n_readouts + 1, "g_tok": info.n_gathers,
-             "f_ro_root": info.n_fields, "f_cand_off": info.n_fields + 1, "c_path_off": info.n_candidates + 1,
-             "c_path": info.n_paths}
+             "f_ro_root": info.n_fields, "f_cand_off": info.n_fields + 1, "f_mode": info.n_fields,
+             "c_spell_off": info.n_candidates + 1, "s_path_off": info.n_spellings + 1, "s_path": info.n_paths}
     out = {k: np.zeros(max(1, n), np.int32) for k, n in sizes.items()}
     for k in _PLAN_ARRAYS:
         setattr(info, k, _i32p(out[k]))
@@ -223,7 +242,8 @@ def limits_for(vocab_size: int, max_seq: int, prefix_lens: Sequence[int], reques
     p = debug_plan(vocab_size, max_seq, prefix_lens, requests)
     return dict(max_prefill_tokens=max(max_prefill, max(prefix_lens)), max_branch_tokens=len(p["tok"]),
                 max_readouts=len(p["ro_tok"]), max_gathers=len(p["g_tok"]), max_fields=len(p["f_ro_root"]),
-                max_candidates=len(p["c_path_off"]) - 1, max_requests=len(prefix_lens))
+                max_candidates=len(p["c_spell_off"]) - 1, max_requests=len(prefix_lens),
+                max_spellings=len(p["s_path_off"]) - 1)
 
 
 def _stream_handle(torch):

@@ -63,7 +63,13 @@ int64_t plan_block_cap(const pcd_config &c, const pcd_limits &l) {
     return pre + br;  // a fused pass has both kinds of blocks
 }
 
-int64_t path_cap(const pcd_limits &l) { return 8 * (int64_t)l.max_candidates + l.max_gathers; }
+// spellings of one decide call: the limit, or one per candidate when unset
+static_assert(SCORE_PATH == PCD_SCORE_PATH && SCORE_EXACT == PCD_SCORE_EXACT && SCORE_LEVEL == PCD_SCORE_LEVEL &&
+                  SCORE_MEAN == PCD_SCORE_MEAN,
+              "kernel scoring-mode values");
+
+int64_t spell_cap(const pcd_limits &l) { return l.max_spellings > 0 ? l.max_spellings : l.max_candidates; }
+int64_t path_cap(const pcd_limits &l) { return 8 * spell_cap(l) + l.max_gathers; }
 
 // partial sums of the residual GEMMs: up to SPLITK_MAX splits below
 // SPLITK_ROWS rows, one above
@@ -100,9 +106,9 @@ Layout layout(const pcd_config &c, const pcd_limits &l) {
     L.outs_bytes = align_up((size_t)(2 * l.max_candidates + 3 * l.max_fields + l.max_readouts + l.max_gathers) * 4 + 8 * 256);
     L.outs = take(L.outs_bytes);
     const int64_t ints = 8 * (int64_t)rows + 8 * (int64_t)l.max_branch_tokens + 2 * (int64_t)l.max_readouts + 2 + 2 * (int64_t)l.max_gathers +
-                         2 * (int64_t)l.max_fields + 1 + (int64_t)l.max_candidates + 1 + path_cap(l) +
+                         3 * (int64_t)l.max_fields + 1 + (int64_t)l.max_candidates + 1 + spell_cap(l) + 1 + path_cap(l) +
                          2 * (int64_t)l.max_requests;
-    L.plan_bytes = align_up((size_t)ints * 4 + 20 * 256) + align_up((size_t)l.max_requests * 8) +
+    L.plan_bytes = align_up((size_t)ints * 4 + 32 * 256) + align_up((size_t)l.max_requests * 8) +
                    align_up((size_t)plan_block_cap(c, l) * sizeof(AttnBlock));
     L.plan = take(L.plan_bytes);
     L.total = off;
@@ -124,7 +130,7 @@ int check_config(const pcd_config *c, const pcd_limits *l) {
         return fail(PCD_E_ARG, "d_model, ffn_dim, n_heads*head_dim and vocab_size must be multiples of 128");
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(PCD_E_ARG, "rms_eps and rope_theta must be positive");
     if (l->max_prefill_tokens <= 0 || l->max_branch_tokens <= 0 || l->max_readouts <= 0 || l->max_gathers <= 0 ||
-        l->max_fields <= 0 || l->max_candidates <= 0 || l->max_requests <= 0)
+        l->max_fields <= 0 || l->max_candidates <= 0 || l->max_requests <= 0 || l->max_spellings < 0)
         return fail(PCD_E_ARG, "limits must be positive");
     if (l->max_prefill_tokens > c->max_seq) return fail(PCD_E_ARG, "max_prefill_tokens exceeds max_seq");
     return PCD_OK;
@@ -604,8 +610,9 @@ int pcd_debug_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *pre
     info->n_readouts = (int32_t)p.ro_tok.size();
     info->n_gathers = (int32_t)p.g_tok.size();
     info->n_fields = (int32_t)p.f_ro_root.size();
-    info->n_candidates = (int32_t)p.c_path_off.size() - 1;
-    info->n_paths = (int32_t)p.c_path.size();
+    info->n_candidates = (int32_t)p.c_spell_off.size() - 1;
+    info->n_spellings = (int32_t)p.s_path_off.size() - 1;
+    info->n_paths = (int32_t)p.s_path.size();
     info->n_anc = (int32_t)p.anc.size();
     auto cp = [](int32_t *dst, const std::vector<int32_t> &v) {
         if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * 4);
@@ -622,8 +629,10 @@ int pcd_debug_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *pre
     cp(info->g_tok, p.g_tok);
     cp(info->f_ro_root, p.f_ro_root);
     cp(info->f_cand_off, p.f_cand_off);
-    cp(info->c_path_off, p.c_path_off);
-    cp(info->c_path, p.c_path);
+    cp(info->f_mode, p.f_mode);
+    cp(info->c_spell_off, p.c_spell_off);
+    cp(info->s_path_off, p.s_path_off);
+    cp(info->s_path, p.s_path);
     return PCD_OK;
 }
 
@@ -670,9 +679,10 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
     int rc = build_plan(c.vocab_size, c.max_seq, n_req, lens.data(), reqs, p, err);
     if (rc != PCD_OK) return fail(rc, err);
     const int Tb = (int)p.tok.size(), R = (int)p.ro_tok.size(), G = (int)p.g_tok.size();
-    const int F = (int)p.f_ro_root.size(), C = (int)p.c_path_off.size() - 1, NP = (int)p.c_path.size();
+    const int F = (int)p.f_ro_root.size(), C = (int)p.c_spell_off.size() - 1, S = (int)p.s_path_off.size() - 1;
+    const int NP = (int)p.s_path.size();
     if (Tb > lim.max_branch_tokens || R > lim.max_readouts || G > lim.max_gathers || F > lim.max_fields ||
-        C > lim.max_candidates || NP > path_cap(lim))
+        C > lim.max_candidates || S > spell_cap(lim) || NP > path_cap(lim))
         return fail(PCD_E_CAP, "decide call of " + std::to_string(Tb) + " branch tokens, " + std::to_string(R) +
                                    " readouts, " + std::to_string(G) + " gathers exceeds the model's limits");
     const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim, d = c.d_model;
@@ -772,8 +782,10 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
     const int32_t *d_gro = pk.put(p.g_ro.data(), G);
     const int32_t *d_froot = pk.put(p.f_ro_root.data(), F);
     const int32_t *d_fcand = pk.put(p.f_cand_off.data(), F + 1);
-    const int32_t *d_cpo = pk.put(p.c_path_off.data(), C + 1);
-    const int32_t *d_cp = pk.put(p.c_path.data(), NP);
+    const int32_t *d_fmode = pk.put(p.f_mode.data(), F);
+    const int32_t *d_cso = pk.put(p.c_spell_off.data(), C + 1);
+    const int32_t *d_spo = pk.put(p.s_path_off.data(), S + 1);
+    const int32_t *d_sp = pk.put(p.s_path.data(), NP);
     std::vector<int32_t> strides(n_req);
     for (int r = 0; r < n_req; ++r) strides[r] = states[r]->cap;
     const int32_t *d_stride = pk.put(strides.data(), n_req);
@@ -894,8 +906,10 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
     cc.n_fields = F;
     cc.f_cand_off = d_fcand;
     cc.f_ro_root = d_froot;
-    cc.c_path_off = d_cpo;
-    cc.c_path = d_cp;
+    cc.f_mode = d_fmode;
+    cc.c_spell_off = d_cso;
+    cc.s_path_off = d_spo;
+    cc.s_path = d_sp;
     cc.g_off = d_goff;
     cc.g_ro = d_gro;
     cc.z = z;
@@ -985,6 +999,11 @@ int pcd_decide_sequenced(pcd_state *s, const pcd_field *fields, int32_t n_fields
     if (!out->cand_prob || !out->field_mass || !out->field_margin || !out->field_argmax)
         return fail(PCD_E_ARG, "null output array");
     pcd_model *m = s->m;
+    // the tokens written for a label: its first spelling (the whole candidate without spellings)
+    auto answer_len = [](const pcd_candidate &cd) {
+        const int n = (cd.spell_len && cd.n_spellings > 0) ? cd.spell_len[0] : cd.n_tokens;
+        return std::max(0, std::min(n, cd.n_tokens));
+    };
     // Longest possible answer of the first fields: each scaffold plus its longest candidate.
     int64_t ans_max = 0, c1 = 0;
     for (int f = 0; f < n_first; ++f) {
@@ -992,7 +1011,7 @@ int pcd_decide_sequenced(pcd_state *s, const pcd_field *fields, int32_t n_fields
         if (fd.cand_offset < 0 || fd.n_cands < 0 || (int64_t)fd.cand_offset + fd.n_cands > n_candidates || !candidates)
             return fail(PCD_E_ARG, "field " + std::to_string(f) + ": candidates outside the candidate array");
         int lmax = 0;
-        for (int k = 0; k < fd.n_cands; ++k) lmax = std::max(lmax, candidates[fd.cand_offset + k].n_tokens);
+        for (int k = 0; k < fd.n_cands; ++k) lmax = std::max(lmax, answer_len(candidates[fd.cand_offset + k]));
         ans_max += std::max(0, fd.n_scaffold) + lmax;
         c1 += fd.n_cands;
     }
@@ -1021,7 +1040,7 @@ int pcd_decide_sequenced(pcd_state *s, const pcd_field *fields, int32_t n_fields
         const pcd_field &fd = fields[f];
         ans.insert(ans.end(), fd.scaffold, fd.scaffold + fd.n_scaffold);
         const pcd_candidate &cd = candidates[fd.cand_offset + out->field_argmax[f]];
-        ans.insert(ans.end(), cd.tokens, cd.tokens + cd.n_tokens);
+        ans.insert(ans.end(), cd.tokens, cd.tokens + answer_len(cd));
     }
     rc = pcd_extend(s, ans.data(), (int32_t)ans.size(), stream);
     if (rc != PCD_OK) return rc;

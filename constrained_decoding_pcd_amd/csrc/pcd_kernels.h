@@ -116,10 +116,13 @@ void attention_merge(const TailCall &c, hipStream_t st);
 // lse[r] from the per-tile partials of the readout GEMM.
 void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hipStream_t st);
 
+// Scoring modes of a field in CombineCall::f_mode (the public PCD_SCORE_* values).
+constexpr int SCORE_PATH = 0, SCORE_EXACT = 1, SCORE_LEVEL = 2, SCORE_MEAN = 3;
+
 // Per field: logscore, softmax(logscore / T), mass, argmax, margin.
 struct CombineCall {
     int32_t n_fields;
-    const int32_t *f_cand_off, *f_ro_root, *c_path_off, *c_path, *g_off, *g_ro;
+    const int32_t *f_cand_off, *f_ro_root, *f_mode, *c_spell_off, *s_path_off, *s_path, *g_off, *g_ro;
     const float *z, *lse;
     float temperature;
     float *prob, *logscore, *mass, *margin;

@@ -1382,23 +1382,47 @@ void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hip
     hipLaunchKernelGGL(k_readout_lse, dim3(R), dim3(256), 0, st, part, n_tiles, R, lse);
 }
 
+// One thread per field.  A spelling's score sums the log-probabilities of the
+// edges on its path: z - lse (full vocabulary), or in SCORE_LEVEL z minus
+// the log-sum-exp of its readout's gathered child logits; SCORE_MEAN
+// divides the sum by the path length.  A label's score is the log-sum-exp of
+// its spellings' scores.  The scores are written to c.logscore first and read
+// back from there (same thread).
 __global__ void k_combine(CombineCall c) {
     const int f = blockIdx.x * blockDim.x + threadIdx.x;
     if (f >= c.n_fields) return;
     const int c0 = c.f_cand_off[f], c1 = c.f_cand_off[f + 1];
-    auto score = [&](int k) {
+    const int mode = c.f_mode[f];
+    auto norm = [&](int r) {
+        if (mode != SCORE_LEVEL) return c.lse[r];
+        float mx = -INFINITY;
+        for (int gi = c.g_off[r]; gi < c.g_off[r + 1]; ++gi) mx = fmaxf(mx, c.z[gi]);
+        float sum = 0.f;
+        for (int gi = c.g_off[r]; gi < c.g_off[r + 1]; ++gi) sum += __expf(c.z[gi] - mx);
+        return mx + __logf(sum);
+    };
+    auto spelling = [&](int sp) {
         float s = 0.f;
-        for (int i = c.c_path_off[k]; i < c.c_path_off[k + 1]; ++i) {
-            const int gi = c.c_path[i];
-            s += c.z[gi] - c.lse[c.g_ro[gi]];
+        const int i0 = c.s_path_off[sp], i1 = c.s_path_off[sp + 1];
+        for (int i = i0; i < i1; ++i) {
+            const int gi = c.s_path[i];
+            s += c.z[gi] - norm(c.g_ro[gi]);
         }
-        return s;
+        return mode == SCORE_MEAN ? s / (float)(i1 - i0) : s;
     };
     float best = -INFINITY, second = -INFINITY;
     int arg = 0;
     for (int k = c0; k < c1; ++k) {
-        const float s = score(k);
-        if (c.logscore) c.logscore[k] = s;
+        const int s0 = c.c_spell_off[k], s1 = c.c_spell_off[k + 1];
+        float s = spelling(s0);
+        if (s1 - s0 > 1) {
+            float mx = s;
+            for (int sp = s0 + 1; sp < s1; ++sp) mx = fmaxf(mx, spelling(sp));
+            float sum = 0.f;
+            for (int sp = s0; sp < s1; ++sp) sum += __expf(spelling(sp) - mx);
+            s = mx + __logf(sum);
+        }
+        c.logscore[k] = s;
         if (s > best) {
             second = best;
             best = s;
@@ -1409,8 +1433,8 @@ __global__ void k_combine(CombineCall c) {
     }
     const float invT = 1.0f / c.temperature;
     float den = 0.f;
-    for (int k = c0; k < c1; ++k) den += __expf((score(k) - best) * invT);
-    for (int k = c0; k < c1; ++k) c.prob[k] = __expf((score(k) - best) * invT) / den;
+    for (int k = c0; k < c1; ++k) den += __expf((c.logscore[k] - best) * invT);
+    for (int k = c0; k < c1; ++k) c.prob[k] = __expf((c.logscore[k] - best) * invT) / den;
     const int root = c.f_ro_root[f];
     float mass = 0.f;
     for (int gi = c.g_off[root]; gi < c.g_off[root + 1]; ++gi) mass += __expf(c.z[gi] - c.lse[root]);

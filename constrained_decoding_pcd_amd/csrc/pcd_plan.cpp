@@ -21,14 +21,61 @@ std::string fmt(const char *f, long a = 0, long b = 0, long c = 0) {
     return buf;
 }
 
-// Field validation in a fixed order: empty scaffold, candidate count, token
-// range, empty candidate, duplicate, proper prefix.  The limits follow the
-// pages' schema rules ("Parallel Constrained Decoding: A Technical
-// Reference", "At a glance" and the schema checklist: 2..255 choices).
-int validate(const pcd_field &f, const pcd_candidate *cands, int32_t V, std::string &err) {
+// One spelling of a label, as a view into the candidate's token array.
+struct Spell {
+    const int32_t *tok;
+    int32_t n;
+};
+
+// Field validation in a fixed order: scoring mode, empty scaffold, candidate
+// count, spelling layout, spelling count, token range, empty spelling,
+// duplicate, proper prefix.  The limits follow the pages' schema rules
+// ("Parallel Constrained Decoding: A Technical Reference", "At a glance" and
+// the schema checklist: 2..255 choices).  On success `sp` holds the field's
+// spellings, label by label.
+int validate(const pcd_field &f, const pcd_candidate *cands, int32_t V, std::vector<Spell> &sp,
+             std::vector<int32_t> &n_spell, std::string &err) {
+    if (f.score_mode < PCD_SCORE_PATH || f.score_mode > PCD_SCORE_MEAN) {
+        err = fmt("unknown scoring mode %ld", f.score_mode);
+        return PCD_E_ARG;
+    }
     if (f.n_scaffold <= 0 || !f.scaffold) { err = "empty scaffold"; return PCD_E_EMPTY; }
     if (f.n_cands < 2 || f.n_cands > PCD_MAX_CANDIDATES) {
         err = fmt("%ld candidates (allowed 2..%ld)", f.n_cands, PCD_MAX_CANDIDATES);
+        return PCD_E_NCAND;
+    }
+    sp.clear();
+    n_spell.clear();
+    for (int c = 0; c < f.n_cands; ++c) {
+        const pcd_candidate &k = cands[c];
+        if (k.n_tokens < 0 || (k.n_tokens > 0 && !k.tokens)) { err = "null candidate tokens"; return PCD_E_ARG; }
+        if (!k.spell_len) {
+            sp.push_back({k.tokens, k.n_tokens});
+            n_spell.push_back(1);
+            continue;
+        }
+        if (k.n_spellings <= 0) { err = fmt("candidate %ld: a label without spellings", c); return PCD_E_EMPTY; }
+        if (k.n_spellings > PCD_MAX_SPELLINGS) {
+            err = fmt("%ld spellings (allowed up to %ld)", k.n_spellings, PCD_MAX_SPELLINGS);
+            return PCD_E_NCAND;
+        }
+        int64_t off = 0;
+        for (int j = 0; j < k.n_spellings; ++j) {
+            if (k.spell_len[j] < 0 || off + k.spell_len[j] > k.n_tokens) {
+                err = fmt("candidate %ld: spelling lengths do not add up to its %ld tokens", c, k.n_tokens);
+                return PCD_E_ARG;
+            }
+            sp.push_back({k.tokens + off, k.spell_len[j]});
+            off += k.spell_len[j];
+        }
+        if (off != k.n_tokens) {
+            err = fmt("candidate %ld: spelling lengths do not add up to its %ld tokens", c, k.n_tokens);
+            return PCD_E_ARG;
+        }
+        n_spell.push_back(k.n_spellings);
+    }
+    if ((int64_t)sp.size() > PCD_MAX_SPELLINGS) {
+        err = fmt("%ld spellings (allowed up to %ld)", (long)sp.size(), PCD_MAX_SPELLINGS);
         return PCD_E_NCAND;
     }
     for (int i = 0; i < f.n_scaffold; ++i)
@@ -36,19 +83,17 @@ int validate(const pcd_field &f, const pcd_candidate *cands, int32_t V, std::str
             err = fmt("token id %ld outside [0, %ld)", f.scaffold[i], V);
             return PCD_E_TOKEN;
         }
-    for (int c = 0; c < f.n_cands; ++c) {
-        const pcd_candidate &k = cands[c];
-        if (k.n_tokens > 0 && !k.tokens) { err = "null candidate tokens"; return PCD_E_ARG; }
-        for (int i = 0; i < k.n_tokens; ++i)
-            if (k.tokens[i] < 0 || k.tokens[i] >= V) {
-                err = fmt("token id %ld outside [0, %ld)", k.tokens[i], V);
+    for (const Spell &s : sp)
+        for (int i = 0; i < s.n; ++i)
+            if (s.tok[i] < 0 || s.tok[i] >= V) {
+                err = fmt("token id %ld outside [0, %ld)", s.tok[i], V);
                 return PCD_E_TOKEN;
             }
-    }
+    for (const Spell &s : sp)
+        if (s.n <= 0) { err = "empty candidate"; return PCD_E_EMPTY; }
     std::set<std::vector<int32_t>> seen;
-    for (int c = 0; c < f.n_cands; ++c) {
-        if (cands[c].n_tokens <= 0) { err = "empty candidate"; return PCD_E_EMPTY; }
-        std::vector<int32_t> sq(cands[c].tokens, cands[c].tokens + cands[c].n_tokens);
+    for (const Spell &s : sp) {
+        std::vector<int32_t> sq(s.tok, s.tok + s.n);
         if (!seen.insert(sq).second) { err = fmt("duplicate candidate (%ld tokens)", (long)sq.size()); return PCD_E_DUP; }
     }
     std::vector<std::vector<int32_t>> sorted(seen.begin(), seen.end());
@@ -63,14 +108,14 @@ int validate(const pcd_field &f, const pcd_candidate *cands, int32_t V, std::str
     return PCD_OK;
 }
 
-// Trie with nodes renumbered breadth-first (node 0 = root).
-std::vector<Node> make_trie(const pcd_candidate *cands, int32_t n) {
+// Trie over the spellings with nodes renumbered breadth-first (node 0 = root).
+std::vector<Node> make_trie(const std::vector<Spell> &sp) {
     std::vector<Node> t(1);
-    for (int c = 0; c < n; ++c) {
+    for (const Spell &s : sp) {
         int cur = 0;
         t[0].n_cands++;
-        for (int i = 0; i < cands[c].n_tokens; ++i) {
-            int32_t tk = cands[c].tokens[i];
+        for (int i = 0; i < s.n; ++i) {
+            int32_t tk = s.tok[i];
             int nxt = -1;
             for (int k : t[cur].kids)
                 if (t[k].token == tk) { nxt = k; break; }
@@ -112,7 +157,8 @@ int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_
     p.anc_off.push_back(0);
     p.g_off.push_back(0);
     p.f_cand_off.push_back(0);
-    p.c_path_off.push_back(0);
+    p.c_spell_off.push_back(0);
+    p.s_path_off.push_back(0);
     int32_t gf = 0;
     for (int r = 0; r < n_req; ++r) {
         const pcd_request &rq = reqs[r];
@@ -135,12 +181,17 @@ int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_
                 return PCD_E_ARG;
             }
             const pcd_candidate *cands = rq.candidates + f.cand_offset;
-            int rc = validate(f, cands, V, err);
+            std::vector<Spell> sp;
+            std::vector<int32_t> n_spell;
+            int rc = validate(f, cands, V, sp, n_spell, err);
             if (rc != PCD_OK) {
                 err = fmt("request %ld field %ld: ", r, fi) + err;
                 return rc;
             }
-            std::vector<Node> t = make_trie(cands, f.n_cands);
+            // scoring to the end: every node a spelling continues from is read out
+            const bool to_end = f.score_mode == PCD_SCORE_EXACT || f.score_mode == PCD_SCORE_MEAN;
+            std::vector<Node> t = make_trie(sp);
+            auto is_ro = [&](size_t v) { return v == 0 || (to_end ? !t[v].kids.empty() : t[v].n_cands >= 2); };
             const int32_t ns = f.n_scaffold;
             if (P + ns - 1 >= max_seq) {
                 err = fmt("position %ld reaches max_seq %ld", P + ns - 1, max_seq);
@@ -159,11 +210,11 @@ int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_
                 for (int a = base; a <= base + j; ++a) p.anc.push_back(a);
                 p.anc_off.push_back((int32_t)p.anc.size());
             }
-            // continuation tokens: non-root nodes with >= 2 candidates below, BFS order
+            // continuation tokens: non-root readout nodes, BFS order
             std::vector<int32_t> branch_of(t.size(), -1), ro_of(t.size(), -1);
             branch_of[0] = base + ns - 1;
             for (size_t v = 1; v < t.size(); ++v) {
-                if (t[v].n_cands < 2) continue;
+                if (!is_ro(v)) continue;
                 const int32_t bi = (int32_t)p.tok.size();
                 branch_of[v] = bi;
                 const int32_t posv = P + ns + t[v].depth - 1;
@@ -189,7 +240,7 @@ int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_
             // readouts (root first, then BFS) and the child tokens gathered at each
             std::vector<int32_t> g_first(t.size(), -1);
             for (size_t v = 0; v < t.size(); ++v) {
-                if (v != 0 && t[v].n_cands < 2) continue;
+                if (!is_ro(v)) continue;
                 const int32_t ri = (int32_t)p.ro_tok.size();
                 if (v == 0) p.f_ro_root.push_back(ri);
                 ro_of[v] = ri;
@@ -202,21 +253,24 @@ int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_
                 }
                 p.g_off.push_back((int32_t)p.g_tok.size());
             }
-            // each candidate is scored on its edges down to the first node no other candidate reaches
-            for (int c = 0; c < f.n_cands; ++c) {
+            // each spelling is scored on its edges down to the first node no other
+            // spelling reaches, or on all of them when scoring to the end
+            for (const Spell &s : sp) {
                 int cur = 0;
-                for (int i = 0; i < cands[c].n_tokens; ++i) {
-                    const int32_t tk = cands[c].tokens[i];
+                for (int i = 0; i < s.n; ++i) {
+                    const int32_t tk = s.tok[i];
                     int slot = 0, nxt = -1;
                     for (; slot < (int)t[cur].kids.size(); ++slot)
                         if (t[t[cur].kids[slot]].token == tk) { nxt = t[cur].kids[slot]; break; }
-                    p.c_path.push_back(g_first[cur] + slot);
-                    if (t[nxt].n_cands == 1) break;
+                    p.s_path.push_back(g_first[cur] + slot);
+                    if (t[nxt].n_cands == 1 && !to_end) break;
                     cur = nxt;
                 }
-                p.c_path_off.push_back((int32_t)p.c_path.size());
+                p.s_path_off.push_back((int32_t)p.s_path.size());
             }
+            for (int c = 0; c < f.n_cands; ++c) p.c_spell_off.push_back(p.c_spell_off.back() + n_spell[c]);
             p.f_cand_off.push_back(p.f_cand_off.back() + f.n_cands);
+            p.f_mode.push_back(f.score_mode);
         }
     }
     p.r_tok.push_back((int32_t)p.tok.size());

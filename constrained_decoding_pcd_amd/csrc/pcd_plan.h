@@ -9,10 +9,18 @@
 // token is not enough").  Readout rows are the scaffold's last token (the
 // trie root) and every continuation token.
 //
-// Canonical numbering: candidates are inserted in declaration order, so a
-// node's children are ordered by the first candidate that reaches them;
-// nodes are numbered breadth-first.  The test suite checks these arrays
-// against an independent CPU implementation element by element.
+// Spellings ("Parallel Constrained Decoding from Scratch", "Small models
+// quote their booleans"): a label may be a set of token paths; the trie is
+// built over every spelling of every label of the field, and a spelling is
+// followed until no other spelling shares its tokens.  Scoring modes that
+// score a label to its end (EXACT, MEAN) make every node some spelling
+// continues from a continuation token and a readout.
+//
+// Canonical numbering: spellings are inserted in declaration order (label by
+// label, then in the order given), so a node's children are ordered by the
+// first spelling that reaches them; nodes are numbered breadth-first.  The
+// test suite checks these arrays against an independent CPU implementation
+// element by element.
 #pragma once
 #include <cstdint>
 #include <string>
@@ -35,9 +43,11 @@ struct Plan {
     // per gather
     std::vector<int32_t> g_tok, g_ro;
     // per field
-    std::vector<int32_t> f_ro_root, f_cand_off;
-    // per candidate
-    std::vector<int32_t> c_path_off, c_path;
+    std::vector<int32_t> f_ro_root, f_cand_off, f_mode;
+    // per candidate: its spellings
+    std::vector<int32_t> c_spell_off;
+    // per spelling: the gathers it is scored on, in depth order
+    std::vector<int32_t> s_path_off, s_path;
     // per request: first branch token / readout / gather / field / candidate (size n_req + 1)
     std::vector<int32_t> r_tok, r_ro, r_g, r_field, r_cand;
     std::vector<int32_t> prefix_len;  // per request

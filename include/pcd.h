@@ -15,6 +15,15 @@
  *     the same batched pass and multiplying along the path.
  *   - "Parallel Constrained Decoding: A Technical Reference" (shivam2003.com),
  *     section 4 "The algorithm": candidate softmax with temperature, argmax.
+ *   - "Parallel Constrained Decoding from Scratch", "Small models quote their
+ *     booleans": a label is the set of its spellings; its probability is the
+ *     sum of its spellings' path products (pcd_candidate.spell_len).
+ *   - Scoring modes for multi-token labels (pcd_field.score_mode): the same
+ *     page's "When one token is not enough" (scoring a label to the end of
+ *     its line), the "Parallel Constrained Decoding" engine README, "The
+ *     technique" (a product of per-level probabilities), and "Parallel
+ *     Constrained Decoding, From First Principles", "Multi-token candidates"
+ *     (length-normalised log-probabilities).
  *
  * Everything here works on token ids; tokenizing is the caller's business.
  *
@@ -45,8 +54,8 @@ extern "C" {
 #define PCD_OK 0
 #define PCD_E_ARG (-1)     /* null pointer, negative count, unsupported shape */
 #define PCD_E_TOKEN (-2)   /* token id outside [0, vocab_size) */
-#define PCD_E_NCAND (-3)   /* a field with fewer than 2 or more than 255 candidates */
-#define PCD_E_EMPTY (-4)   /* empty scaffold or empty candidate */
+#define PCD_E_NCAND (-3)   /* a field with fewer than 2 or more than 255 candidates, or too many spellings */
+#define PCD_E_EMPTY (-4)   /* empty scaffold, empty candidate or spelling, or a label without spellings */
 #define PCD_E_DUP (-5)     /* two identical candidate token sequences in one field */
 #define PCD_E_PREFIX (-6)  /* a candidate is a proper prefix of another one */
 #define PCD_E_CAP (-7)     /* a size exceeds max_seq, the workspace limits or a buffer */
@@ -55,6 +64,23 @@ extern "C" {
 #define PCD_E_NOMEM (-10)  /* host allocation failed */
 
 #define PCD_MAX_CANDIDATES 255
+#define PCD_MAX_SPELLINGS 1024 /* spellings of all labels of one field */
+
+/* Scoring modes.  A label's spelling c is scored on the log-probabilities of
+ * its tokens c[0..u], each conditioned on prefix + scaffold + c[<i]:
+ *   PATH  (0, the default): full-vocabulary log p, down to u(c), the first
+ *         token at which no other spelling of the field shares c's tokens;
+ *   EXACT (1): full-vocabulary log p of every token of c, to its end;
+ *   LEVEL (2): down to u(c), each token's probability renormalised over the
+ *         distinct tokens that the field's spellings continue with at that
+ *         point (a softmax over the trie node's children);
+ *   MEAN  (3): the EXACT sum divided by c's token count.
+ * The candidate mass is always the full-vocabulary probability of the
+ * distinct first tokens. */
+#define PCD_SCORE_PATH 0
+#define PCD_SCORE_EXACT 1
+#define PCD_SCORE_LEVEL 2
+#define PCD_SCORE_MEAN 3
 
 #define PCD_DTYPE_F32 0
 #define PCD_DTYPE_BF16 1
@@ -95,12 +121,21 @@ typedef struct {
     int32_t max_fields;          /* fields of one decide call, all requests */
     int32_t max_candidates;      /* candidates of one decide call, all requests */
     int32_t max_requests;        /* requests of one pcd_decide_many call */
+    int32_t max_spellings;       /* spellings of one decide call, all requests; 0: max_candidates */
 } pcd_limits;
 
 /* ---- one request's schema (host memory, read during the call) ------------ */
+/* A candidate is one label.  Without spellings (spell_len NULL) its token
+ * ids are `tokens`.  With spellings, `tokens` holds n_spellings token
+ * sequences back to back, of lengths spell_len[0..n_spellings), each >= 1 and
+ * summing to n_tokens; the label's probability sums over them.  Within a
+ * field, all spellings of all labels must be distinct and none a proper
+ * prefix of another; a field has at most PCD_MAX_SPELLINGS spellings. */
 typedef struct {
-    const int32_t *tokens;  /* the candidate's token ids */
+    const int32_t *tokens;
     int32_t n_tokens;
+    const int32_t *spell_len;  /* NULL: one spelling */
+    int32_t n_spellings;       /* ignored when spell_len is NULL */
 } pcd_candidate;
 
 typedef struct {
@@ -108,6 +143,7 @@ typedef struct {
     int32_t n_scaffold;
     int32_t cand_offset;      /* first candidate of this field in the request's candidate array */
     int32_t n_cands;          /* 2..255 */
+    int32_t score_mode;       /* PCD_SCORE_*; 0 (zero-initialised) is PCD_SCORE_PATH */
 } pcd_field;
 
 typedef struct {
@@ -120,7 +156,8 @@ typedef struct {
 /* ---- results (caller-owned HOST arrays, written only on PCD_OK) ---------- */
 typedef struct {
     float *cand_prob;        /* [n_candidates] softmax of logscore / T over each field's candidates */
-    float *cand_logscore;    /* [n_candidates] nullable: sum of log p along the candidate's scored path */
+    float *cand_logscore;    /* [n_candidates] nullable: the label's score under its field's mode; with
+                              * spellings, log of the sum of exp(spelling score) */
     float *field_mass;       /* [n_fields] full-vocabulary probability of the distinct first tokens */
     float *field_margin;     /* [n_fields] top-1 minus top-2 logscore, nats */
     int32_t *field_argmax;   /* [n_fields] candidate index within the field; ties to the lowest index */
@@ -139,16 +176,18 @@ typedef struct {
 
 /* Plan of one decide call, as laid out for the batched pass (host only). */
 typedef struct {
-    int32_t n_branch, n_readouts, n_gathers, n_fields, n_candidates, n_paths, n_anc;
+    int32_t n_branch, n_readouts, n_gathers, n_fields, n_candidates, n_paths, n_anc, n_spellings;
     /* Optional host arrays (NULL to skip), sized by the counts above:
      * per branch token: tok, pos, req, field; anc_off [n_branch+1] and anc
      * [n_anc]: the branch tokens each one sees (ascending, itself last);
      * per readout: ro_tok, ro_field, g_off [n_readouts+1]; per gather: g_tok;
-     * per field: f_ro_root, f_cand_off [n_fields+1]; per candidate:
-     * c_path_off [n_candidates+1] and c_path [n_paths] (gather indices). */
+     * per field: f_ro_root, f_cand_off [n_fields+1], f_mode (PCD_SCORE_*);
+     * per candidate: c_spell_off [n_candidates+1] (its spellings); per
+     * spelling: s_path_off [n_spellings+1] and s_path [n_paths] (the gather
+     * indices it is scored on, in depth order). */
     int32_t *tok, *pos, *req, *field, *anc_off, *anc;
     int32_t *ro_tok, *ro_field, *g_off, *g_tok;
-    int32_t *f_ro_root, *f_cand_off, *c_path_off, *c_path;
+    int32_t *f_ro_root, *f_cand_off, *f_mode, *c_spell_off, *s_path_off, *s_path;
 } pcd_plan_info;
 
 /* ---- functions -------------------------------------------------------------- */
@@ -254,7 +293,8 @@ int pcd_new_state(pcd_model *m, void *kv_buf, size_t kv_bytes, pcd_state **out);
 
 /* The first-field round: decide fields[0..n_first) in one batched pass,
  * append each of them (its scaffold followed by its argmax candidate's
- * tokens, in field order) to the state with pcd_extend, then decide the
+ * tokens, the first spelling of a label with spellings, in field order) to
+ * the state with pcd_extend, then decide the
  * remaining fields in a second batched pass against the extended prefix, so
  * that their rows see the earlier answers ("Parallel Constrained Decoding
  * from Scratch", "The idea: parallel constrained decoding": decide the first

@@ -81,7 +81,7 @@ def test_tiny_extend_kv_matches_prefill(tiny_w, tiny_dec):
     # decide against the grown state equals decide against the concatenation
     got = [m.decide(st, fields, debug=True)]
     ref = opcd.decide(tiny_dec, [(A + B + C, fields)])
-    _compare("tiny-extend", got, ref, ref.plan.c_path_off, "f32")
+    _compare("tiny-extend", got, ref, ref.plan, "f32")
     st.close()
     m.close()
 
@@ -103,7 +103,7 @@ def test_tiny_fork_serves_two_requests(tiny_w, tiny_dec):
         st.extend(inp)
         got = [m.decide(st, fields, debug=True)]
         ref = opcd.decide(tiny_dec, [(head + inp, fields)])
-        _compare(f"tiny-fork{k}", got, ref, ref.plan.c_path_off, "f32")
+        _compare(f"tiny-fork{k}", got, ref, ref.plan, "f32")
         st.close()
     assert torch.equal(kv0, hs.kv) and hs.n_tokens == len(head)
     hs.close()
@@ -125,6 +125,24 @@ def test_tiny_first_field_round(tiny_w, tiny_dec):
     _compare_fields("tiny-sequenced", got, first.fields + rest.fields, "f32")
     s = m.stats()
     assert s["prefill_passes"] == 2 and s["branch_passes"] == 2
+    st.close()
+    m.close()
+
+
+def test_tiny_first_field_round_spellings(tiny_w, tiny_dec):
+    """The first-field round on labels with spellings: the answer written in
+    is the chosen label's first spelling."""
+    sh = pi.SHAPES["tiny"]
+    prefix = _tokens(np.random.default_rng(24), sh.vocab_size, 50)
+    fields = pi.random_spelling_fields(1800, sh.vocab_size, 4, max_labels=5, max_spellings=3, max_len=3)
+    fields[2].mode = "exact"
+    ans_max = len(fields[0].scaffold) + max(len(c) for c in fields[0].candidates)
+    m = _model(sh, tiny_w, [len(prefix) + ans_max], [fields], len(prefix) + ans_max)
+    st = m.prefill(prefix, capacity=len(prefix) + ans_max)
+    got = m.decide_sequenced(st, fields, 1)
+    first, rest, ext = opcd.decide_sequenced(tiny_dec, prefix, fields, 1)
+    assert st.n_tokens == len(ext)
+    _compare_fields("tiny-sequenced-spell", got, first.fields + rest.fields, "f32")
     st.close()
     m.close()
 
@@ -171,7 +189,7 @@ def test_bf16_two_layer_warm_head_and_first_field_round(q15_l2):
     st.extend(prefix[400:])
     got = [m.decide(st, fields, debug=True)]
     ref = opcd.decide(dec, [(list(prefix), fields)])
-    _compare("q15-L2-warm", got, ref, ref.plan.c_path_off, "bf16")
+    _compare("q15-L2-warm", got, ref, ref.plan, "bf16")
     seq = m.decide_sequenced(st, fields, 1)
     first, rest, ext = opcd.decide_sequenced(dec, prefix, fields, 1)
     assert st.n_tokens == len(ext)
@@ -204,7 +222,7 @@ def test_tiny_fused_cold_request(tiny_w, tiny_dec):
     got = [m.extend_decide(st, prefix, fields, debug=True)]
     assert st.n_tokens == len(prefix)
     ref = opcd.decide(tiny_dec, [(prefix, fields)])
-    _compare("tiny-fused-cold", got, ref, ref.plan.c_path_off, "f32")
+    _compare("tiny-fused-cold", got, ref, ref.plan, "f32")
     kv = _kv(st, sh, len(prefix), np.float32)
     rkv = opcd.prefill(tiny_dec, prefix)
     err = max(float(np.max(np.abs(kv[l, i] - rkv[l][i]))) for l in range(sh.n_layers) for i in range(2))
@@ -213,7 +231,7 @@ def test_tiny_fused_cold_request(tiny_w, tiny_dec):
     assert s["branch_passes"] == 1 and s["prefill_passes"] == 0
     # the state serves later decides as a prefilled one would
     again = [m.decide(st, fields, debug=True)]
-    _compare("tiny-fused-then-decide", again, ref, ref.plan.c_path_off, "f32")
+    _compare("tiny-fused-then-decide", again, ref, ref.plan, "f32")
     st.close()
     m.close()
 
@@ -230,11 +248,28 @@ def test_tiny_fused_warm_request(tiny_w, tiny_dec):
     st = hs.fork(capacity=len(head) + len(inp))
     got = [m.extend_decide(st, inp, fields, debug=True)]
     ref = opcd.decide(tiny_dec, [(head + inp, fields)])
-    _compare("tiny-fused-warm", got, ref, ref.plan.c_path_off, "f32")
+    _compare("tiny-fused-warm", got, ref, ref.plan, "f32")
     got0 = [m.extend_decide(st, [], fields, debug=True)]
-    _compare("tiny-fused-none", got0, ref, ref.plan.c_path_off, "f32")
+    _compare("tiny-fused-none", got0, ref, ref.plan, "f32")
     st.close()
     hs.close()
+    m.close()
+
+
+def test_tiny_fused_spellings_and_modes(tiny_w, tiny_dec):
+    """Single-pass mode with labels that have spellings, one field pair per
+    scoring mode (90-token prefix)."""
+    sh = pi.SHAPES["tiny"]
+    prefix = _tokens(np.random.default_rng(34), sh.vocab_size, 90)
+    fields = []
+    for i, mode in enumerate(("path", "exact", "level", "mean")):
+        fields += pi.random_spelling_fields(1900 + i, sh.vocab_size, 2, max_spellings=4, max_len=4, mode=mode)
+    m = _fused_model(sh, tiny_w, len(prefix), fields)
+    st = m.new_state(len(prefix))
+    got = [m.extend_decide(st, prefix, fields, debug=True)]
+    ref = opcd.decide(tiny_dec, [(prefix, fields)])
+    _compare("tiny-fused-spell", got, ref, ref.plan, "f32")
+    st.close()
     m.close()
 
 
@@ -250,6 +285,6 @@ def test_bf16_two_layer_fused_cold(q15_l2):
         st = m.new_state(len(prefix))
         got = [m.extend_decide(st, prefix, fields, debug=True)]
         ref = opcd.decide(dec, [(list(prefix), fields)])
-        _compare(f"q15-L2-fused-{name}", got, ref, ref.plan.c_path_off, "bf16")
+        _compare(f"q15-L2-fused-{name}", got, ref, ref.plan, "bf16")
         st.close()
         m.close()

@@ -24,6 +24,7 @@ import pytest
 import pcd_inputs as pi
 from oracle import decoder as odec
 from oracle import pcd as opcd
+from test_gpu_parity import cand_depth
 
 cpd = pytest.importorskip("constrained_decoding_pcd_amd")
 torch = pytest.importorskip("torch")
@@ -34,7 +35,7 @@ DEEP = dict(z=6e-2, ls=6e-2, prob=2.5e-2, mass=5e-2)
 MARGIN_WAIVER = 0.05
 
 
-def _errors(got, ref_fields, ref_lse, ref_z, c_path_off):
+def _errors(got, ref_fields, ref_lse, ref_z, plan):
     prob = np.concatenate([g["prob"] for g in got])
     ls = np.concatenate([g["logscore"] for g in got])
     mass = np.concatenate([g["mass"] for g in got])
@@ -44,7 +45,7 @@ def _errors(got, ref_fields, ref_lse, ref_z, c_path_off):
     d = {
         "lse": float(np.max(np.abs(np.concatenate([g["lse"] for g in got]) - ref_lse))),
         "z": float(np.max(np.abs(np.concatenate([g["z"] for g in got]) - ref_z))),
-        "ls/len": float(np.max(np.abs(ls - rls) / np.diff(c_path_off))),
+        "ls/len": float(np.max(np.abs(ls - rls) / cand_depth(plan))),
         "prob": float(np.max(np.abs(prob - rprob))),
         "mass_rel": float(np.max(np.abs(mass - rmass) / rmass)),
     }
@@ -52,7 +53,7 @@ def _errors(got, ref_fields, ref_lse, ref_z, c_path_off):
 
 
 def _check(name, got, ref, tol=DEEP):
-    d = _errors(got, ref.fields, ref.lse, ref.z, ref.plan.c_path_off)
+    d = _errors(got, ref.fields, ref.lse, ref.z, ref.plan)
     arg = np.concatenate([g["argmax"] for g in got])
     agree = sum(int(a == f.argmax) for a, f in zip(arg, ref.fields))
     print(f"[{name}] max errors: " + ", ".join(f"{k} {v:.3e}" for k, v in d.items()) +

@@ -43,8 +43,16 @@ def _model(shape, weights, requests, max_prefill=0):
     return cpd.PcdModel(cpd.config_of(shape), dev, lim)
 
 
-def _compare(name, got, ref, plan_paths, dtype, label=""):
-    """got: list of per-request dicts from the library; ref: oracle result."""
+def cand_depth(plan) -> np.ndarray:
+    """Per candidate, the longest scored path over its spellings."""
+    slen = np.diff(plan.s_path_off)
+    return np.array([slen[plan.c_spell_off[c]:plan.c_spell_off[c + 1]].max()
+                     for c in range(len(plan.c_spell_off) - 1)])
+
+
+def _compare(name, got, ref, plan, dtype, label=""):
+    """got: list of per-request dicts from the library; ref: oracle result;
+    plan: the oracle's plan (for the candidates' path lengths)."""
     tol = TOL[dtype]
     lse = np.concatenate([g["lse"] for g in got])
     z = np.concatenate([g["z"] for g in got])
@@ -55,7 +63,7 @@ def _compare(name, got, ref, plan_paths, dtype, label=""):
     rprob = np.concatenate([f.prob for f in ref.fields])
     rls = np.concatenate([f.logscore for f in ref.fields])
     rmass = np.array([f.mass for f in ref.fields])
-    plen = np.diff(plan_paths)
+    plen = cand_depth(plan)
     d = {
         "lse": float(np.max(np.abs(lse - ref.lse))),
         "z": float(np.max(np.abs(z - ref.z))),
@@ -88,7 +96,7 @@ def _run_case(name, shape, weights, requests, temperature=1.0, dec=None):
     got = m.decide_many(states, [f for _, f in requests], temperature, debug=True)
     dec = dec or odec.Decoder(weights, np.float64)
     ref = opcd.decide(dec, requests, temperature)
-    _compare(name, got, ref, ref.plan.c_path_off, shape.dtype)
+    _compare(name, got, ref, ref.plan, shape.dtype)
     for s in states:
         s.close()
     m.close()
@@ -159,6 +167,34 @@ def test_tiny_deep_chains(tiny_w, tiny_dec):
         prefix = [int(t) for t in rng.integers(0, V, size=P)]
         reqs.append((prefix, _deep_chain_fields(900 + k, V) + pi.random_trie_fields(910 + k, V, 2)))
     _run_case("tiny-deep", pi.SHAPES["tiny"], tiny_w, reqs, dec=tiny_dec)
+
+
+@pytest.mark.parametrize("mode", ["path", "exact", "level", "mean"])
+def test_tiny_spellings_and_modes(tiny_w, tiny_dec, mode):
+    """Labels with up to four spellings sharing prefixes, plus deep tries,
+    under each scoring mode; two requests (prefixes 9 and 70) in one pass."""
+    V = pi.SHAPES["tiny"].vocab_size
+    rng = np.random.default_rng(13)
+    reqs = []
+    for k, P in enumerate((9, 70)):
+        prefix = [int(t) for t in rng.integers(0, V, size=P)]
+        fields = pi.random_spelling_fields(1300 + k, V, 4, max_labels=6, max_spellings=4, max_len=4, mode=mode)
+        fields += pi.random_trie_fields(1400 + k, V, 2, max_cands=9, max_len=4)
+        for f in fields[-2:]:
+            f.mode = mode
+        reqs.append((prefix, fields))
+    _run_case(f"tiny-spell-{mode}", pi.SHAPES["tiny"], tiny_w, reqs, dec=tiny_dec)
+
+
+def test_tiny_mixed_modes_one_request(tiny_w, tiny_dec):
+    """Fields of one request each in its own mode, labels with spellings,
+    at temperature 0.7."""
+    V = pi.SHAPES["tiny"].vocab_size
+    prefix = [int(t) for t in np.random.default_rng(14).integers(0, V, size=40)]
+    fields = []
+    for i, mode in enumerate(("path", "exact", "level", "mean", "exact", "level")):
+        fields += pi.random_spelling_fields(1500 + i, V, 1, max_labels=5, max_spellings=3, max_len=3, mode=mode)
+    _run_case("tiny-mixed-modes", pi.SHAPES["tiny"], tiny_w, [(prefix, fields)], 0.7, dec=tiny_dec)
 
 
 def test_tiny_prefill_kv(tiny_w, tiny_dec):
@@ -237,6 +273,19 @@ def test_bf16_two_layer_cfg1(q15_l2):
     1.5B-shaped model: every output of every field."""
     sh, w, dec = q15_l2
     _run_case("q15-L2-cfg1", sh, w, _reqs(pi.make_workload("cfg1")), dec=dec)
+
+
+def test_bf16_two_layer_spellings_and_modes(q15_l2):
+    """The 1.5B widths in bf16: the cfg1 prefix with fields whose labels have
+    several spellings, one field group per scoring mode, in one pass."""
+    sh, w, dec = q15_l2
+    wl = pi.make_workload("cfg1")
+    prefix = wl.requests[0].prefix
+    fields = []
+    for i, mode in enumerate(("path", "exact", "level", "mean")):
+        fields += pi.random_spelling_fields(1600 + i, sh.vocab_size, 3, max_labels=8, max_spellings=3,
+                                            max_len=3, mode=mode)
+    _run_case("q15-L2-spell", sh, w, [(prefix, fields)], dec=dec)
 
 
 def test_bf16_two_layer_cfg2_id_field(q15_l2):

@@ -65,6 +65,25 @@ def test_plan_equals_oracle_random_tries(seed):
     _compare_plans(reqs, V)
 
 
+@pytest.mark.parametrize("mode", ["path", "exact", "level", "mean"])
+@pytest.mark.parametrize("seed", range(3))
+def test_plan_equals_oracle_spellings_and_modes(seed, mode):
+    """Labels with several spellings, and every scoring mode (EXACT and MEAN
+    read out at every node a spelling continues from)."""
+    V = 3000
+    rng = np.random.default_rng(50 + seed)
+    reqs = []
+    for r in range(1 + seed % 2):
+        prefix = [int(t) for t in rng.integers(0, V, size=int(rng.integers(1, 40)))]
+        fields = pi.random_spelling_fields(700 + 10 * seed + r, V, 4, max_labels=6, max_spellings=4, max_len=4,
+                                           mode=mode)
+        fields += pi.random_trie_fields(900 + 10 * seed + r, V, 2, max_cands=9, max_len=4)
+        for f in fields[-2:]:
+            f.mode = mode
+        reqs.append((prefix, fields))
+    _compare_plans(reqs, V)
+
+
 def test_plan_id_field_with_255_options():
     wl = pi.make_workload("cfg2")
     r = wl.requests[0]
@@ -81,6 +100,12 @@ def test_plan_id_field_with_255_options():
     (pi.Field([3], [[1], [1, 2]]), "PREFIX"),
     (pi.Field([3], [[1], [5000]]), "TOKEN"),
     (pi.Field([-1], [[1], [2]]), "TOKEN"),
+    (pi.Field([3], [[1], [2]], mode="greedy"), "ARG"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1]], []]), "EMPTY"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1], [7, 2]], [[2], [7, 2]]]), "DUP"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1], [7]], [[2], [7, 2]]]), "PREFIX"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1], [7, 9999]], [[2]]]), "TOKEN"),
+    (pi.Field([3], [[1], [2]], spellings=[[[1]], [[2]] + [[9, i] for i in range(1023)]]), "NCAND"),
 ])
 def test_plan_rejects_like_the_oracle(bad, code):
     with pytest.raises(oplan.PlanError) as e:
@@ -102,7 +127,7 @@ def test_positions_beyond_max_seq_are_rejected():
 def test_workspace_bytes_rejects_bad_configs(lib):
     good = dict(n_layers=2, d_model=128, n_heads=4, n_kv_heads=2, head_dim=32, ffn_dim=384, vocab_size=2048,
                 max_seq=512, rope_theta=1e4, rms_eps=1e-6, tied_lm_head=1, dtype=0)
-    lim = cpd.binding.pcd_limits(256, 64, 16, 64, 8, 32, 2)
+    lim = cpd.binding.pcd_limits(256, 64, 16, 64, 8, 32, 2, 0)
     assert lib.pcd_workspace_bytes(ctypes.byref(cpd.binding.pcd_config(**good)), ctypes.byref(lim)) > 0
     for k, v in (("head_dim", 48), ("n_kv_heads", 3), ("d_model", 100), ("dtype", 7), ("vocab_size", 2000)):
         bad = dict(good, **{k: v})
