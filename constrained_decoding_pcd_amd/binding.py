@@ -22,7 +22,8 @@ ERROR_NAMES = {-1: "ARG", -2: "TOKEN", -3: "NCAND", -4: "EMPTY", -5: "DUP", -6: 
                -8: "STATE", -9: "DEVICE", -10: "NOMEM"}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_extend",
+EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_prefill_many",
+           "pcd_extend",
            "pcd_fork", "pcd_state_tokens", "pcd_new_state", "pcd_decide", "pcd_extend_decide",
            "pcd_decide_sequenced", "pcd_decide_many",
            "pcd_debug_plan", "pcd_get_stats",
@@ -121,6 +122,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        P(c_void_p)]),
         "pcd_state_bytes": (c_size_t, [c_void_p, c_int32]),
         "pcd_prefill": (c_int32, [c_void_p, P(c_int32), c_int32, c_void_p, c_size_t, c_void_p, P(c_void_p)]),
+        "pcd_prefill_many": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_void_p), P(c_size_t),
+                                       c_void_p, P(c_void_p)]),
         "pcd_extend": (c_int32, [c_void_p, P(c_int32), c_int32, c_void_p]),
         "pcd_fork": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p, P(c_void_p)]),
         "pcd_state_tokens": (c_int32, [c_void_p]),
@@ -348,6 +351,24 @@ class PcdModel:
         _check(self.lib.pcd_prefill(self.handle, _i32p(t), t.size, c_void_p(kv.data_ptr()), kv.numel(),
                                     _stream_handle(torch), ctypes.byref(h)))
         return PcdState(self, h, kv, t.size)
+
+    def prefill_many(self, seqs: Sequence[Sequence[int]], kvs=None) -> List[PcdState]:
+        """pcd_prefill_many: every sequence prefilled in one pass, each into its
+        own buffer (`kvs`, or new buffers of exactly its length)."""
+        torch = self.torch
+        arrs = [np.ascontiguousarray(q, dtype=np.int32) for q in seqs]
+        toks = np.ascontiguousarray(np.concatenate(arrs) if arrs else np.zeros(0, np.int32), dtype=np.int32)
+        lens = np.ascontiguousarray([a.size for a in arrs], dtype=np.int32)
+        if kvs is None:
+            kvs = [torch.empty(max(self.state_bytes(a.size), 1), dtype=torch.uint8, device=self.workspace.device)
+                   for a in arrs]
+        n = len(arrs)
+        bufs = (c_void_p * max(1, n))(*[kv.data_ptr() for kv in kvs])
+        sizes = (c_size_t * max(1, n))(*[kv.numel() for kv in kvs])
+        hs = (c_void_p * max(1, n))()
+        _check(self.lib.pcd_prefill_many(self.handle, n, _i32p(toks), _i32p(lens), bufs, sizes,
+                                         _stream_handle(torch), hs))
+        return [PcdState(self, c_void_p(hs[i]), kvs[i], int(lens[i])) for i in range(n)]
 
     def decide(self, state: PcdState, fields, temperature: float = 1.0, debug: bool = False) -> dict:
         return self.decide_many([state], [fields], temperature, debug)[0]

@@ -238,9 +238,16 @@ bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W,
 // KV head, and whose attention is run by `attn` (prefill or branch)
 enum class Pass { Prefill, Branch, Fused };  // which timing classes a layer's kernels count under
 
+// K/V destinations of rows spread over several state buffers (batched prefill)
+struct KvRows {
+    const int32_t *req, *row, *cap;  // per row: buffer, token slot; per buffer: tokens per slab
+    const uint64_t *base;            // per buffer: device address
+};
+
 template <class Attn>
 int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, int cap, Pass kind, Attn attn,
-          hipStream_t st, void *kc2 = nullptr, void *vc2 = nullptr, int cap2 = 0, int kv_split = 0) {
+          hipStream_t st, void *kc2 = nullptr, void *vc2 = nullptr, int cap2 = 0, int kv_split = 0,
+          const KvRows *kr = nullptr) {
     const bool br = kind == Pass::Branch, fu = kind == Pass::Fused;
     const int K_QKV = fu ? PCD_KC_FUSED_QKV : br ? PCD_KC_BRANCH_QKV : PCD_KC_PREFILL_QKV;
     const int K_O = fu ? PCD_KC_FUSED_O : br ? PCD_KC_BRANCH_O : PCD_KC_PREFILL_O;
@@ -273,6 +280,13 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     g.vc2 = vc2;
     g.cap2 = cap2;
     g.kv_split = kv_split;
+    if (kr) {
+        g.kv_req = kr->req;
+        g.kv_row = kr->row;
+        g.kv_cap = kr->cap;
+        g.kv_base = kr->base;
+        g.kv_layer = l;
+    }
     g.pos = pos;
     g.rope = reinterpret_cast<const float2 *>(m->ws + m->L.rope);
     g.n_q = nq;
@@ -433,7 +447,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
         for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
             const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
             for (int k = 0; k < ns && k * slen <= t_last; ++k)
-                blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0, 1});
+                blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0, 1, P0});
         }
     if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
     std::vector<int32_t> tok_splits(n);
@@ -480,7 +494,6 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
             a.req_stride = d_stride;
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
-            a.q_pos0 = P0;
             a.tok_splits = d_tsp;
             a.out = ao;
             a.part_o = part_o;
@@ -524,6 +537,122 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     return PCD_OK;
 }
 
+// One causal pass over n_seqs sequences laid back to back (prefill of a batch
+// of prompts): token t of sequence r sits at position t - t0[r] and attends
+// the keys of its own sequence up to itself; each sequence's K and V go to
+// its own buffer (bufs[r], caps[r] tokens per slab).  Attention is split over
+// workgroups as in causal_pass, with one split length for all sequences.
+int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps, const int32_t *tokens,
+                const int32_t *lens, hipStream_t st) {
+    const pcd_config &c = m->cfg;
+    const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim;
+    std::vector<int32_t> t0(n_seqs + 1, 0);
+    int max_len = 0;
+    int64_t row_blocks = 0;
+    for (int r = 0; r < n_seqs; ++r) {
+        t0[r + 1] = t0[r] + lens[r];
+        max_len = std::max(max_len, lens[r]);
+        row_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + ATT_ROWS - 1) / ATT_ROWS);
+    }
+    const int n = t0[n_seqs];
+    int ns = att_splits(row_blocks, (max_len + 63) / 64);
+    const int slen = ((max_len + ns - 1) / ns + 63) / 64 * 64;
+    ns = (max_len + slen - 1) / slen;
+    std::vector<AttnBlock> blocks;
+    for (int r = 0; r < n_seqs; ++r)
+        for (int g = 0; g < c.n_kv_heads; ++g)
+            for (int r0 = t0[r] * grp; r0 < t0[r + 1] * grp; r0 += ATT_ROWS) {
+                const int nr = std::min(ATT_ROWS, t0[r + 1] * grp - r0);
+                const int p_last = (r0 + nr - 1) / grp - t0[r];  // position of the block's last token
+                for (int k = 0; k < ns && k * slen <= p_last; ++k)
+                    blocks.push_back(AttnBlock{r, g, r0, nr, k * slen, std::min(lens[r], (k + 1) * slen), k, ns, 0, 0,
+                                               1, -t0[r]});
+            }
+    if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
+    std::vector<int32_t> tok_splits(n), pos(n), req(n);
+    std::vector<uint64_t> base(n_seqs);
+    for (int r = 0; r < n_seqs; ++r) {
+        base[r] = reinterpret_cast<uint64_t>(bufs[r]);
+        for (int t = t0[r]; t < t0[r + 1]; ++t) {
+            pos[t] = t - t0[r];
+            req[t] = r;
+            tok_splits[t] = pos[t] / slen + 1;
+        }
+    }
+    Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
+    const int32_t *d_tok = pk.put(tokens, n);
+    const int32_t *d_pos = pk.put(pos.data(), n);
+    const int32_t *d_req = pk.put(req.data(), n);
+    const uint64_t *d_kv = pk.put(base.data(), n_seqs);
+    const int32_t *d_stride = pk.put(caps, n_seqs);
+    const int32_t *d_tsp = pk.put(tok_splits.data(), n);
+    const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
+    if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
+    const KvRows kr{d_req, d_pos, d_stride, d_kv};  // a token's slot in its buffer is its position
+    m->settle_prefill();
+    HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipEventRecord(m->ev[5], st));
+    HIP_TRY(hipEventRecord(m->ev[3], st));
+    float *x = reinterpret_cast<float *>(m->ws + m->L.x);
+    m->tbegin(PCD_KC_OTHER, st);
+    embed(c.dtype, d_tok, n, m->embed, c.d_model, x, m->an[0], c.rms_eps, m->ws + m->L.h, st);
+    m->tend(st);
+    float *part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
+    float2 *part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
+    for (int l = 0; l < c.n_layers; ++l) {
+        auto attn = [&](void *q, void *ao) {
+            AttnCall a{};
+            a.dt = c.dtype;
+            a.hd = hd;
+            a.n_heads = c.n_heads;
+            a.n_kv_heads = c.n_kv_heads;
+            a.layer = l;
+            a.q = q;
+            a.req_kv = d_kv;
+            a.req_stride = d_stride;
+            a.blocks = d_blk;
+            a.n_blocks = (int)blocks.size();
+            a.tok_splits = d_tsp;
+            a.out = ao;
+            a.part_o = part_o;
+            a.part_ml = part_ml;
+            a.n_tokens = n;
+            m->tbegin(PCD_KC_PREFILL_ATTN, st);
+            const bool ok = attention(a, st);
+            m->tend(st);
+            if (!ok) return fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
+            if (ns > 1) {
+                TailCall t{};
+                t.dt = c.dtype;
+                t.hd = hd;
+                t.n_heads = c.n_heads;
+                t.n_kv_heads = c.n_kv_heads;
+                t.n_tokens = n;
+                t.part_o = part_o;
+                t.part_ml = part_ml;
+                t.tok_splits = d_tsp;
+                t.out = ao;
+                m->tbegin(PCD_KC_PREFILL_ATTN, st);
+                attention_merge(t, st);
+                m->tend(st);
+            }
+            return PCD_OK;
+        };
+        int rc = layer(m, l, n, d_pos, nullptr, nullptr, 0, Pass::Prefill, attn, st, nullptr, nullptr, 0, 0, &kr);
+        if (rc != PCD_OK) return rc;
+    }
+    HIP_TRY(hipEventRecord(m->ev[4], st));
+    HIP_TRY(hipGetLastError());
+    HIP_TRY(hipEventSynchronize(m->ev[5]));
+    m->prefill_pending = true;
+    if (m->timing) {
+        HIP_TRY(hipStreamSynchronize(st));
+        m->tcollect();
+    }
+    m->stats.prefill_passes += 1;
+    return PCD_OK;
+}
+
 int check_tokens(const pcd_model *m, const int32_t *tokens, int32_t n) {
     for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab_size)
@@ -532,6 +661,55 @@ int check_tokens(const pcd_model *m, const int32_t *tokens, int32_t n) {
 }
 
 }  // namespace
+
+int pcd_prefill_many(pcd_model *m, int32_t n_seqs, const int32_t *tokens, const int32_t *lens, void *const *kv_bufs,
+                     const size_t *kv_bytes, void *stream, pcd_state **out) {
+    if (!m || !tokens || !lens || !kv_bufs || !kv_bytes || !out) return fail(PCD_E_ARG, "null argument");
+    const pcd_config &c = m->cfg;
+    if (n_seqs <= 0 || n_seqs > m->lim.max_requests)
+        return fail(PCD_E_ARG, std::to_string(n_seqs) + " sequences (allowed 1.." +
+                                   std::to_string(m->lim.max_requests) + ")");
+    int64_t total = 0;
+    std::vector<int32_t> caps(n_seqs);
+    std::vector<std::pair<uint64_t, uint64_t>> spans(n_seqs);
+    for (int r = 0; r < n_seqs; ++r) {
+        if (lens[r] <= 0) return fail(PCD_E_ARG, "sequence " + std::to_string(r) + " is empty");
+        if (!kv_bufs[r]) return fail(PCD_E_ARG, "null KV buffer for sequence " + std::to_string(r));
+        if (lens[r] > c.max_seq) return fail(PCD_E_CAP, "sequence " + std::to_string(r) + " exceeds max_seq");
+        if (kv_bytes[r] < pcd_state_bytes(m, lens[r]))
+            return fail(PCD_E_CAP, "KV buffer of sequence " + std::to_string(r) + " too small");
+        total += lens[r];
+        caps[r] = (int32_t)std::min<size_t>(kv_bytes[r] / per_token_bytes(m), (size_t)c.max_seq);
+        const uint64_t b = reinterpret_cast<uint64_t>(kv_bufs[r]);
+        spans[r] = {b, b + (uint64_t)caps[r] * per_token_bytes(m)};
+    }
+    if (total > m->lim.max_prefill_tokens)
+        return fail(PCD_E_CAP, std::to_string(total) + " tokens exceed the model's max_prefill_tokens");
+    std::sort(spans.begin(), spans.end());
+    for (int r = 1; r < n_seqs; ++r)
+        if (spans[r].first < spans[r - 1].second) return fail(PCD_E_ARG, "two sequences share KV buffer memory");
+    int rc = check_tokens(m, tokens, (int32_t)total);
+    if (rc != PCD_OK) return rc;
+    std::vector<pcd_state *> made(n_seqs, nullptr);
+    for (int r = 0; r < n_seqs; ++r) {
+        made[r] = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_bufs[r], 0, caps[r]};
+        if (!made[r]) {
+            for (pcd_state *p : made) delete p;
+            return fail(PCD_E_NOMEM, "state allocation");
+        }
+    }
+    rc = causal_many(m, n_seqs, kv_bufs, caps.data(), tokens, lens, static_cast<hipStream_t>(stream));
+    if (rc != PCD_OK) {
+        for (pcd_state *p : made) delete p;
+        return rc;
+    }
+    for (int r = 0; r < n_seqs; ++r) {
+        made[r]->P = lens[r];
+        out[r] = made[r];
+    }
+    m->n_states += n_seqs;
+    return PCD_OK;
+}
 
 int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, size_t kv_bytes, void *stream,
                 pcd_state **out) {
@@ -725,7 +903,7 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                 const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
                 for (int k = 0; k < s && k * slen <= t_last; ++k)
                     blocks.push_back(
-                        AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1});
+                        AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1, P0});
             }
     }
     for (int r = 0; r < n_req; ++r) {
@@ -742,7 +920,7 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                 const int b_first = r0 / grp - n_new, b_last = (r0 + nr - 1) / grp - n_new;  // plan indices
                 for (int k = 0; k < s; ++k)
                     blocks.push_back(AttnBlock{r, g, r0, nr, k * slen, std::min(P, (k + 1) * slen), k, s,
-                                               k == s - 1 ? p.fs[b_first] : 0, k == s - 1 ? b_last + 1 : 0, 0});
+                                               k == s - 1 ? p.fs[b_first] : 0, k == s - 1 ? b_last + 1 : 0, 0, 0});
             }
     }
     if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
@@ -836,7 +1014,6 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
             a.req_stride = d_stride;
             a.blocks = d_blk;
             a.n_blocks = (int)blocks.size();
-            a.q_pos0 = P0;
             a.branch0 = n_new;
             a.tok_splits = d_tsp;
             a.out = ao;

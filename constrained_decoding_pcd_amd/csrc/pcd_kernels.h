@@ -45,6 +45,13 @@ struct GemmCall {
     int32_t cap;     // Qkv: tokens per KV head in the cache
     void *kc2, *vc2; // Qkv (optional): rows m >= kv_split go to row m - kv_split of this cache instead
     int32_t cap2, kv_split;
+    // Qkv (optional, replaces kc/vc): rows spread over several KV buffers.
+    // Row m goes to buffer kv_req[m] at token slot kv_row[m]; buffer r
+    // starts at kv_base[r], is laid out [layer][K|V][Hkv][kv_cap[r]][hd],
+    // and this call writes layer kv_layer.
+    const int32_t *kv_req, *kv_row, *kv_cap;
+    const uint64_t *kv_base;
+    int32_t kv_layer;
     const int32_t *pos;  // Qkv: position of each row (NULL: row index)
     const float2 *rope;  // Qkv: [max_seq][hd/2] (cos, sin)
     int32_t n_q, n_k, hd;    // Qkv: columns of q and of k; head dim
@@ -76,7 +83,9 @@ void resid_norm(int dt, const float *part, int32_t splits, int32_t M, int32_t N,
 // partials for attention_merge.
 struct AttnBlock {
     int32_t req, g, row0, nrows, key0, key1, split, nsplit, sfx_lo, sfx_hi;
-    int32_t causal;  // rows see keys up to their own position (q_pos0 + token); else the whole key range
+    int32_t causal;  // rows see keys up to their own position; else the whole key range
+    int32_t qoff;    // causal blocks: row token t is at position t + qoff and sees keys <= t + qoff
+                     // (rows with t + qoff < key0 are skipped)
 };
 struct AttnCall {
     int dt;
@@ -86,8 +95,6 @@ struct AttnCall {
     const int32_t *req_stride; // per request: tokens per (layer, K|V, KV head) slab of its KV buffer
     const AttnBlock *blocks;
     int32_t n_blocks;
-    int32_t q_pos0;         // causal blocks: row token t is at position q_pos0 + t and sees keys <= q_pos0 + t
-                            // (rows with q_pos0 + t < key0 are skipped)
     int32_t branch0;        // first row token of the branch tokens (their plan index is token - branch0)
     const int32_t *tok_splits;  // per row token: key splits covering it (<= 1: written directly)
     void *out;              // [tokens][Hq][hd] (dt)

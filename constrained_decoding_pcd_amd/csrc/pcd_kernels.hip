@@ -134,6 +134,9 @@ struct EpiArgs {
     float *x, *part;
     void *out, *kc, *vc, *kc2, *vc2;
     int32_t cap, cap2, kv_split, n_q, n_k, hd;
+    const int32_t *kv_req, *kv_row, *kv_cap;
+    const uint64_t *kv_base;
+    int32_t kv_layer;
     const int32_t *pos;
     const float2 *rope;
     float2 *ro_part;
@@ -391,6 +394,14 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
                 T *dst;
                 if (n < e.n_q) {
                     dst = reinterpret_cast<T *>(e.out) + (size_t)m * e.n_q + (n - j);
+                } else if (e.kv_req) {
+                    // one of several KV buffers (batched prefill)
+                    const int rq = e.kv_req[m], Hkv = e.n_k / hd;
+                    const size_t slab = (size_t)e.kv_cap[rq] * hd;
+                    const bool is_k = n < e.n_q + e.n_k;
+                    const int kh = is_k ? (n - e.n_q) / hd : (n - e.n_q - e.n_k) / hd;
+                    dst = reinterpret_cast<T *>(e.kv_base[rq]) +
+                          ((size_t)(e.kv_layer * 2 + (is_k ? 0 : 1)) * Hkv + kh) * slab + (size_t)e.kv_row[m] * hd;
                 } else {
                     // rows from kv_split on go to the second cache (the branch tokens of a fused pass)
                     const bool second = m >= e.kv_split;
@@ -455,6 +466,11 @@ static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     e.vc2 = c.vc2;
     e.cap2 = c.cap2;
     e.kv_split = c.kc2 ? c.kv_split : c.M;
+    e.kv_req = c.kv_req;
+    e.kv_row = c.kv_row;
+    e.kv_cap = c.kv_cap;
+    e.kv_base = c.kv_base;
+    e.kv_layer = c.kv_layer;
     e.n_q = c.n_q;
     e.n_k = c.n_k;
     e.hd = c.hd;
@@ -798,7 +814,7 @@ __device__ __forceinline__ void attn_write(const AttnCall &c, const AttnBlock &b
         if (w * 16 + qi >= blk.nrows) continue;
         const int row = blk.row0 + w * 16 + qi;
         const int t = row / grp, h = blk.g * grp + row % grp;
-        if (blk.causal && c.q_pos0 + t < blk.key0) continue;  // causal row with no key in this split
+        if (blk.causal && blk.qoff + t < blk.key0) continue;  // causal row with no key in this split
         if (c.tok_splits[t] <= 1) {
             T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
             const float inv = 1.0f / lq;
@@ -851,11 +867,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     Frag<T> qf[HS];
 #pragma unroll
     for (int s = 0; s < HS; ++s) ld8(qf[s], Q + ((size_t)tq * Hq + hq) * HD + s * 32 + lg * 8);
-    const int kend_row = blk.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
+    const int kend_row = blk.causal ? min(blk.qoff + tq + 1, blk.key1) : blk.key1;
 
     int kmax = blk.key1;
     if (blk.causal) {
-        const int last = c.q_pos0 + (blk.row0 + blk.nrows - 1) / grp + 1;
+        const int last = blk.qoff + (blk.row0 + blk.nrows - 1) / grp + 1;
         kmax = last < kmax ? last : kmax;
     }
     const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;
@@ -1081,10 +1097,10 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     const bool row_ok = (w * 16 + lr) < blk.nrows;
     const int rr = row_ok ? blk.row0 + w * 16 + lr : blk.row0;
     const int tq = rr / grp;
-    const int kend_row = blk.causal ? min(c.q_pos0 + tq + 1, blk.key1) : blk.key1;
+    const int kend_row = blk.causal ? min(blk.qoff + tq + 1, blk.key1) : blk.key1;
     int kmax = blk.key1;
     if (blk.causal) {
-        const int last = c.q_pos0 + (blk.row0 + blk.nrows - 1) / grp + 1;
+        const int last = blk.qoff + (blk.row0 + blk.nrows - 1) / grp + 1;
         kmax = last < kmax ? last : kmax;
     }
     const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;

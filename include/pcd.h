@@ -231,6 +231,21 @@ size_t pcd_state_bytes(const pcd_model *m, int32_t n_tokens);
 int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n_tokens, void *kv_buf, size_t kv_bytes,
                 void *stream, pcd_state **out);
 
+/* Prefill of a batch of prompts in one causal pass: n_seqs sequences given
+ * back to back in tokens (host array; sequence r has lens[r] >= 1 tokens),
+ * each at positions 0..lens[r]-1 and attending only its own tokens, so the
+ * result per sequence is that of pcd_prefill on it alone (the batched form of
+ * "Parallel Constrained Decoding from Scratch", "The idea: parallel
+ * constrained decoding", step 1, for many requests at once).  Sequence r's K
+ * and V go to kv_bufs[r] (device, kv_bytes[r] >= pcd_state_bytes(m,
+ * lens[r]); buffers must not overlap), and out[r] (host array of n_seqs
+ * handles) receives its state.  n_seqs <= max_requests and the total token
+ * count <= max_prefill_tokens; everything is validated before any device
+ * work, and on failure no state is created.  Ordering and timing as for
+ * pcd_prefill. */
+int pcd_prefill_many(pcd_model *m, int32_t n_seqs, const int32_t *tokens, const int32_t *lens, void *const *kv_bufs,
+                     const size_t *kv_bytes, void *stream, pcd_state **out);
+
 /* Append tokens[0..n_tokens) (host array) to a state: one causal pass of the
  * decoder at positions P..P+n_tokens-1 whose attention covers the state's P
  * cached tokens and the new ones before each token, writing the new tokens'

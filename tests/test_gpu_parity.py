@@ -197,6 +197,61 @@ def test_tiny_mixed_modes_one_request(tiny_w, tiny_dec):
     _run_case("tiny-mixed-modes", pi.SHAPES["tiny"], tiny_w, [(prefix, fields)], 0.7, dec=tiny_dec)
 
 
+def test_tiny_prefill_many(tiny_w, tiny_dec):
+    """Three prompts (1, 64 and 130 tokens: below, at and across the 64-key
+    tile) prefilled in one pass: each state's KV equals the oracle's prefill
+    of that prompt alone, and one branch pass over the three states decides
+    as the oracle does."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(17)
+    reqs = []
+    for k, P in enumerate((1, 64, 130)):
+        prefix = [int(t) for t in rng.integers(0, sh.vocab_size, size=P)]
+        reqs.append((prefix, pi.random_trie_fields(1100 + k, sh.vocab_size, 3)))
+    m = _model(sh, tiny_w, reqs, max_prefill=sum(len(p) for p, _ in reqs))
+    states = m.prefill_many([p for p, _ in reqs])
+    for st, (prefix, _) in zip(states, reqs):
+        assert st.n_tokens == len(prefix)
+        kv = st.kv.view(torch.float32).cpu().numpy().reshape(sh.n_layers, 2, sh.n_kv_heads, len(prefix), sh.head_dim)
+        ref = opcd.prefill(tiny_dec, prefix)
+        err = max(float(np.max(np.abs(kv[l, i] - ref[l][i]))) for l in range(sh.n_layers) for i in range(2))
+        print(f"[prefill-many] P={len(prefix)} KV max abs error {err:.3e}", flush=True)
+        assert err < 1e-4
+    got = m.decide_many(states, [f for _, f in reqs], debug=True)
+    ref = opcd.decide(tiny_dec, reqs)
+    _compare("tiny-prefill-many", got, ref, ref.plan, "f32")
+    assert m.stats()["prefill_passes"] == 1
+    for st in states:
+        st.close()
+    m.close()
+
+
+def test_tiny_prefill_many_errors(tiny_w):
+    """Rejected before any device work: shared buffer memory, too many tokens,
+    a token outside the vocabulary, an empty sequence."""
+    sh = pi.SHAPES["tiny"]
+    fields = pi.make_workload("cfg0").requests[0].fields
+    m = _model(sh, tiny_w, [([1] * 10, fields), ([2] * 10, fields)], max_prefill=20)
+    one = torch.empty(m.state_bytes(20), dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(cpd.PcdError) as e:
+        m.prefill_many([[1] * 10, [2] * 10], kvs=[one, one])
+    assert e.value.name == "ARG"
+    with pytest.raises(cpd.PcdError) as e:
+        m.prefill_many([[1] * 12, [2] * 10])
+    assert e.value.name == "CAP"
+    with pytest.raises(cpd.PcdError) as e:
+        m.prefill_many([[1] * 10, [2, sh.vocab_size]])
+    assert e.value.name == "TOKEN"
+    with pytest.raises(cpd.PcdError) as e:
+        m.prefill_many([[1] * 10, []])
+    assert e.value.name == "ARG"
+    sts = m.prefill_many([[1] * 10, [2] * 10])
+    assert [s.n_tokens for s in sts] == [10, 10]
+    for s in sts:
+        s.close()
+    m.close()
+
+
 def test_tiny_prefill_kv(tiny_w, tiny_dec):
     """The state's KV buffer holds every layer's K (after RoPE) and V of the
     prefix, [layer][K|V][kv head][token][head_dim]."""
@@ -286,6 +341,21 @@ def test_bf16_two_layer_spellings_and_modes(q15_l2):
         fields += pi.random_spelling_fields(1600 + i, sh.vocab_size, 3, max_labels=8, max_spellings=3,
                                             max_len=3, mode=mode)
     _run_case("q15-L2-spell", sh, w, [(prefix, fields)], dec=dec)
+
+
+def test_bf16_two_layer_prefill_many(q15_l2):
+    """Four prompts of the throughput workload (1024 tokens each) prefilled in
+    one pass at the 1.5B widths, then one branch pass over the four states."""
+    sh, w, dec = q15_l2
+    reqs = _reqs(pi.make_workload("cfg3"))[:4]
+    m = _model(sh, w, reqs, max_prefill=sum(len(p) for p, _ in reqs))
+    states = m.prefill_many([p for p, _ in reqs])
+    got = m.decide_many(states, [f for _, f in reqs], debug=True)
+    ref = opcd.decide(dec, reqs)
+    _compare("q15-L2-prefill-many", got, ref, ref.plan, "bf16")
+    for st in states:
+        st.close()
+    m.close()
 
 
 def test_bf16_two_layer_cfg2_id_field(q15_l2):
