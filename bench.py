@@ -185,6 +185,7 @@ def main():
 
     import constrained_decoding_pcd_amd as cpd
     import pcd_inputs as pi
+    from constrained_decoding_pcd_amd import greedy
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -284,6 +285,20 @@ def main():
             warm[key] = round(float(np.percentile(np.array(lw) * 1e3, 50)), 4)
         head_st.close()
 
+    # The token-by-token baseline on the same kernels: the prefill, then one
+    # decoder pass per output token (every scaffold token and label token of
+    # the 28 fields, each field written after the earlier answers).
+    greedy.decode(model, req.prefix, req.fields[:2])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gd = greedy.decode(model, req.prefix, req.fields)
+    torch.cuda.synchronize()
+    tbt_ms = (time.perf_counter() - t0) * 1e3
+    token_by_token = {"request_ms": round(tbt_ms, 3), "passes": gd.passes, "ms_per_pass": round(tbt_ms / gd.passes, 4),
+                      "pcd_speedup": round(tbt_ms / p50, 1),
+                      "same_answers": int(sum(int(a == b) for a, b in zip(gd.labels, out["argmax"])))}
+    print(f"# token-by-token: {gd.passes} passes, {tbt_ms:.1f} ms", file=sys.stderr, flush=True)
+
     # the same steps again with every kernel launch bracketed by hipEvents on the library's stream
     model.set_kernel_timing(True)
     for _ in range(args.steps):
@@ -330,6 +345,7 @@ def main():
                                                             "launches", "bound")} for c, e in kernels.items()},
         "kernel_timed_ms_per_step": round(timed_ms_per_step, 4),
     }
+    res["token_by_token"] = token_by_token
     if warm is not None:
         res["warm"] = warm
     if args.cpu_layers > 0:

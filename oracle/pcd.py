@@ -241,6 +241,43 @@ def scratch_readouts(dec: Decoder, requests, n_layers: Optional[int] = None):
     return plan, edge, lse
 
 
+def greedy_decode(dec: Decoder, prefix, fields, n_layers: Optional[int] = None):
+    """The token-by-token baseline, from scratch: fields in order, each
+    written after the text so far ([Scratch], "The problem: most of a JSON
+    answer is not an answer").  Scaffold tokens are copied; at each label
+    token the allowed tokens are the next tokens of the spellings that agree
+    with what was written (in first-appearance order), and the one with the
+    largest log p(. | text) is written (ties to the first); a single allowed
+    token is written without a choice.  Stops a field when a spelling is
+    complete.  Returns (label per field, output tokens, output token count)."""
+    text = [int(t) for t in prefix]
+    labels, out = [], []
+    for f in fields:
+        text += [int(t) for t in f.scaffold]
+        out += [int(t) for t in f.scaffold]
+        spells = [(k, list(s)) for k, lab in enumerate(field_spellings(f)) for s in lab]
+        w: List[int] = []
+        while True:
+            live = [(k, s) for k, s in spells if s[:len(w)] == w]
+            done = [k for k, s in live if len(s) == len(w)]
+            if done:
+                labels.append(done[0])
+                break
+            allowed = []
+            for _, s in live:
+                if s[len(w)] not in allowed:
+                    allowed.append(s[len(w)])
+            if len(allowed) == 1:
+                c = allowed[0]
+            else:
+                lp = next_token_logp(dec, text, n_layers)
+                c = max(allowed, key=lambda t: (lp[t], -allowed.index(t)))
+            w.append(c)
+            text.append(c)
+            out.append(c)
+    return labels, out, len(out)
+
+
 def greedy_first_token(dec: Decoder, prefix, field, n_layers: Optional[int] = None) -> int:
     """Brute-force constrained greedy step for one field decided on its own:
     run prefix + scaffold from scratch and take the allowed first token with

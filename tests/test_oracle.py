@@ -319,6 +319,21 @@ def test_exact_mode_scores_every_token(tiny, cfg0t):
     assert np.max(np.abs(ex.fields[0].logscore - np.array(ref))) < 1e-10
 
 
+def test_greedy_decode_is_the_sequential_argmax(tiny, cfg0):
+    """The token-by-token baseline on single-token labels: each field's label
+    is the PCD argmax of that field decided after the prefix plus the earlier
+    fields' scaffolds and answers, and it writes one token per scaffold token
+    and per label token."""
+    prefix, fields = _reqs(cfg0)[0]
+    labels, out, n = opcd.greedy_decode(tiny, prefix, fields)
+    ext = list(prefix)
+    for f, lab in zip(fields, labels):
+        assert lab == opcd.decide(tiny, [(ext, [f])]).fields[0].argmax
+        ext += list(f.scaffold) + list(f.candidates[lab])
+    assert out == ext[len(prefix):]
+    assert n == sum(len(f.scaffold) + 1 for f in fields)
+
+
 def test_sequenced_rest_sees_the_answers(tiny, cfg0t):
     """The first-field round: the remaining fields' scores equal from-scratch
     conditionals after prefix + the first field's scaffold and chosen
