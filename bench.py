@@ -134,7 +134,7 @@ def measured_traffic(cls):
     """HBM bytes per launch of kernel class `cls` from the committed rocprofv3
     counter summary, or None when there is none for it or the kernel source
     has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_cfg1.txt")
+    path = os.path.join(ROOT, "profiles", f"{cls}_cfg1_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -168,6 +168,9 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=28, help="layers of the CPU-oracle sample (0: skip)")
     ap.add_argument("--warm-input", type=int, default=100,
                     help="warm request: the prefix minus this many tokens is a cached head (0: skip)")
+    ap.add_argument("--mode", choices=("both", "single-pass", "two-pass"), default="both",
+                    help="request modes to time; the faster timed mode is the headline")
+    ap.add_argument("--no-token-by-token", action="store_true", help="skip the token-by-token baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -215,7 +218,7 @@ def main():
         st.close()
         return out
 
-    def timed(step):
+    def timed(step, fused):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -230,11 +233,18 @@ def main():
              "p50_request_ms": float(np.percentile(np.array(lat) * 1e3, 50)),
              "p90_request_ms": float(np.percentile(np.array(lat) * 1e3, 90)), "out": out}
         st = model.stats()
+        # the single-pass mode runs no prefill pass: its one pass is the branch pass
         r["phases_ms"] = {k: round(st[f"last_{k}_ms"], 4) for k in ("prefill", "branch", "readout")}
+        if fused:
+            r["phases_ms"] = {"fused": r["phases_ms"]["branch"], "readout": r["phases_ms"]["readout"]}
         return r
 
     nf = len(req.fields)
-    modes = {"two-pass": timed(step_two_pass), "single-pass": timed(step_single_pass)}
+    modes = {}
+    if args.mode in ("both", "two-pass"):
+        modes["two-pass"] = timed(step_two_pass, False)
+    if args.mode in ("both", "single-pass"):
+        modes["single-pass"] = timed(step_single_pass, True)
     mode = min(modes, key=lambda k: modes[k]["ms_per_step"])
     head = modes[mode]
     step, out = (step_single_pass if mode == "single-pass" else step_two_pass), head["out"]
@@ -242,10 +252,7 @@ def main():
     for k, r in modes.items():
         print(f"# {k}: {args.steps} steps: {r['ms_per_step']:.3f} ms/step, p50 {r['p50_request_ms']:.3f} ms, "
               f"p90 {r['p90_request_ms']:.3f} ms", file=sys.stderr, flush=True)
-    if mode == "single-pass":
-        phases = {"fused": head["phases_ms"]["branch"], "readout": head["phases_ms"]["readout"]}
-    else:
-        phases = dict(head["phases_ms"])
+    phases = dict(head["phases_ms"])
     dev_ms = sum(phases.values())
 
     # Warm requests: the prefix's first tokens are a cached head; each request
@@ -288,16 +295,18 @@ def main():
     # The token-by-token baseline on the same kernels: the prefill, then one
     # decoder pass per output token (every scaffold token and label token of
     # the 28 fields, each field written after the earlier answers).
-    greedy.decode(model, req.prefix, req.fields[:2])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    gd = greedy.decode(model, req.prefix, req.fields)
-    torch.cuda.synchronize()
-    tbt_ms = (time.perf_counter() - t0) * 1e3
-    token_by_token = {"request_ms": round(tbt_ms, 3), "passes": gd.passes, "ms_per_pass": round(tbt_ms / gd.passes, 4),
-                      "pcd_speedup": round(tbt_ms / p50, 1),
-                      "same_answers": int(sum(int(a == b) for a, b in zip(gd.labels, out["argmax"])))}
-    print(f"# token-by-token: {gd.passes} passes, {tbt_ms:.1f} ms", file=sys.stderr, flush=True)
+    token_by_token = None
+    if not args.no_token_by_token:
+        greedy.decode(model, req.prefix, req.fields[:2])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gd = greedy.decode(model, req.prefix, req.fields)
+        torch.cuda.synchronize()
+        tbt_ms = (time.perf_counter() - t0) * 1e3
+        token_by_token = {"request_ms": round(tbt_ms, 3), "passes": gd.passes,
+                          "ms_per_pass": round(tbt_ms / gd.passes, 4), "pcd_speedup": round(tbt_ms / p50, 1),
+                          "same_answers": int(sum(int(a == b) for a, b in zip(gd.labels, out["argmax"])))}
+        print(f"# token-by-token: {gd.passes} passes, {tbt_ms:.1f} ms", file=sys.stderr, flush=True)
 
     # the same steps again with every kernel launch bracketed by hipEvents on the library's stream
     model.set_kernel_timing(True)
@@ -345,7 +354,8 @@ def main():
                                                             "launches", "bound")} for c, e in kernels.items()},
         "kernel_timed_ms_per_step": round(timed_ms_per_step, 4),
     }
-    res["token_by_token"] = token_by_token
+    if token_by_token is not None:
+        res["token_by_token"] = token_by_token
     if warm is not None:
         res["warm"] = warm
     if args.cpu_layers > 0:
