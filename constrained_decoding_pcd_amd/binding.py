@@ -164,51 +164,78 @@ def _f32p(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(POINTER(c_float))
 
 
+def _struct_dtype(ctype) -> np.dtype:
+    """NumPy view of a ctypes Structure whose fields are pointers or int32."""
+    names = [n for n, _ in ctype._fields_]
+    fmts = [np.uint64 if issubclass(t, ctypes._Pointer) else np.int32 for _, t in ctype._fields_]
+    offs = [getattr(ctype, n).offset for n in names]
+    return np.dtype({"names": names, "formats": fmts, "offsets": offs, "itemsize": ctypes.sizeof(ctype)})
+
+
+_CAND_DT = _struct_dtype(pcd_candidate)
+_FIELD_DT = _struct_dtype(pcd_field)
+
+
 class _Marshalled:
     """C view of requests: lists of fields, each with .scaffold and
-    .candidates (token-id sequences).  Keeps the NumPy buffers alive."""
+    .candidates (token-id sequences), optionally .spellings and .mode.  Per
+    request, every token id goes into one int32 buffer and the pcd_field /
+    pcd_candidate arrays are filled in bulk through NumPy views of them.
+    Keeps the buffers alive."""
 
     def __init__(self, requests: Sequence[Sequence]):
         self.keep = []
         self.reqs = (pcd_request * len(requests))()
         self.n_cands, self.n_fields = [], []
         for r, fields in enumerate(requests):
-            # per label: None (one spelling: the candidate) or its list of spellings
-            labels = []
+            flat: List[int] = []              # scaffolds, then candidate tokens
+            spl: List[int] = []               # spelling lengths
+            f_off, f_len, c_off, c_len, s_off, s_n = [], [], [], [], [], []
+            for f in fields:
+                f_off.append(len(flat))
+                f_len.append(len(f.scaffold))
+                flat += f.scaffold
             for f in fields:
                 sp = getattr(f, "spellings", None)
-                labels += [(c, None if sp is None else sp[k]) for k, c in enumerate(f.candidates)]
-            ca = (pcd_candidate * max(1, len(labels)))()
+                for k, c in enumerate(f.candidates):
+                    c_off.append(len(flat))
+                    if sp is None:
+                        flat += c
+                        c_len.append(len(c))
+                        s_off.append(-1)
+                        s_n.append(0)
+                    else:
+                        n0 = len(flat)
+                        for x in sp[k]:
+                            flat += x
+                        c_len.append(len(flat) - n0)
+                        s_off.append(len(spl))
+                        s_n.append(len(sp[k]))
+                        spl += [len(x) for x in sp[k]]
+            tok = np.ascontiguousarray(flat, dtype=np.int32)
+            sl = np.ascontiguousarray(spl, dtype=np.int32)
+            ca = (pcd_candidate * max(1, len(c_off)))()
             fa = (pcd_field * max(1, len(fields)))()
-            off = 0
-            for i, (c, spell) in enumerate(labels):
-                if spell is None:
-                    a = np.ascontiguousarray(c, dtype=np.int32)
-                else:
-                    a = np.ascontiguousarray([t for x in spell for t in x], dtype=np.int32)
-                    ln = np.ascontiguousarray([len(x) for x in spell], dtype=np.int32)
-                    self.keep.append(ln)
-                    ca[i].spell_len = _i32p(ln)
-                    ca[i].n_spellings = ln.size
-                self.keep.append(a)
-                ca[i].tokens = _i32p(a)
-                ca[i].n_tokens = a.size
-            for i, f in enumerate(fields):
-                s = np.ascontiguousarray(f.scaffold, dtype=np.int32)
-                self.keep.append(s)
-                fa[i].scaffold = _i32p(s)
-                fa[i].n_scaffold = s.size
-                fa[i].cand_offset = off
-                fa[i].n_cands = len(f.candidates)
-                mode = getattr(f, "mode", None) or "path"
-                fa[i].score_mode = SCORE_MODES.get(mode, -1)
-                off += len(f.candidates)
-            self.keep += [ca, fa]
+            tb, sb = tok.ctypes.data, sl.ctypes.data
+            cv = np.frombuffer(ca, dtype=_CAND_DT)[:len(c_off)]
+            cv["tokens"] = tb + 4 * np.asarray(c_off, dtype=np.uint64)
+            cv["n_tokens"] = c_len
+            so = np.asarray(s_off, dtype=np.int64)
+            cv["spell_len"] = np.where(so >= 0, sb + 4 * np.maximum(so, 0), 0).astype(np.uint64)
+            cv["n_spellings"] = s_n
+            fv = np.frombuffer(fa, dtype=_FIELD_DT)[:len(fields)]
+            fv["scaffold"] = tb + 4 * np.asarray(f_off, dtype=np.uint64)
+            fv["n_scaffold"] = f_len
+            nc = [len(f.candidates) for f in fields]
+            fv["cand_offset"] = np.cumsum([0] + nc[:-1]) if fields else []
+            fv["n_cands"] = nc
+            fv["score_mode"] = [SCORE_MODES.get(getattr(f, "mode", None) or "path", -1) for f in fields]
+            self.keep += [tok, sl, ca, fa]
             self.reqs[r].fields = fa
             self.reqs[r].n_fields = len(fields)
             self.reqs[r].candidates = ca
-            self.reqs[r].n_candidates = len(labels)
-            self.n_cands.append(len(labels))
+            self.reqs[r].n_candidates = len(c_off)
+            self.n_cands.append(len(c_off))
             self.n_fields.append(len(fields))
 
 

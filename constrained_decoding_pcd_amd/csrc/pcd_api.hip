@@ -37,9 +37,12 @@ constexpr uint64_t STATE_MAGIC = 0x70636473746174ull;
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
-// Attention workgroups per launch that keep every compute unit busy (two
-// per unit), and the shortest key range worth a workgroup of its own.
-constexpr int ATT_TARGET_BLOCKS = 512;
+// Attention workgroups per launch (about one per compute unit: more splits
+// cost more in partial writes and the merge than they gain in parallelism;
+// measured on the 1.5B shape, 256 beats 512 and 1024 on the single-pass
+// request and ties on the two-pass one), and the shortest key range worth a
+// workgroup of its own.
+constexpr int ATT_TARGET_BLOCKS = 256;
 constexpr int ATT_MIN_SPLIT_TILES = 2;  // 64-key tiles
 // Key splits of a row block: enough for `row_blocks` blocks to reach the
 // target count, no split shorter than the minimum, at most MAX_SPLITS.
