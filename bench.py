@@ -323,6 +323,39 @@ def main():
     if traffic is not None:
         kernels[dominant]["traffic"] = traffic
     timed_ms_per_step = sum(ms for ms, _ in kt.values()) / args.steps
+    # Phase rooflines (hipEvent phase times of the timed steps): the branch
+    # pass against HBM (every weight matrix, the prefix K/V read once, the
+    # branch K/V and activations), prefill and the single pass against
+    # MFMA, the readout against HBM (the LM head).
+    def phase_roofline():
+        out = {}
+        e = 2 if sh.dtype == "bf16" else 4
+        P = len(req.prefix)
+        w_bytes = float(sum(work[c][1] for c in ("branch_qkv", "branch_o", "branch_gateup", "branch_down")))
+        kv_tok = sh.n_layers * 2 * sh.n_kv_heads * sh.head_dim * e
+        br_bytes = w_bytes * sh.n_layers + P * kv_tok + Tb * kv_tok
+        pf_flops = sum(work[c][0] for c in ("prefill_qkv", "prefill_o", "prefill_gateup", "prefill_down",
+                                            "prefill_attn")) * sh.n_layers
+        fu_flops = sum(work[c][0] for c in ("fused_qkv", "fused_o", "fused_gateup", "fused_down",
+                                            "fused_attn")) * sh.n_layers
+        ro_bytes = float(work["readout_lmhead"][1])
+        if "two-pass" in modes:
+            ph = modes["two-pass"]["phases_ms"]
+            out["branch_pass"] = {"ms": ph["branch"], "bytes": br_bytes,
+                                  "GB/s": round(br_bytes / ph["branch"] / 1e6, 1),
+                                  "hbm_frac": round(br_bytes / ph["branch"] / 1e6 / HBM_PEAK_GBS, 4)}
+            out["prefill"] = {"ms": ph["prefill"], "flops": pf_flops,
+                              "TFLOP/s": round(pf_flops / ph["prefill"] / 1e9, 1),
+                              "mfma_frac": round(pf_flops / ph["prefill"] / 1e9 / peak_mfma, 4)}
+        if "single-pass" in modes:
+            ph = modes["single-pass"]["phases_ms"]
+            out["single_pass"] = {"ms": ph["fused"], "flops": fu_flops,
+                                  "TFLOP/s": round(fu_flops / ph["fused"] / 1e9, 1),
+                                  "mfma_frac": round(fu_flops / ph["fused"] / 1e9 / peak_mfma, 4)}
+        ro = head["phases_ms"]["readout"]
+        out["readout"] = {"ms": ro, "bytes": ro_bytes, "GB/s": round(ro_bytes / ro / 1e6, 1),
+                          "hbm_frac": round(ro_bytes / ro / 1e6 / HBM_PEAK_GBS, 4)}
+        return out
     res = {
         "metric": "schema fields decided/sec + p50 28-field request ms, 1.5B-shaped bf16",
         "value": round(nf / (ms_per_step / 1e3), 2),
@@ -350,6 +383,7 @@ def main():
         "modes": {k: {"ms_per_step": round(r["ms_per_step"], 4), "p50_request_ms": round(r["p50_request_ms"], 4),
                       "phases_ms": r["phases_ms"]} for k, r in modes.items()},
         "roofline": kernels[dominant],
+        "phase_roofline": phase_roofline(),
         "kernels": {c: {k: v for k, v in e.items() if k in ("achieved", "unit", "frac", "avg_launch_us",
                                                             "launches", "bound")} for c, e in kernels.items()},
         "kernel_timed_ms_per_step": round(timed_ms_per_step, 4),
