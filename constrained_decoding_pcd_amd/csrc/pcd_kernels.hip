@@ -294,52 +294,75 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
             for (int j = 0; j < FN; ++j)
                 frag(fb[bb][q][j], st + A_BYTES + q * B_BYTES, wn * WTN + j * 16 + lr, s * 4 * CPL + lg * CPL);
     };
-    auto mfmas = [&](auto BUF) {
-        constexpr int bb = decltype(BUF)::value;
+    // matrix instructions [lo, hi) of one k-step, in (q, j, i) order
+    constexpr int NM = NB * FN * FM;
+    auto mfmas = [&](auto BUF, auto LO, auto HI) {
+        constexpr int bb = decltype(BUF)::value, lo = decltype(LO)::value, hi = decltype(HI)::value;
 #pragma unroll
         for (int q = 0; q < NB; ++q)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int i = 0; i < FM; ++i) mma(acc[q][i][j], fa[bb][i], fb[bb][q][j]);
-    };
-    // wait until stage `next` has landed; the stages issued after it may stay in
-    // flight: S-1 of them before the loop, S-2 inside it (stage next+S-1 is
-    // issued only after this wait)
-    auto wait_stage = [&](int next) {
-        const int ahead = min(next == 0 ? S - 1 : S - 2, nkt - 1 - next);
-        vm_wait_ahead<LPS, S - 1>(ahead);
+                for (int i = 0; i < FM; ++i) {
+                    const int idx = (q * FN + j) * FM + i;
+                    if (idx >= lo && idx < hi) mma(acc[q][i][j], fa[bb][i], fb[bb][q][j]);
+                }
     };
     static_assert(KSTEPS % 2 == 0, "k-steps per stage must be even for the fragment ping-pong");
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
+    using M0 = std::integral_constant<int, 0>;
+    using MH = std::integral_constant<int, NM / 4>;
+    using MN = std::integral_constant<int, NM>;
+
+    // One stage, k-steps in pairs: buffer 0 computes while buffer 1 loads and
+    // the reverse.  The order within a pair is pinned (sched_barrier): a
+    // quarter of buffer 0's matrix instructions, the LDS reads of buffer 1,
+    // the rest of buffer 0, then (after the stage's last k-step) the refill
+    // of the slot just consumed, the reads of the next stage's first k-step,
+    // and buffer 1's matrix instructions.  So no wait ever covers reads issued
+    // for a later k-step, and each read has a run of matrix instructions to
+    // land behind.  KIND 0: S-2 later stages in flight, refill stage kt+S;
+    // KIND 1 (the last stages): wait for everything, no refill; KIND 2: the
+    // final stage, nothing follows.
+    auto stage = [&](int kt, auto KIND) {
+        constexpr int kind = decltype(KIND)::value;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; s += 2) {
+            mfmas(B0{}, M0{}, MH{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(B1{}, kt, s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(B0{}, MH{}, MN{});
+            if (s + 2 < KSTEPS) {
+                read_frags(B0{}, kt, s + 2);
+            } else if constexpr (kind != 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                // this wave's reads of stage kt must be done before anyone refills its slot
+                lds_reads_done();
+                if constexpr (kind == 0) vm_wait<(S - 2) * LPS>();
+                else vm_wait<0>();
+                barrier_keep_loads();
+                if constexpr (kind == 0) issue(kt + S);
+                read_frags(B0{}, kt + 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(B1{}, M0{}, MN{});
+        }
+    };
 
 #pragma unroll
     for (int s = 0; s < S; ++s)
         if (s < nkt) issue(s);
-    wait_stage(0);
+    // stage 0 landed; the S-1 stages issued after it may stay in flight
+    if (nkt >= S) vm_wait<(S - 1) * LPS>();
+    else vm_wait<0>();
     barrier_keep_loads();
     read_frags(B0{}, 0, 0);
-    for (int kt = 0; kt < nkt; ++kt) {
-#pragma unroll
-        for (int s = 0; s < KSTEPS; s += 2) {
-            // even k-step: compute buffer 0 while buffer 1 loads
-            read_frags(B1{}, kt, s + 1);
-            mfmas(B0{});
-            // odd k-step: compute buffer 1 while buffer 0 loads (possibly from the next stage)
-            if (s + 2 < KSTEPS) {
-                read_frags(B0{}, kt, s + 2);
-            } else if (kt + 1 < nkt) {
-                // this wave's reads of stage kt must be done before anyone refills its slot
-                lds_reads_done();
-                wait_stage(kt + 1);
-                barrier_keep_loads();
-                if (kt + S < nkt) issue(kt + S);
-                read_frags(B0{}, kt + 1, 0);
-            }
-            mfmas(B1{});
-        }
-    }
+    int kt = 0;
+    for (; kt + S < nkt; ++kt) stage(kt, std::integral_constant<int, 0>{});
+    for (; kt + 1 < nkt; ++kt) stage(kt, std::integral_constant<int, 1>{});
+    stage(kt, std::integral_constant<int, 2>{});
 
     if constexpr (!LDS_EPI) {
 #pragma unroll
