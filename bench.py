@@ -10,6 +10,7 @@ the roofline position of the dominant kernel (timed live with hipEvents on
 the library's stream) and the CPU oracle timed on a bounded sample.
 """
 import argparse
+import gc
 import json
 import os
 import sys
@@ -223,15 +224,19 @@ def main():
             step()
         torch.cuda.synchronize()
         lat = []
+        gc.collect()
+        gc.disable()  # no collector pause inside the timed steps
         t0 = time.perf_counter()
         for _ in range(args.steps):
             s0 = time.perf_counter()
             out = step()
             lat.append(time.perf_counter() - s0)
         torch.cuda.synchronize()
+        gc.enable()
         r = {"ms_per_step": (time.perf_counter() - t0) / args.steps * 1e3,
              "p50_request_ms": float(np.percentile(np.array(lat) * 1e3, 50)),
-             "p90_request_ms": float(np.percentile(np.array(lat) * 1e3, 90)), "out": out}
+             "p90_request_ms": float(np.percentile(np.array(lat) * 1e3, 90)), "out": out,
+             "max_request_ms": float(np.max(lat) * 1e3), "slowest_step": int(np.argmax(lat))}
         st = model.stats()
         # the single-pass mode runs no prefill pass: its one pass is the branch pass
         r["phases_ms"] = {k: round(st[f"last_{k}_ms"], 4) for k in ("prefill", "branch", "readout")}
@@ -382,6 +387,7 @@ def main():
                        token_by_token_equivalent=int(sum(len(f.scaffold) + len(f.candidates[int(a)])
                                                          for f, a in zip(req.fields, out["argmax"])))),
         "modes": {k: {"ms_per_step": round(r["ms_per_step"], 4), "p50_request_ms": round(r["p50_request_ms"], 4),
+                      "max_request_ms": round(r["max_request_ms"], 4), "slowest_step": r["slowest_step"],
                       "phases_ms": r["phases_ms"]} for k, r in modes.items()},
         "roofline": kernels[dominant],
         "phase_roofline": phase_roofline(),
