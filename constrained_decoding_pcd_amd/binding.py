@@ -8,6 +8,7 @@ library.  It fails loudly when the library has not been built.
 from __future__ import annotations
 
 import ctypes
+from itertools import chain
 import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
 from typing import Dict, List, Optional, Sequence
@@ -164,79 +165,72 @@ def _f32p(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(POINTER(c_float))
 
 
-def _struct_dtype(ctype) -> np.dtype:
-    """NumPy view of a ctypes Structure whose fields are pointers or int32."""
-    names = [n for n, _ in ctype._fields_]
-    fmts = [np.uint64 if issubclass(t, ctypes._Pointer) else np.int32 for _, t in ctype._fields_]
-    offs = [getattr(ctype, n).offset for n in names]
-    return np.dtype({"names": names, "formats": fmts, "offsets": offs, "itemsize": ctypes.sizeof(ctype)})
-
-
-_CAND_DT = _struct_dtype(pcd_candidate)
-_FIELD_DT = _struct_dtype(pcd_field)
+# the 64-bit word layouts _Marshalled writes (x86-64 / little-endian ABI)
+assert ctypes.sizeof(pcd_candidate) == 32 and pcd_candidate.spell_len.offset == 16
+assert ctypes.sizeof(pcd_field) == 24 and pcd_field.cand_offset.offset == 12 and pcd_field.score_mode.offset == 20
 
 
 class _Marshalled:
     """C view of requests: lists of fields, each with .scaffold and
     .candidates (token-id sequences), optionally .spellings and .mode.  Per
-    request, every token id goes into one int32 buffer and the pcd_field /
-    pcd_candidate arrays are filled in bulk through NumPy views of them.
-    Keeps the buffers alive."""
+    request, every token id goes into one int32 buffer, and the pcd_field /
+    pcd_candidate arrays are NumPy structured arrays that ctypes views
+    without a copy.  Keeps the buffers alive."""
 
     def __init__(self, requests: Sequence[Sequence]):
         self.keep = []
         self.reqs = (pcd_request * len(requests))()
         self.n_cands, self.n_fields = [], []
         for r, fields in enumerate(requests):
-            flat: List[int] = []              # scaffolds, then candidate tokens
-            spl: List[int] = []               # spelling lengths
-            f_off, f_len, c_off, c_len, s_off, s_n = [], [], [], [], [], []
-            for f in fields:
-                f_off.append(len(flat))
-                f_len.append(len(f.scaffold))
-                flat += f.scaffold
-            for f in fields:
-                sp = getattr(f, "spellings", None)
-                for k, c in enumerate(f.candidates):
-                    c_off.append(len(flat))
-                    if sp is None:
-                        flat += c
-                        c_len.append(len(c))
-                        s_off.append(-1)
-                        s_n.append(0)
-                    else:
-                        n0 = len(flat)
-                        for x in sp[k]:
-                            flat += x
-                        c_len.append(len(flat) - n0)
+            nf = len(fields)
+            spelled = [getattr(f, "spellings", None) for f in fields]
+            # token lists: every scaffold, then every candidate (its spellings back to back)
+            cand_lists, spl, s_off, s_n = [], [], [], []
+            for f, sp in zip(fields, spelled):
+                if sp is None:
+                    cand_lists += f.candidates
+                    s_off += [-1] * len(f.candidates)
+                    s_n += [0] * len(f.candidates)
+                else:
+                    for lab in sp:
+                        cand_lists.append(list(chain.from_iterable(lab)))
                         s_off.append(len(spl))
-                        s_n.append(len(sp[k]))
-                        spl += [len(x) for x in sp[k]]
-            tok = np.ascontiguousarray(flat, dtype=np.int32)
-            sl = np.ascontiguousarray(spl, dtype=np.int32)
-            ca = (pcd_candidate * max(1, len(c_off)))()
-            fa = (pcd_field * max(1, len(fields)))()
+                        s_n.append(len(lab))
+                        spl += map(len, lab)
+            scaf = [f.scaffold for f in fields]
+            nc = len(cand_lists)
+            lens = np.fromiter(map(len, chain(scaf, cand_lists)), dtype=np.int64, count=nf + nc)
+            offs = np.zeros(nf + nc, dtype=np.int64)
+            np.cumsum(lens[:-1], out=offs[1:])
+            tok = np.fromiter(chain.from_iterable(chain(scaf, cand_lists)), dtype=np.int32, count=int(lens.sum()))
+            sl = np.asarray(spl, dtype=np.int32)
             tb, sb = tok.ctypes.data, sl.ctypes.data
-            cv = np.frombuffer(ca, dtype=_CAND_DT)[:len(c_off)]
-            cv["tokens"] = tb + 4 * np.asarray(c_off, dtype=np.uint64)
-            cv["n_tokens"] = c_len
+            # pcd_candidate is 4 little-endian 64-bit words: tokens, n_tokens, spell_len, n_spellings;
+            # pcd_field is 3: scaffold, n_scaffold | cand_offset << 32, n_cands | score_mode << 32
+            cv = np.zeros((max(1, nc), 4), dtype=np.int64)
+            cv[:nc, 0] = tb + 4 * offs[nf:]
+            cv[:nc, 1] = lens[nf:]
             so = np.asarray(s_off, dtype=np.int64)
-            cv["spell_len"] = np.where(so >= 0, sb + 4 * np.maximum(so, 0), 0).astype(np.uint64)
-            cv["n_spellings"] = s_n
-            fv = np.frombuffer(fa, dtype=_FIELD_DT)[:len(fields)]
-            fv["scaffold"] = tb + 4 * np.asarray(f_off, dtype=np.uint64)
-            fv["n_scaffold"] = f_len
-            nc = [len(f.candidates) for f in fields]
-            fv["cand_offset"] = np.cumsum([0] + nc[:-1]) if fields else []
-            fv["n_cands"] = nc
-            fv["score_mode"] = [SCORE_MODES.get(getattr(f, "mode", None) or "path", -1) for f in fields]
-            self.keep += [tok, sl, ca, fa]
+            cv[:nc, 2] = np.where(so >= 0, sb + 4 * so, 0)
+            cv[:nc, 3] = s_n
+            fv = np.zeros((max(1, nf), 3), dtype=np.int64)
+            fv[:nf, 0] = tb + 4 * offs[:nf]
+            ncf = np.fromiter((len(f.candidates) for f in fields), dtype=np.int64, count=nf)
+            c_first = np.zeros(nf, dtype=np.int64)
+            np.cumsum(ncf[:-1], out=c_first[1:])
+            fv[:nf, 1] = lens[:nf] | (c_first << 32)
+            modes = np.asarray([SCORE_MODES.get(getattr(f, "mode", None) or "path", -1) for f in fields],
+                               dtype=np.int64)
+            fv[:nf, 2] = ncf | ((modes & 0xFFFFFFFF) << 32)
+            ca = (pcd_candidate * len(cv)).from_buffer(cv)
+            fa = (pcd_field * len(fv)).from_buffer(fv)
+            self.keep += [tok, sl, cv, fv, ca, fa]
             self.reqs[r].fields = fa
-            self.reqs[r].n_fields = len(fields)
+            self.reqs[r].n_fields = nf
             self.reqs[r].candidates = ca
-            self.reqs[r].n_candidates = len(c_off)
-            self.n_cands.append(len(c_off))
-            self.n_fields.append(len(fields))
+            self.reqs[r].n_candidates = nc
+            self.n_cands.append(nc)
+            self.n_fields.append(nf)
 
 
 def debug_plan(vocab_size: int, max_seq: int, prefix_lens: Sequence[int], requests) -> Dict[str, np.ndarray]:
