@@ -785,7 +785,7 @@ int pcd_debug_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *pre
     if (!info) return fail(PCD_E_ARG, "null info");
     Plan p;
     std::string err;
-    int rc = build_plan(V, max_seq, n_req, prefix_lens, reqs, p, err);
+    int rc = build_plan(V, max_seq, n_req, prefix_lens, reqs, p, err, true);
     if (rc != PCD_OK) return fail(rc, err);
     info->n_branch = (int32_t)p.tok.size();
     info->n_readouts = (int32_t)p.ro_tok.size();

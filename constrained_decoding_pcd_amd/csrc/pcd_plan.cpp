@@ -4,7 +4,6 @@
 
 #include <algorithm>
 #include <cstdio>
-#include <set>
 
 namespace pcd {
 
@@ -46,6 +45,8 @@ int validate(const pcd_field &f, const pcd_candidate *cands, int32_t V, std::vec
     }
     sp.clear();
     n_spell.clear();
+    sp.reserve(f.n_cands);
+    n_spell.reserve(f.n_cands);
     for (int c = 0; c < f.n_cands; ++c) {
         const pcd_candidate &k = cands[c];
         if (k.n_tokens < 0 || (k.n_tokens > 0 && !k.tokens)) { err = "null candidate tokens"; return PCD_E_ARG; }
@@ -91,17 +92,25 @@ int validate(const pcd_field &f, const pcd_candidate *cands, int32_t V, std::vec
             }
     for (const Spell &s : sp)
         if (s.n <= 0) { err = "empty candidate"; return PCD_E_EMPTY; }
-    std::set<std::vector<int32_t>> seen;
-    for (const Spell &s : sp) {
-        std::vector<int32_t> sq(s.tok, s.tok + s.n);
-        if (!seen.insert(sq).second) { err = fmt("duplicate candidate (%ld tokens)", (long)sq.size()); return PCD_E_DUP; }
+    // spellings in lexicographic order: a duplicate sits next to its twin, and a
+    // proper prefix right before some extension of it
+    std::vector<int32_t> ord(sp.size());
+    for (size_t i = 0; i < ord.size(); ++i) ord[i] = (int32_t)i;
+    auto less = [&](int32_t x, int32_t y) {
+        return std::lexicographical_compare(sp[x].tok, sp[x].tok + sp[x].n, sp[y].tok, sp[y].tok + sp[y].n);
+    };
+    std::sort(ord.begin(), ord.end(), less);
+    for (size_t i = 1; i < ord.size(); ++i) {
+        const Spell &a = sp[ord[i - 1]], &b = sp[ord[i]];
+        if (a.n == b.n && std::equal(a.tok, a.tok + a.n, b.tok)) {
+            err = fmt("duplicate candidate (%ld tokens)", (long)a.n);
+            return PCD_E_DUP;
+        }
     }
-    std::vector<std::vector<int32_t>> sorted(seen.begin(), seen.end());
-    // in lexicographic order a proper prefix sorts right before some extension of it
-    for (size_t i = 1; i < sorted.size(); ++i) {
-        const auto &a = sorted[i - 1], &b = sorted[i];
-        if (a.size() < b.size() && std::equal(a.begin(), a.end(), b.begin())) {
-            err = fmt("a candidate of %ld tokens is a proper prefix of one of %ld", (long)a.size(), (long)b.size());
+    for (size_t i = 1; i < ord.size(); ++i) {
+        const Spell &a = sp[ord[i - 1]], &b = sp[ord[i]];
+        if (a.n < b.n && std::equal(a.tok, a.tok + a.n, b.tok)) {
+            err = fmt("a candidate of %ld tokens is a proper prefix of one of %ld", (long)a.n, (long)b.n);
             return PCD_E_PREFIX;
         }
     }
@@ -150,7 +159,7 @@ std::vector<Node> make_trie(const std::vector<Spell> &sp) {
 }  // namespace
 
 int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_lens, const pcd_request *reqs,
-               Plan &p, std::string &err) {
+               Plan &p, std::string &err, bool with_anc) {
     p = Plan();
     if (n_req <= 0 || !prefix_lens || !reqs) { err = "no requests"; return PCD_E_ARG; }
     p.n_req = n_req;
@@ -207,8 +216,10 @@ int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_
                 p.fs.push_back(base);
                 p.nsc.push_back(ns);
                 p.par.push_back(-1);
-                for (int a = base; a <= base + j; ++a) p.anc.push_back(a);
-                p.anc_off.push_back((int32_t)p.anc.size());
+                if (with_anc) {
+                    for (int a = base; a <= base + j; ++a) p.anc.push_back(a);
+                    p.anc_off.push_back((int32_t)p.anc.size());
+                }
             }
             // continuation tokens: non-root readout nodes, BFS order
             std::vector<int32_t> branch_of(t.size(), -1), ro_of(t.size(), -1);
@@ -230,12 +241,14 @@ int build_plan(int32_t V, int32_t max_seq, int32_t n_req, const int32_t *prefix_
                 p.fs.push_back(base);
                 p.nsc.push_back(ns);
                 p.par.push_back(t[v].parent == 0 ? -1 : branch_of[t[v].parent]);
-                std::vector<int32_t> chain;
-                for (int a = (int)v; a != 0; a = t[a].parent) chain.push_back(branch_of[a]);
-                for (int a = base; a < base + ns; ++a) p.anc.push_back(a);
-                std::sort(chain.begin(), chain.end());
-                p.anc.insert(p.anc.end(), chain.begin(), chain.end());
-                p.anc_off.push_back((int32_t)p.anc.size());
+                if (with_anc) {
+                    std::vector<int32_t> chain;
+                    for (int a = (int)v; a != 0; a = t[a].parent) chain.push_back(branch_of[a]);
+                    for (int a = base; a < base + ns; ++a) p.anc.push_back(a);
+                    std::sort(chain.begin(), chain.end());
+                    p.anc.insert(p.anc.end(), chain.begin(), chain.end());
+                    p.anc_off.push_back((int32_t)p.anc.size());
+                }
             }
             // readouts (root first, then BFS) and the child tokens gathered at each
             std::vector<int32_t> g_first(t.size(), -1);

@@ -55,8 +55,9 @@ struct Plan {
 };
 
 // Validates and lays out the requests.  Returns PCD_OK or a PCD_E_* code with
-// a message in err.
+// a message in err.  The visibility lists anc_off/anc (a debug view) are
+// filled only when with_anc is set.
 int build_plan(int32_t vocab_size, int32_t max_seq, int32_t n_req, const int32_t *prefix_lens,
-               const pcd_request *reqs, Plan &out, std::string &err);
+               const pcd_request *reqs, Plan &out, std::string &err, bool with_anc = false);
 
 }  // namespace pcd
