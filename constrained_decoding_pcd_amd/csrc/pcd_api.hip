@@ -29,7 +29,7 @@ int fail(int code, const std::string &msg) {
         if (e_ != hipSuccess) return fail(PCD_E_DEVICE, std::string(#expr ": ") + hipGetErrorString(e_)); \
     } while (0)
 
-constexpr int MAX_SPLITS = 8;         // key splits of one attention row block
+constexpr int MAX_SPLITS = ATT_MAX_SPLITS;  // key splits of one attention row block
 constexpr int ATT_ROWS = 64;          // query rows per attention workgroup
 constexpr int SPLITK_MAX = 8;
 constexpr int SPLITK_ROWS = 1024;     // split-K is only used below this many rows

@@ -108,6 +108,10 @@ struct AttnCall {
 };
 bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
 
+// Key splits of one attention row block at most (the merge kernel holds
+// every split of a (token, head) in registers).
+constexpr int ATT_MAX_SPLITS = 8;
+
 // Merge the split partials of each (token, head) whose request used more
 // than one split.
 struct TailCall {

@@ -1419,7 +1419,9 @@ bool attention(const AttnCall &c, hipStream_t st) {
 
 // Merge the split partials of each (token, head) of the requests that used
 // more than one split: m = max, l = sum l_s 2^(m_s - m), O = sum O_s 2^(m_s - m).
-template <typename T, int HD>
+// Every split's loads go out before the first is used (one memory round trip
+// per (token, head) rather than one per split); SMAX bounds the split count.
+template <typename T, int HD, int SMAX>
 __global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
     constexpr int PL = (HD + 63) / 64;
     const int lane = threadIdx.x & 63;
@@ -1429,20 +1431,30 @@ __global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
     const int t = id / Hq, h = id % Hq;
     const int ns = c.tok_splits[t];
     if (ns <= 1) return;  // written directly by the attention kernel
-    float m = -INFINITY, l = 0.f, o[PL];
+    float2 ml[SMAX];
+    float po[SMAX][PL];
 #pragma unroll
-    for (int i = 0; i < PL; ++i) o[i] = 0.f;
-    for (int s = 0; s < ns; ++s) {
+    for (int s = 0; s < SMAX; ++s) {
+        if (s >= ns) break;
         const size_t pi = ((size_t)s * c.n_tokens + t) * Hq + h;
-        const float2 ml = c.part_ml[pi];
-        const float mn = fmaxf(m, ml.x);
-        const float a = __builtin_amdgcn_exp2f(m - mn), b = __builtin_amdgcn_exp2f(ml.x - mn);
+        ml[s] = c.part_ml[pi];
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
             const int d = lane + 64 * i;
-            if (d < HD) o[i] = o[i] * a + c.part_o[pi * HD + d] * b;
+            po[s][i] = d < HD ? c.part_o[pi * HD + d] : 0.f;
         }
-        l = l * a + ml.y * b;
+    }
+    float m = -INFINITY, l = 0.f, o[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+        if (s >= ns) break;
+        const float mn = fmaxf(m, ml[s].x);
+        const float a = __builtin_amdgcn_exp2f(m - mn), b = __builtin_amdgcn_exp2f(ml[s].x - mn);
+#pragma unroll
+        for (int i = 0; i < PL; ++i) o[i] = o[i] * a + po[s][i] * b;
+        l = l * a + ml[s].y * b;
         m = mn;
     }
     T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD;
@@ -1459,9 +1471,9 @@ template <typename T> static void merge_t(const TailCall &c, hipStream_t st) {
     if (waves <= 0) return;
     const dim3 grid((waves + 3) / 4);
     switch (c.hd) {
-        case 32: hipLaunchKernelGGL((k_attn_merge<T, 32>), grid, dim3(256), 0, st, c); break;
-        case 64: hipLaunchKernelGGL((k_attn_merge<T, 64>), grid, dim3(256), 0, st, c); break;
-        case 128: hipLaunchKernelGGL((k_attn_merge<T, 128>), grid, dim3(256), 0, st, c); break;
+        case 32: hipLaunchKernelGGL((k_attn_merge<T, 32, ATT_MAX_SPLITS>), grid, dim3(256), 0, st, c); break;
+        case 64: hipLaunchKernelGGL((k_attn_merge<T, 64, ATT_MAX_SPLITS>), grid, dim3(256), 0, st, c); break;
+        case 128: hipLaunchKernelGGL((k_attn_merge<T, 128, ATT_MAX_SPLITS>), grid, dim3(256), 0, st, c); break;
     }
 }
 void attention_merge(const TailCall &c, hipStream_t st) {
