@@ -182,6 +182,14 @@ class _Marshalled:
         self.reqs = (pcd_request * len(requests))()
         self.n_cands, self.n_fields = [], []
         for r, fields in enumerate(requests):
+            if isinstance(fields, CompiledFields):
+                # already marshalled: share its arrays
+                src = fields.m
+                self.keep.append(src)
+                self.reqs[r] = src.reqs[0]
+                self.n_cands.append(src.n_cands[0])
+                self.n_fields.append(src.n_fields[0])
+                continue
             nf = len(fields)
             spelled = [getattr(f, "spellings", None) for f in fields]
             # token lists: every scaffold, then every candidate (its spellings back to back)
@@ -231,6 +239,27 @@ class _Marshalled:
             self.reqs[r].n_candidates = nc
             self.n_cands.append(nc)
             self.n_fields.append(nf)
+
+
+class CompiledFields:
+    """A schema (list of fields) marshalled once into the C arrays the
+    library reads, for reuse across requests: every decide call accepts it in
+    place of the field list.  The library still validates the fields and
+    builds the plan on every call; only the Python-to-C conversion is saved.
+    The fields must not change while it is in use."""
+
+    def __init__(self, fields: Sequence):
+        self.fields = list(fields)
+        self.m = _Marshalled([self.fields])
+
+    def __len__(self):
+        return len(self.fields)
+
+    def __iter__(self):
+        return iter(self.fields)
+
+    def __getitem__(self, i):
+        return self.fields[i]
 
 
 def debug_plan(vocab_size: int, max_seq: int, prefix_lens: Sequence[int], requests) -> Dict[str, np.ndarray]:
@@ -390,6 +419,11 @@ class PcdModel:
         _check(self.lib.pcd_prefill_many(self.handle, n, _i32p(toks), _i32p(lens), bufs, sizes,
                                          _stream_handle(torch), hs))
         return [PcdState(self, c_void_p(hs[i]), kvs[i], int(lens[i])) for i in range(n)]
+
+    @staticmethod
+    def compile_fields(fields) -> CompiledFields:
+        """Marshal a schema once for repeated decide calls."""
+        return CompiledFields(fields)
 
     def decide(self, state: PcdState, fields, temperature: float = 1.0, debug: bool = False) -> dict:
         return self.decide_many([state], [fields], temperature, debug)[0]

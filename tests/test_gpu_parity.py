@@ -384,3 +384,43 @@ def test_bf16_two_layer_deep_chains(q15_l2):
         reqs.append((prefix, _deep_chain_fields(920 + k, sh.vocab_size) +
                      pi.random_trie_fields(930 + k, sh.vocab_size, 2, max_len=6)))
     _run_case("q15-L2-deep", sh, w, reqs, dec=dec)
+
+
+def test_tiny_compiled_fields_match_lists(tiny_w):
+    """Every decide path gives bit-identical results whether it is handed the
+    field list or the same schema marshalled once."""
+    V = pi.SHAPES["tiny"].vocab_size
+    rng = np.random.default_rng(77)
+    prefix = [int(t) for t in rng.integers(0, V, size=50)]
+    fields = pi.random_spelling_fields(7700, V, 3, max_labels=5, max_spellings=3, max_len=3, mode="exact")
+    fields += pi.random_trie_fields(7701, V, 2, max_cands=8, max_len=3)
+    print("case tiny-compiled: prefix 50", flush=True)
+    sh = pi.SHAPES["tiny"]
+    cap = len(prefix) + len(fields[0].scaffold) + max(len(c) for c in fields[0].candidates)
+    dev = cpd.upload_weights(tiny_w.mats, sh.n_layers, sh.d_model, "cuda:0")
+    lim = cpd.limits_for(sh.vocab_size, sh.max_seq, [cap, cap], [fields, fields], cap + 64)
+    m = cpd.PcdModel(cpd.config_of(sh), dev, lim)
+    comp = m.compile_fields(fields)
+    keys = ("prob", "logscore", "mass", "margin", "argmax")
+
+    def same(a, b):
+        for k in keys:
+            assert np.array_equal(a[k], b[k]), k
+
+    st = m.prefill(prefix)
+    same(m.decide(st, fields), m.decide(st, comp))
+    same(m.decide_many([st, st], [fields, fields])[1], m.decide_many([st, st], [comp, fields])[0])
+    outs = []
+    for f in (fields, comp):
+        s2 = st.fork(capacity=cap)
+        outs.append(m.decide_sequenced(s2, f, 1))
+        s2.close()
+    same(*outs)
+    outs = []
+    for f in (fields, comp):
+        s3 = m.new_state(len(prefix))
+        outs.append(m.extend_decide(s3, prefix, f))
+        s3.close()
+    same(*outs)
+    st.close()
+    m.close()

@@ -140,3 +140,21 @@ def test_null_arguments_are_rejected(lib):
     assert b"null" in lib.pcd_last_error()
     lib.pcd_free_state(None)
     lib.pcd_free_model(None)
+
+
+def test_compiled_fields_give_the_same_plan():
+    """A schema marshalled once (CompiledFields) hands the library the same
+    C arrays as the field lists: the plans are identical, also mixed with
+    plain lists in one multi-request call."""
+    V = 3000
+    wl = pi.make_workload("cfg1")
+    r = wl.requests[0]
+    sp = pi.random_spelling_fields(4242, V, 3, max_labels=5, max_spellings=3, max_len=3, mode="level")
+    for fields, P, vocab in ((r.fields, len(r.prefix), wl.shape.vocab_size), (sp, 17, V)):
+        comp = cpd.PcdModel.compile_fields(fields)
+        a = cpd.debug_plan(vocab, 1 << 20, [P, P + 5], [fields, fields])
+        b = cpd.debug_plan(vocab, 1 << 20, [P, P + 5], [comp, fields])
+        c = cpd.debug_plan(vocab, 1 << 20, [P, P + 5], [comp, comp])
+        for k in a:
+            assert np.array_equal(a[k], b[k]) and np.array_equal(a[k], c[k]), k
+    assert len(comp) == len(sp) and comp[0] is sp[0]
