@@ -648,10 +648,50 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t *tok, const T *E, i
     for (int j = threadIdx.x; j < d; j += 256) h[(size_t)t * d + j] = from_f<T>(to_f(row[j]) * inv * w[j]);
 }
 
+// The same for d = 512 * NE: the row and the norm weight are loaded once, up
+// front, as pairs, so a row costs one memory round trip.
+template <typename T, int NE>
+__global__ __launch_bounds__(256) void k_embed_n(const int32_t *tok, const T *E, float *x, const float *w, float eps,
+                                                 T *h) {
+    constexpr int D = 512 * NE;
+    __shared__ float red[4];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const T *row = E + (size_t)tok[t] * D;
+    float2 v[NE], wv[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int j = 2 * (tid + 256 * i);
+        v[i] = make_float2(to_f(row[j]), to_f(row[j + 1]));
+        wv[i] = reinterpret_cast<const float2 *>(w)[tid + 256 * i];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        reinterpret_cast<float2 *>(x + (size_t)t * D)[tid + 256 * i] = v[i];
+        ss += v[i].x * v[i].x + v[i].y * v[i].y;
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)D + eps);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        T *hp = h + (size_t)t * D + 2 * (tid + 256 * i);
+        hp[0] = from_f<T>(v[i].x * inv * wv[i].x);
+        hp[1] = from_f<T>(v[i].y * inv * wv[i].y);
+    }
+}
+
 void embed(int dt, const int32_t *tok, int32_t T, const void *E, int32_t d, float *x, const float *w, float eps,
            void *h, hipStream_t st) {
     if (T <= 0) return;
-    if (dt == PCD_DT_F32)
+    if (dt != PCD_DT_F32 && d == 1536)
+        hipLaunchKernelGGL((k_embed_n<bf16_t, 3>), dim3(T), dim3(256), 0, st, tok, (const bf16_t *)E, x, w, eps,
+                           (bf16_t *)h);
+    else if (dt != PCD_DT_F32 && d == 3584)
+        hipLaunchKernelGGL((k_embed_n<bf16_t, 7>), dim3(T), dim3(256), 0, st, tok, (const bf16_t *)E, x, w, eps,
+                           (bf16_t *)h);
+    else if (dt == PCD_DT_F32)
         hipLaunchKernelGGL(k_embed<float>, dim3(T), dim3(256), 0, st, tok, (const float *)E, d, x, w, eps, (float *)h);
     else
         hipLaunchKernelGGL(k_embed<bf16_t>, dim3(T), dim3(256), 0, st, tok, (const bf16_t *)E, d, x, w, eps,
@@ -673,10 +713,43 @@ __global__ void k_rmsnorm(const float *x, const int32_t *rows, int32_t d, const 
     for (int j = threadIdx.x; j < d; j += 256) out[(size_t)i * d + j] = from_f<T>(xr[j] * inv * w[j]);
 }
 
+// The same for d = 512 * NE, every load of the row up front.
+template <typename T, int NE>
+__global__ __launch_bounds__(256) void k_rmsnorm_n(const float *x, const int32_t *rows, const float *w, float eps,
+                                                   T *out) {
+    constexpr int D = 512 * NE;
+    __shared__ float red[4];
+    const int i = blockIdx.x, tid = threadIdx.x;
+    const float2 *xr = reinterpret_cast<const float2 *>(x + (size_t)(rows ? rows[i] : i) * D);
+    float2 v[NE], wv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        v[e] = xr[tid + 256 * e];
+        wv[e] = reinterpret_cast<const float2 *>(w)[tid + 256 * e];
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) s += v[e].x * v[e].x + v[e].y * v[e].y;
+    s = wave_sum(s);
+    if ((tid & 63) == 0) red[tid >> 6] = s;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)D + eps);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        T *op = out + (size_t)i * D + 2 * (tid + 256 * e);
+        op[0] = from_f<T>(v[e].x * inv * wv[e].x);
+        op[1] = from_f<T>(v[e].y * inv * wv[e].y);
+    }
+}
+
 void rmsnorm(int dt, const float *x, const int32_t *rows, int32_t n, int32_t d, const float *w, float eps, void *out,
              hipStream_t st) {
     if (n <= 0) return;
-    if (dt == PCD_DT_F32)
+    if (dt != PCD_DT_F32 && d == 1536)
+        hipLaunchKernelGGL((k_rmsnorm_n<bf16_t, 3>), dim3(n), dim3(256), 0, st, x, rows, w, eps, (bf16_t *)out);
+    else if (dt != PCD_DT_F32 && d == 3584)
+        hipLaunchKernelGGL((k_rmsnorm_n<bf16_t, 7>), dim3(n), dim3(256), 0, st, x, rows, w, eps, (bf16_t *)out);
+    else if (dt == PCD_DT_F32)
         hipLaunchKernelGGL(k_rmsnorm<float>, dim3(n), dim3(256), 0, st, x, rows, d, w, eps, (float *)out);
     else hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(n), dim3(256), 0, st, x, rows, d, w, eps, (bf16_t *)out);
 }
@@ -1505,9 +1578,41 @@ __global__ __launch_bounds__(256) void k_readout_lse(const float2 *part, int32_t
     if (threadIdx.x == 0) lse[r] = mx + logf(red[0] + red[1] + red[2] + red[3]);
 }
 
+// The same arithmetic in the same order for up to 256 * KMAX tiles, with each
+// thread's partials loaded once into registers (one memory round trip).
+constexpr int LSE_KMAX = 8;
+__global__ __launch_bounds__(256) void k_readout_lse_reg(const float2 *part, int32_t n_tiles, int32_t R, float *lse) {
+    __shared__ float red[4];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    float2 p[LSE_KMAX];
+#pragma unroll
+    for (int k = 0; k < LSE_KMAX; ++k) {
+        const int i = tid + 256 * k;
+        p[k] = i < n_tiles ? part[(size_t)i * R + r] : make_float2(-INFINITY, 0.f);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < LSE_KMAX; ++k) mx = fmaxf(mx, p[k].x);
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < LSE_KMAX; ++k)
+        if (tid + 256 * k < n_tiles) s += p[k].y * __expf(p[k].x - mx);
+    s = wave_sum(s);
+    if ((tid & 63) == 0) red[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) lse[r] = mx + logf(red[0] + red[1] + red[2] + red[3]);
+}
+
 void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hipStream_t st) {
     if (R <= 0) return;
-    hipLaunchKernelGGL(k_readout_lse, dim3(R), dim3(256), 0, st, part, n_tiles, R, lse);
+    if (n_tiles <= 256 * LSE_KMAX)
+        hipLaunchKernelGGL(k_readout_lse_reg, dim3(R), dim3(256), 0, st, part, n_tiles, R, lse);
+    else hipLaunchKernelGGL(k_readout_lse, dim3(R), dim3(256), 0, st, part, n_tiles, R, lse);
 }
 
 // One thread per field.  A spelling's score sums the log-probabilities of the
