@@ -44,6 +44,7 @@ size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 // workgroup of its own.
 constexpr int ATT_TARGET_BLOCKS = 256;
 constexpr int ATT_MIN_SPLIT_TILES = 2;  // 64-key tiles
+constexpr int MAX_PASS_ROWS = 1 << 18;  // token rows of one decoder pass
 // Key splits of a row block: enough for `row_blocks` blocks to reach the
 // target count, no split shorter than the minimum, at most MAX_SPLITS.
 static int att_splits(int64_t row_blocks, int key_tiles) {
@@ -135,7 +136,11 @@ int check_config(const pcd_config *c, const pcd_limits *l) {
     if (l->max_prefill_tokens <= 0 || l->max_branch_tokens <= 0 || l->max_readouts <= 0 || l->max_gathers <= 0 ||
         l->max_fields <= 0 || l->max_candidates <= 0 || l->max_requests <= 0 || l->max_spellings < 0)
         return fail(PCD_E_ARG, "limits must be positive");
-    if (l->max_prefill_tokens > c->max_seq) return fail(PCD_E_ARG, "max_prefill_tokens exceeds max_seq");
+    // rows of one pass (pcd_prefill_many puts every sequence in one); each
+    // sequence is bounded by max_seq on its own
+    if (l->max_prefill_tokens > MAX_PASS_ROWS || l->max_branch_tokens > MAX_PASS_ROWS)
+        return fail(PCD_E_ARG, "max_prefill_tokens and max_branch_tokens must be at most " +
+                                   std::to_string(MAX_PASS_ROWS));
     return PCD_OK;
 }
 

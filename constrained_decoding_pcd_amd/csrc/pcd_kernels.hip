@@ -183,7 +183,10 @@ __device__ __forceinline__ void barrier_keep_loads() {
 template <typename T, int BM, int BN, int NB, Epi E, int KB = 128> struct GemmLds {
     static constexpr bool LDS_EPI = (E == Epi::Qkv || E == Epi::Readout);
     static constexpr int STAGE = (BM + NB * BN) * KB;
-    static constexpr int C_BYTES = LDS_EPI ? BM * (BN + 4) * 4 : 0;
+    // Qkv: after the C tile, per row its position and the destinations of up
+    // to 4 heads (BN = 128 columns of heads of at least 32)
+    static constexpr int META = E == Epi::Qkv ? BM * (4 + 4 * 8) : 0;
+    static constexpr int C_BYTES = LDS_EPI ? BM * (BN + 4) * 4 + META : 0;
     static int bytes(int S) { return S * STAGE > C_BYTES ? S * STAGE : C_BYTES; }
 };
 
@@ -397,45 +400,69 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
                     Cs[(wm * WTM + i * 16 + lg * 4 + r) * LDC + wn * WTN + j * 16 + lr] = acc[0][i][j][r];
         __syncthreads();
         if constexpr (E == Epi::Qkv) {
-            // rotate-half RoPE: pair (j, j + hd/2) of each head of q and k
-            const int hd = e.hd, half = hd >> 1;
-            for (int idx = tid; idx < BM * (BN / 2); idx += NT) {
-                const int r = idx / (BN / 2), c = idx % (BN / 2);
+            // rotate-half RoPE: pair (j, j + hd/2) of each head of q and k.
+            // First the row metadata, once per tile and in parallel: each row's
+            // position and, per head of the tile, where its hd values go (a q row,
+            // or a row of a K or V cache).  Then every thread loads the (cos, sin)
+            // of all its pairs before its first store, so no load waits on a store.
+            const int hd = e.hd, half = hd >> 1, nh = BN / hd;
+            int *s_pos = reinterpret_cast<int *>(lds + BM * LDC * 4);
+            uint64_t *s_dst = reinterpret_cast<uint64_t *>(lds + BM * LDC * 4 + BM * 4);
+            for (int t = tid; t < BM * nh; t += NT) {
+                const int r = t / nh, hh = t % nh, m = m0 + r;
+                T *dst = nullptr;
+                if (m < g.M) {
+                    if (hh == 0) s_pos[r] = e.pos ? e.pos[m] : m;
+                    const int n = n0 + hh * hd;  // first column of this head
+                    if (n < e.n_q) {
+                        dst = reinterpret_cast<T *>(e.out) + (size_t)m * e.n_q + n;
+                    } else if (e.kv_req) {
+                        // one of several KV buffers (batched prefill)
+                        const int rq = e.kv_req[m], Hkv = e.n_k / hd;
+                        const size_t slab = (size_t)e.kv_cap[rq] * hd;
+                        const bool is_k = n < e.n_q + e.n_k;
+                        const int kh = is_k ? (n - e.n_q) / hd : (n - e.n_q - e.n_k) / hd;
+                        dst = reinterpret_cast<T *>(e.kv_base[rq]) +
+                              ((size_t)(e.kv_layer * 2 + (is_k ? 0 : 1)) * Hkv + kh) * slab +
+                              (size_t)e.kv_row[m] * hd;
+                    } else {
+                        // rows from kv_split on go to the second cache (the branch tokens of a fused pass)
+                        const bool second = m >= e.kv_split;
+                        const int mr = second ? m - e.kv_split : m, cap = second ? e.cap2 : e.cap;
+                        if (n < e.n_q + e.n_k) {
+                            const int kh = (n - e.n_q) / hd;
+                            dst = reinterpret_cast<T *>(second ? e.kc2 : e.kc) + ((size_t)kh * cap + mr) * hd;
+                        } else {
+                            const int vh = (n - e.n_q - e.n_k) / hd;
+                            dst = reinterpret_cast<T *>(second ? e.vc2 : e.vc) + ((size_t)vh * cap + mr) * hd;
+                        }
+                    }
+                }
+                s_dst[r * 4 + hh] = reinterpret_cast<uint64_t>(dst);
+            }
+            __syncthreads();
+            constexpr int PAIRS = BM * (BN / 2), IT = PAIRS / NT;
+            static_assert(IT * NT == PAIRS && BN == 128, "pairs per thread");
+            float2 cs[IT];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int idx = tid + it * NT, r = idx / (BN / 2), c = idx % (BN / 2);
                 const int hh = c / half, j = c % half;
-                const int m = m0 + r;
-                if (m >= g.M) continue;
+                const bool rot = m0 + r < g.M && n0 + hh * hd < e.n_q + e.n_k;
+                cs[it] = rot ? e.rope[(size_t)s_pos[r] * half + j] : make_float2(1.f, 0.f);
+            }
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int idx = tid + it * NT, r = idx / (BN / 2), c = idx % (BN / 2);
+                const int hh = c / half, j = c % half;
+                T *dst = reinterpret_cast<T *>(s_dst[r * 4 + hh]);
+                if (!dst) continue;  // row past M
                 const int col = hh * hd + j;
-                const int n = n0 + col;  // first-half column of this pair
                 float v1 = Cs[r * LDC + col], v2 = Cs[r * LDC + col + half];
-                if (n < e.n_q + e.n_k) {
-                    const int p = e.pos ? e.pos[m] : m;
-                    const float2 cs = e.rope[(size_t)p * half + j];
-                    const float o1 = v1 * cs.x - v2 * cs.y, o2 = v2 * cs.x + v1 * cs.y;
+                if (n0 + hh * hd < e.n_q + e.n_k) {
+                    const float o1 = v1 * cs[it].x - v2 * cs[it].y, o2 = v2 * cs[it].x + v1 * cs[it].y;
                     v1 = o1;
                     v2 = o2;
-                }
-                T *dst;
-                if (n < e.n_q) {
-                    dst = reinterpret_cast<T *>(e.out) + (size_t)m * e.n_q + (n - j);
-                } else if (e.kv_req) {
-                    // one of several KV buffers (batched prefill)
-                    const int rq = e.kv_req[m], Hkv = e.n_k / hd;
-                    const size_t slab = (size_t)e.kv_cap[rq] * hd;
-                    const bool is_k = n < e.n_q + e.n_k;
-                    const int kh = is_k ? (n - e.n_q) / hd : (n - e.n_q - e.n_k) / hd;
-                    dst = reinterpret_cast<T *>(e.kv_base[rq]) +
-                          ((size_t)(e.kv_layer * 2 + (is_k ? 0 : 1)) * Hkv + kh) * slab + (size_t)e.kv_row[m] * hd;
-                } else {
-                    // rows from kv_split on go to the second cache (the branch tokens of a fused pass)
-                    const bool second = m >= e.kv_split;
-                    const int mr = second ? m - e.kv_split : m, cap = second ? e.cap2 : e.cap;
-                    if (n < e.n_q + e.n_k) {
-                        const int kh = (n - e.n_q) / hd;
-                        dst = reinterpret_cast<T *>(second ? e.kc2 : e.kc) + ((size_t)kh * cap + mr) * hd;
-                    } else {
-                        const int vh = (n - e.n_q - e.n_k) / hd;
-                        dst = reinterpret_cast<T *>(second ? e.vc2 : e.vc) + ((size_t)vh * cap + mr) * hd;
-                    }
                 }
                 dst[j] = from_f<T>(v1);
                 dst[j + half] = from_f<T>(v2);
@@ -568,7 +595,7 @@ template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
             case Epi::Qkv:
                 if (128 % c.hd) return false;
                 if (c.M > 1024) {
-                    launch_gemm<T, 64, 128, 2, 2, 1, 4, Epi::Qkv>(c, 1, st);
+                    launch_gemm<T, 128, 128, 2, 4, 1, 3, Epi::Qkv>(c, 1, st);
                 } else {
                     // 32-row tiles while they fit one round of workgroups; 64-row
                     // tiles (8 waves) once 32 rows would need a second round
@@ -586,6 +613,7 @@ template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
                 return true;
             case Epi::Resid:
                 if (rg == Reg::Small) gemm_resid_cfg<T, 32, 128, 1, 4, 4>(c, st);
+                else if (c.K < 4096 && c.M > 1024) gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
                 else if (c.K < 4096) {
                     // 96-row tiles where 64-row ones would need a second round of
                     // workgroups and 96-row ones fit one (799 rows: 17.4 us against 18.3 us

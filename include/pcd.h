@@ -114,8 +114,10 @@ typedef struct {
 
 /* Upper bounds a model's workspace is sized for. */
 typedef struct {
-    int32_t max_prefill_tokens;  /* tokens per pcd_prefill call */
-    int32_t max_branch_tokens;   /* scaffold + trie tokens of one decide call, all requests */
+    int32_t max_prefill_tokens;  /* token rows of one prefill or extend pass: pcd_prefill, pcd_extend,
+                                    all sequences of one pcd_prefill_many (each sequence still at
+                                    most max_seq); at most 262144 */
+    int32_t max_branch_tokens;   /* scaffold + trie tokens of one decide call, all requests; at most 262144 */
     int32_t max_readouts;        /* readout rows of one decide call */
     int32_t max_gathers;         /* candidate-token logits gathered by one decide call */
     int32_t max_fields;          /* fields of one decide call, all requests */

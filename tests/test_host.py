@@ -134,6 +134,23 @@ def test_workspace_bytes_rejects_bad_configs(lib):
         assert lib.pcd_workspace_bytes(ctypes.byref(cpd.binding.pcd_config(**bad)), ctypes.byref(lim)) == 0
 
 
+def test_pass_rows_may_exceed_max_seq_but_are_bounded(lib):
+    """max_prefill_tokens counts the rows of one pass (all sequences of a
+    batched prefill), so it may exceed max_seq; the row count of a pass is
+    bounded (2^18) and every limit must be positive."""
+    cfg = cpd.binding.pcd_config(n_layers=2, d_model=128, n_heads=4, n_kv_heads=2, head_dim=32, ffn_dim=384,
+                                 vocab_size=2048, max_seq=512, rope_theta=1e4, rms_eps=1e-6, tied_lm_head=1,
+                                 dtype=0)
+    ws = lambda *a: lib.pcd_workspace_bytes(ctypes.byref(cfg), ctypes.byref(cpd.binding.pcd_limits(*a)))
+    small = ws(256, 64, 16, 64, 8, 32, 2, 0)
+    big = ws(64 * 512, 64, 16, 64, 8, 32, 64, 0)
+    assert 0 < small < big
+    assert ws(1 << 18, 64, 16, 64, 8, 32, 2, 0) > 0
+    assert ws((1 << 18) + 1, 64, 16, 64, 8, 32, 2, 0) == 0
+    assert ws(256, (1 << 18) + 1, 16, 64, 8, 32, 2, 0) == 0
+    assert ws(0, 64, 16, 64, 8, 32, 2, 0) == 0
+
+
 def test_null_arguments_are_rejected(lib):
     assert lib.pcd_decide_many(None, None, 0, 1.0, None, None) == -1
     assert lib.pcd_prefill(None, None, 0, None, 0, None, None) == -1
