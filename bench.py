@@ -350,10 +350,16 @@ def main():
         w_bytes = float(sum(work[c][1] for c in ("branch_qkv", "branch_o", "branch_gateup", "branch_down")))
         kv_tok = sh.n_layers * 2 * sh.n_kv_heads * sh.head_dim * e
         br_bytes = w_bytes * sh.n_layers + P * kv_tok + Tb * kv_tok
+        # The last layer of a pass does only the work later steps read: QKV of
+        # every row (the K/V), then, in a pass with readouts, the branch rows'
+        # attention and the readout rows' O projection and MLP.
+        d, F, nq = sh.d_model, sh.ffn_dim, sh.n_heads * sh.head_dim
+        last_r = 2.0 * R * (d * nq + 2 * F * d + d * F)
         pf_flops = sum(work[c][0] for c in ("prefill_qkv", "prefill_o", "prefill_gateup", "prefill_down",
-                                            "prefill_attn")) * sh.n_layers
-        fu_flops = sum(work[c][0] for c in ("fused_qkv", "fused_o", "fused_gateup", "fused_down",
-                                            "fused_attn")) * sh.n_layers
+                                            "prefill_attn")) * (sh.n_layers - 1) + work["prefill_qkv"][0]
+        fu_flops = (sum(work[c][0] for c in ("fused_qkv", "fused_o", "fused_gateup", "fused_down",
+                                             "fused_attn")) * (sh.n_layers - 1)
+                    + work["fused_qkv"][0] + work["branch_attn"][0] + last_r)
         ro_bytes = float(work["readout_lmhead"][1])
         if "two-pass" in modes:
             ph = modes["two-pass"]["phases_ms"]

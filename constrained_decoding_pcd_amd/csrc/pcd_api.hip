@@ -54,7 +54,7 @@ static int att_splits(int64_t row_blocks, int key_tiles) {
 }
 
 struct Layout {
-    size_t rope, x, h, q, ao, act, splitk, kvb, part_o, part_ml, hr, ro_part, lse, z, outs, plan;
+    size_t rope, x, h, q, ao, act, splitk, kvb, part_o, part_ml, hr, xr, aor, ro_part, lse, z, outs, plan;
     size_t plan_bytes, outs_bytes, total;
 };
 
@@ -104,6 +104,8 @@ Layout layout(const pcd_config &c, const pcd_limits &l) {
     L.part_o = take((size_t)MAX_SPLITS * rows * hq * 4);
     L.part_ml = take((size_t)MAX_SPLITS * rows * c.n_heads * sizeof(float2));
     L.hr = take((size_t)l.max_readouts * d * esz);
+    L.xr = take((size_t)l.max_readouts * d * 4);     // the last layer's readout rows: residual stream
+    L.aor = take((size_t)l.max_readouts * hq * esz);  // and attention output
     L.ro_part = take((size_t)(c.vocab_size / 128) * l.max_readouts * sizeof(float2));
     L.lse = take((size_t)l.max_readouts * 4);
     L.z = take((size_t)l.max_gathers * 4);
@@ -223,7 +225,8 @@ size_t esize(const pcd_model *m) { return m->cfg.dtype == PCD_DTYPE_F32 ? 4 : 2;
 // O projection or down projection into the residual stream (split-K inside
 // gemm() when the tile count is too small for the chip), followed by the
 // RMSNorm with weight `norm_w` whose output is the next GEMM's input
-bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W, const float *norm_w, hipStream_t st) {
+bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W, const float *norm_w, hipStream_t st,
+                float *x = nullptr, void *h_out = nullptr) {
     GemmCall c{};
     c.dt = m->cfg.dtype;
     c.A = A;
@@ -233,12 +236,12 @@ bool gemm_resid(pcd_model *m, const void *A, int M, int N, int K, const void *W,
     c.B[0].ptr[0] = W;
     c.B[0].nseg = 1;
     c.epi = Epi::Resid;
-    c.x = reinterpret_cast<float *>(m->ws + m->L.x);
+    c.x = x ? x : reinterpret_cast<float *>(m->ws + m->L.x);
     c.part = reinterpret_cast<float *>(m->ws + m->L.splitk);
     c.part_cap = splitk_floats(m->cfg, m->lim);
     c.norm_w = norm_w;
     c.eps = m->cfg.rms_eps;
-    c.h_out = m->ws + m->L.h;
+    c.h_out = h_out ? h_out : m->ws + m->L.h;
     return gemm(c, st);
 }
 
@@ -252,20 +255,29 @@ struct KvRows {
     const uint64_t *base;            // per buffer: device address
 };
 
+// The last layer of a pass computes only what later work reads: every row's
+// K and V (the state keeps the new tokens', the branch attention reads the
+// branch tokens'), then either nothing more (n_keep == 0: a prefill or
+// extend) or the residual stream of the readout rows keep[0..n_keep), which
+// after the attention are gathered into rows 0..n_keep-1 of the compact
+// buffers L.aor / L.xr.  n_keep < 0: the whole layer over all M rows.
 template <class Attn>
 int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, int cap, Pass kind, Attn attn,
           hipStream_t st, void *kc2 = nullptr, void *vc2 = nullptr, int cap2 = 0, int kv_split = 0,
-          const KvRows *kr = nullptr) {
+          const KvRows *kr = nullptr, const int32_t *keep = nullptr, int n_keep = -1) {
     const bool br = kind == Pass::Branch, fu = kind == Pass::Fused;
+    // the readout rows' kernels of a trimmed last layer count as "other", so
+    // every launch of a class has the class's row count
+    const bool few = n_keep > 0;
     const int K_QKV = fu ? PCD_KC_FUSED_QKV : br ? PCD_KC_BRANCH_QKV : PCD_KC_PREFILL_QKV;
-    const int K_O = fu ? PCD_KC_FUSED_O : br ? PCD_KC_BRANCH_O : PCD_KC_PREFILL_O;
-    const int K_GU = fu ? PCD_KC_FUSED_GATEUP : br ? PCD_KC_BRANCH_GATEUP : PCD_KC_PREFILL_GATEUP;
-    const int K_DN = fu ? PCD_KC_FUSED_DOWN : br ? PCD_KC_BRANCH_DOWN : PCD_KC_PREFILL_DOWN;
+    const int K_O = few ? PCD_KC_OTHER : fu ? PCD_KC_FUSED_O : br ? PCD_KC_BRANCH_O : PCD_KC_PREFILL_O;
+    const int K_GU = few ? PCD_KC_OTHER : fu ? PCD_KC_FUSED_GATEUP : br ? PCD_KC_BRANCH_GATEUP : PCD_KC_PREFILL_GATEUP;
+    const int K_DN = few ? PCD_KC_OTHER : fu ? PCD_KC_FUSED_DOWN : br ? PCD_KC_BRANCH_DOWN : PCD_KC_PREFILL_DOWN;
     const pcd_config &c = m->cfg;
     const int d = c.d_model, hd = c.head_dim, nq = c.n_heads * hd, nk = c.n_kv_heads * hd;
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     void *h = m->ws + m->L.h, *q = m->ws + m->L.q, *ao = m->ws + m->L.ao, *act = m->ws + m->L.act;
-    (void)x;  // h holds rmsnorm(x) * attn_norm[l] on entry (embedding or previous layer)
+    // h holds rmsnorm(x) * attn_norm[l] on entry (embedding or previous layer)
     GemmCall g{};
     g.dt = c.dtype;
     g.A = h;
@@ -303,10 +315,22 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     m->tbegin(K_QKV, st);
     if (!gemm(g, st)) return fail(PCD_E_ARG, "QKV projection: unsupported shape");
     m->tend(st);
-    int rc = attn(q, ao);
+    if (n_keep == 0) return PCD_OK;
+    int rc = attn(q, ao, n_keep > 0);
     if (rc != PCD_OK) return rc;
+    float *xo = nullptr;  // residual stream of the rows that go on (NULL: the full buffer)
+    if (n_keep > 0) {
+        xo = reinterpret_cast<float *>(m->ws + m->L.xr);
+        void *aor = m->ws + m->L.aor;
+        m->tbegin(K_O, st);
+        gather_rows2(ao, (size_t)nq * esize(m), aor, x, (size_t)d * 4, xo, keep, n_keep, st);
+        m->tend(st);
+        ao = aor;
+        M = n_keep;
+    }
     m->tbegin(K_O, st);
-    if (!gemm_resid(m, ao, M, d, nq, m->wo[l], m->mn[l], st)) return fail(PCD_E_ARG, "O projection: unsupported shape");
+    if (!gemm_resid(m, ao, M, d, nq, m->wo[l], m->mn[l], st, xo))
+        return fail(PCD_E_ARG, "O projection: unsupported shape");
     m->tend(st);
     GemmCall f{};
     f.dt = c.dtype;
@@ -325,7 +349,7 @@ int layer(pcd_model *m, int l, int M, const int32_t *pos, void *kc, void *vc, in
     m->tend(st);
     m->tbegin(K_DN, st);
     const float *next_norm = l + 1 < c.n_layers ? m->an[l + 1] : nullptr;
-    if (!gemm_resid(m, act, M, d, c.ffn_dim, m->wd[l], next_norm, st))
+    if (!gemm_resid(m, act, M, d, c.ffn_dim, m->wd[l], next_norm, st, xo))
         return fail(PCD_E_ARG, "down projection: unsupported shape");
     m->tend(st);
     return PCD_OK;
@@ -490,7 +514,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
         // this layer's K and V slabs, at the first new token's row
         char *kc = static_cast<char *>(kv_buf) + ((size_t)l * 2 * c.n_kv_heads * slab + (size_t)P0 * hd) * es;
         char *vc = kc + (size_t)c.n_kv_heads * slab * es;
-        auto attn = [&](void *q, void *ao) {
+        auto attn = [&](void *q, void *ao, bool) {
             AttnCall a{};
             a.dt = c.dtype;
             a.hd = hd;
@@ -528,7 +552,8 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
             }
             return PCD_OK;
         };
-        int rc = layer(m, l, n, d_pos, kc, vc, cap, Pass::Prefill, attn, st);
+        int rc = layer(m, l, n, d_pos, kc, vc, cap, Pass::Prefill, attn, st, nullptr, nullptr, 0, 0, nullptr, nullptr,
+                       l + 1 == c.n_layers ? 0 : -1);
         if (rc != PCD_OK) return rc;
     }
     HIP_TRY(hipEventRecord(m->ev[4], st));
@@ -608,7 +633,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
     float *part_o = reinterpret_cast<float *>(m->ws + m->L.part_o);
     float2 *part_ml = reinterpret_cast<float2 *>(m->ws + m->L.part_ml);
     for (int l = 0; l < c.n_layers; ++l) {
-        auto attn = [&](void *q, void *ao) {
+        auto attn = [&](void *q, void *ao, bool) {
             AttnCall a{};
             a.dt = c.dtype;
             a.hd = hd;
@@ -646,7 +671,8 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
             }
             return PCD_OK;
         };
-        int rc = layer(m, l, n, d_pos, nullptr, nullptr, 0, Pass::Prefill, attn, st, nullptr, nullptr, 0, 0, &kr);
+        int rc = layer(m, l, n, d_pos, nullptr, nullptr, 0, Pass::Prefill, attn, st, nullptr, nullptr, 0, 0, &kr,
+                       nullptr, l + 1 == c.n_layers ? 0 : -1);
         if (rc != PCD_OK) return rc;
     }
     HIP_TRY(hipEventRecord(m->ev[4], st));
@@ -914,6 +940,7 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                         AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1, P0});
             }
     }
+    const int n_new_blocks = (int)blocks.size();  // the new tokens' blocks come first
     for (int r = 0; r < n_req; ++r) {
         const int P = lens[r];
         int s, slen;
@@ -1010,7 +1037,7 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                                     ((size_t)l * 2 * c.n_kv_heads * sslab + (size_t)P0 * hd) * es
                               : nullptr;
         char *svc = n_new > 0 ? skc + (size_t)c.n_kv_heads * sslab * es : nullptr;
-        auto attn = [&](void *q, void *ao) {
+        auto attn = [&](void *q, void *ao, bool last) {
             AttnCall a{};
             a.dt = c.dtype;
             a.hd = hd;
@@ -1020,8 +1047,10 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
             a.q = q;
             a.req_kv = d_kv;
             a.req_stride = d_stride;
-            a.blocks = d_blk;
-            a.n_blocks = (int)blocks.size();
+            // the last layer needs no attention output for the new tokens
+            const int b0 = last ? n_new_blocks : 0;
+            a.blocks = d_blk + b0;
+            a.n_blocks = (int)blocks.size() - b0;
             a.branch0 = n_new;
             a.tok_splits = d_tsp;
             a.out = ao;
@@ -1035,7 +1064,7 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
             a.nsc = d_nsc;
             a.par = d_par;
             a.chain = d_chain;
-            m->tbegin(n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_ATTN, st);
+            m->tbegin(last ? PCD_KC_OTHER : n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);
             if (!ok) return fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
@@ -1046,25 +1075,34 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                 t.n_heads = c.n_heads;
                 t.n_kv_heads = c.n_kv_heads;
                 t.n_tokens = M;
+                t.tok0 = last ? n_new : 0;
                 t.part_o = part_o;
                 t.part_ml = part_ml;
                 t.tok_splits = d_tsp;
                 t.out = ao;
-                m->tbegin(n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_TAIL, st);
+                m->tbegin(last ? PCD_KC_OTHER : n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_TAIL, st);
                 attention_merge(t, st);
                 m->tend(st);
             }
             return PCD_OK;
         };
-        rc = n_new > 0 ? layer(m, l, M, d_pos, skc, svc, states[0]->cap, Pass::Fused, attn, st, kc, vc, Tb, n_new)
-                       : layer(m, l, M, d_pos, kc, vc, Tb, Pass::Branch, attn, st);
+        // the last layer carries on only the readout rows
+        const bool last = l + 1 == c.n_layers;
+        const int32_t *keep = last ? d_ro : nullptr;
+        const int n_keep = last ? R : -1;
+        rc = n_new > 0 ? layer(m, l, M, d_pos, skc, svc, states[0]->cap, Pass::Fused, attn, st, kc, vc, Tb, n_new,
+                               nullptr, keep, n_keep)
+                       : layer(m, l, M, d_pos, kc, vc, Tb, Pass::Branch, attn, st, nullptr, nullptr, 0, 0, nullptr, keep,
+                               n_keep);
         if (rc != PCD_OK) return rc;
     }
     HIP_TRY(hipEventRecord(m->ev[1], st));
     // readout: final norm of the readout rows, LM head with online log-sum-exp, combine
     void *hr = m->ws + m->L.hr;
     m->tbegin(PCD_KC_OTHER, st);
-    rmsnorm(c.dtype, x, d_ro, R, d, m->final_norm, c.rms_eps, hr, st);
+    // the readout rows' residual stream, gathered in the last layer
+    rmsnorm(c.dtype, reinterpret_cast<const float *>(m->ws + m->L.xr), nullptr, R, d, m->final_norm, c.rms_eps, hr,
+            st);
     m->tend(st);
     float2 *ro_part = reinterpret_cast<float2 *>(m->ws + m->L.ro_part);
     float *z = reinterpret_cast<float *>(ob + o_z), *lse = reinterpret_cast<float *>(ob + o_lse);

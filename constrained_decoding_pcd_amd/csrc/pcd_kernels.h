@@ -117,12 +117,18 @@ constexpr int ATT_MAX_SPLITS = 8;
 struct TailCall {
     int dt;
     int32_t hd, n_heads, n_kv_heads, n_tokens;
+    int32_t tok0;               // tokens [tok0, n_tokens) are merged
     const float *part_o;
     const float2 *part_ml;
     const int32_t *tok_splits;  // per token: its splits are 0..tok_splits[t]-1 (<= 1: nothing to merge)
     void *out;                  // [tokens][Hq][hd]
 };
 void attention_merge(const TailCall &c, hipStream_t st);
+
+// Row i of dst_a / dst_b = row rows[i] of src_a / src_b, for i < n (rows of
+// bytes_a / bytes_b bytes, multiples of 16).
+void gather_rows2(const void *src_a, size_t bytes_a, void *dst_a, const void *src_b, size_t bytes_b, void *dst_b,
+                  const int32_t *rows, int32_t n, hipStream_t st);
 
 // lse[r] from the per-tile partials of the readout GEMM.
 void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hipStream_t st);

@@ -1528,8 +1528,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
     const int lane = threadIdx.x & 63;
     const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int Hq = c.n_heads;
-    if (id >= c.n_tokens * Hq) return;
-    const int t = id / Hq, h = id % Hq;
+    if (id >= (c.n_tokens - c.tok0) * Hq) return;
+    const int t = c.tok0 + id / Hq, h = id % Hq;
     const int ns = c.tok_splits[t];
     if (ns <= 1) return;  // written directly by the attention kernel
     float2 ml[SMAX];
@@ -1568,7 +1568,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(TailCall c) {
 }
 
 template <typename T> static void merge_t(const TailCall &c, hipStream_t st) {
-    const int waves = c.n_tokens * c.n_heads;
+    const int waves = (c.n_tokens - c.tok0) * c.n_heads;
     if (waves <= 0) return;
     const dim3 grid((waves + 3) / 4);
     switch (c.hd) {
@@ -1604,6 +1604,27 @@ __global__ __launch_bounds__(256) void k_readout_lse(const float2 *part, int32_t
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
     __syncthreads();
     if (threadIdx.x == 0) lse[r] = mx + logf(red[0] + red[1] + red[2] + red[3]);
+}
+
+// Gather of rows for the last layer of a pass: block i < n copies row
+// rows[i] of a, block n + i that of b, in 16-byte units.
+__global__ __launch_bounds__(256) void k_gather_rows2(const uint4 *src_a, int32_t vec_a, uint4 *dst_a,
+                                                      const uint4 *src_b, int32_t vec_b, uint4 *dst_b,
+                                                      const int32_t *rows, int32_t n) {
+    const bool second = (int)blockIdx.x >= n;
+    const int i = second ? blockIdx.x - n : blockIdx.x;
+    const int vec = second ? vec_b : vec_a;
+    const uint4 *src = (second ? src_b : src_a) + (size_t)rows[i] * vec;
+    uint4 *dst = (second ? dst_b : dst_a) + (size_t)i * vec;
+    for (int j = threadIdx.x; j < vec; j += 256) dst[j] = src[j];
+}
+
+void gather_rows2(const void *src_a, size_t bytes_a, void *dst_a, const void *src_b, size_t bytes_b, void *dst_b,
+                  const int32_t *rows, int32_t n, hipStream_t st) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_gather_rows2, dim3(2 * n), dim3(256), 0, st, reinterpret_cast<const uint4 *>(src_a),
+                       (int32_t)(bytes_a / 16), reinterpret_cast<uint4 *>(dst_a), reinterpret_cast<const uint4 *>(src_b),
+                       (int32_t)(bytes_b / 16), reinterpret_cast<uint4 *>(dst_b), rows, n);
 }
 
 // The same arithmetic in the same order for up to 256 * KMAX tiles, with each
