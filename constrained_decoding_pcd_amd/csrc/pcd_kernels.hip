@@ -613,6 +613,11 @@ template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
                 return true;
             case Epi::Resid:
                 if (rg == Reg::Small) gemm_resid_cfg<T, 32, 128, 1, 4, 4>(c, st);
+                // many rows: 256x256 tiles (half the operand bytes per flop of 128x128)
+                // once they alone fill the chip (65,536 rows: O 0.31 against 0.48 ms,
+                // down 1.44 against 2.20 ms)
+                else if (c.M > 1024 && (c.M + 255) / 256 * (c.N / 256) >= 240 && c.N % 256 == 0)
+                    gemm_resid_cfg<T, 256, 256, 2, 4, 2>(c, st);
                 else if (c.K < 4096 && c.M > 1024) gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st);
                 else if (c.K < 4096) {
                     // 96-row tiles where 64-row ones would need a second round of
@@ -635,6 +640,8 @@ template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
                 // round is still cheaper per tile than any smaller tile's rounds
                 const int rows = (c.M + 127) / 128;
                 if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
+                // many rows: 256-row tiles (2,048 rows: 115 against 120 us; 65,536: 2.76 against 3.12 ms)
+                else if (c.M > 1024) launch_gemm<T, 256, 128, 2, 4, 2, 2, Epi::SwiGlu>(c, 1, st);
                 else if (rows * (c.N / 128) > 256 && c.N % 160 == 0 && rows * (c.N / 160) <= 256)
                     launch_gemm<T, 128, 160, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
                 else launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
