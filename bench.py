@@ -210,16 +210,17 @@ def main():
     # for a schema it serves many times; the library validates it and builds
     # the plan on every request
     schema = model.compile_fields(req.fields)
+    prompt = np.asarray(req.prefix, dtype=np.int32)  # token ids as a tokenizer hands them over
 
     def step_two_pass():  # prefill pass, then the branch pass
-        st = model.prefill(req.prefix, kv)
+        st = model.prefill(prompt, kv)
         out = model.decide(st, schema)
         st.close()
         return out
 
     def step_single_pass():  # an empty state; the prefix rows and the branch rows in one pass
         st = model.new_state(len(req.prefix), kv)
-        out = model.extend_decide(st, req.prefix, schema)
+        out = model.extend_decide(st, prompt, schema)
         st.close()
         return out
 
@@ -280,9 +281,9 @@ def main():
         def warm_step(kind):
             st = head_st.fork(kv=kv_w)
             if kind == "single_pass_p50_ms":
-                model.extend_decide(st, req.prefix[head_n:], schema)
+                model.extend_decide(st, prompt[head_n:], schema)
             else:
-                st.extend(req.prefix[head_n:])
+                st.extend(prompt[head_n:])
                 if kind == "first_field_round_p50_ms":
                     model.decide_sequenced(st, schema, 1)
                 else:

@@ -82,10 +82,32 @@ class pcd_request(ctypes.Structure):
 
 
 class pcd_outputs(ctypes.Structure):
-    _fields_ = [("cand_prob", POINTER(c_float)), ("cand_logscore", POINTER(c_float)),
-                ("field_mass", POINTER(c_float)), ("field_margin", POINTER(c_float)),
-                ("field_argmax", POINTER(c_int32)), ("readout_lse", POINTER(c_float)),
-                ("gather_logit", POINTER(c_float))]
+    # pointer-sized address fields (the C struct's float* / int32_t*), set from
+    # NumPy arrays' addresses
+    _fields_ = [("cand_prob", c_void_p), ("cand_logscore", c_void_p), ("field_mass", c_void_p),
+                ("field_margin", c_void_p), ("field_argmax", c_void_p), ("readout_lse", c_void_p),
+                ("gather_logit", c_void_p)]
+
+
+def _result_arrays(n_cands: int, n_fields: int, o: Optional[pcd_outputs] = None):
+    """One request's result arrays (the library writes every element when
+    the call succeeds) and the pcd_outputs that points at them (o, if given,
+    is filled in place)."""
+    d = {"prob": np.empty(n_cands, np.float32), "logscore": np.empty(n_cands, np.float32),
+         "mass": np.empty(n_fields, np.float32), "margin": np.empty(n_fields, np.float32),
+         "argmax": np.empty(n_fields, np.int32)}
+    if o is None:
+        o = pcd_outputs()
+    o.cand_prob, o.cand_logscore = d["prob"].ctypes.data, d["logscore"].ctypes.data
+    o.field_mass, o.field_margin = d["mass"].ctypes.data, d["margin"].ctypes.data
+    o.field_argmax = d["argmax"].ctypes.data
+    return d, o
+
+
+def _debug_arrays(d: dict, o: pcd_outputs, n_readouts: int, n_gathers: int):
+    d["lse"] = np.zeros(max(1, n_readouts), np.float32)
+    d["z"] = np.zeros(max(1, n_gathers), np.float32)
+    o.readout_lse, o.gather_logit = d["lse"].ctypes.data, d["z"].ctypes.data
 
 
 class pcd_stats(ctypes.Structure):
@@ -161,8 +183,6 @@ def _i32p(a: np.ndarray):
     return a.ctypes.data_as(POINTER(c_int32))
 
 
-def _f32p(a: Optional[np.ndarray]):
-    return None if a is None else a.ctypes.data_as(POINTER(c_float))
 
 
 # the 64-bit word layouts _Marshalled writes (x86-64 / little-endian ABI)
@@ -453,31 +473,17 @@ class PcdModel:
     def _outputs(self, mr, r, requests, debug_prefix):
         """Result arrays of request r and their pcd_outputs view (debug: sized
         from the plan at a prefix of debug_prefix tokens)."""
-        d = {"prob": np.zeros(mr.n_cands[r], np.float32), "logscore": np.zeros(mr.n_cands[r], np.float32),
-             "mass": np.zeros(mr.n_fields[r], np.float32), "margin": np.zeros(mr.n_fields[r], np.float32),
-             "argmax": np.zeros(mr.n_fields[r], np.int32)}
-        o = pcd_outputs()
-        o.cand_prob, o.cand_logscore = _f32p(d["prob"]), _f32p(d["logscore"])
-        o.field_mass, o.field_margin = _f32p(d["mass"]), _f32p(d["margin"])
-        o.field_argmax = _i32p(d["argmax"])
+        d, o = _result_arrays(mr.n_cands[r], mr.n_fields[r])
         if debug_prefix is not None:
             plan = debug_plan(self.cfg.vocab_size, self.cfg.max_seq, [debug_prefix], [requests[r]])
-            d["lse"] = np.zeros(max(1, len(plan["ro_tok"])), np.float32)
-            d["z"] = np.zeros(max(1, len(plan["g_tok"])), np.float32)
-            o.readout_lse, o.gather_logit = _f32p(d["lse"]), _f32p(d["z"])
+            _debug_arrays(d, o, len(plan["ro_tok"]), len(plan["g_tok"]))
         return d, o
 
     def decide_sequenced(self, state: PcdState, fields, n_first: int, temperature: float = 1.0) -> dict:
         """pcd_decide_sequenced: the first n_first fields, their answers appended
         to the state, then the rest; results indexed as for decide()."""
         mr = _Marshalled([fields])
-        d = {"prob": np.zeros(mr.n_cands[0], np.float32), "logscore": np.zeros(mr.n_cands[0], np.float32),
-             "mass": np.zeros(mr.n_fields[0], np.float32), "margin": np.zeros(mr.n_fields[0], np.float32),
-             "argmax": np.zeros(mr.n_fields[0], np.int32)}
-        o = pcd_outputs()
-        o.cand_prob, o.cand_logscore = _f32p(d["prob"]), _f32p(d["logscore"])
-        o.field_mass, o.field_margin = _f32p(d["mass"]), _f32p(d["margin"])
-        o.field_argmax = _i32p(d["argmax"])
+        d, o = _result_arrays(mr.n_cands[0], mr.n_fields[0])
         rq = mr.reqs[0]
         _check(self.lib.pcd_decide_sequenced(state.handle, rq.fields, rq.n_fields, rq.candidates, rq.n_candidates,
                                              n_first, temperature, ctypes.byref(o), _stream_handle(self.torch)))
@@ -498,17 +504,9 @@ class PcdModel:
         outs = (pcd_outputs * len(states))()
         res = []
         for r in range(len(states)):
-            d = {"prob": np.zeros(mr.n_cands[r], np.float32), "logscore": np.zeros(mr.n_cands[r], np.float32),
-                 "mass": np.zeros(mr.n_fields[r], np.float32), "margin": np.zeros(mr.n_fields[r], np.float32),
-                 "argmax": np.zeros(mr.n_fields[r], np.int32)}
-            o = outs[r]
-            o.cand_prob, o.cand_logscore = _f32p(d["prob"]), _f32p(d["logscore"])
-            o.field_mass, o.field_margin = _f32p(d["mass"]), _f32p(d["margin"])
-            o.field_argmax = _i32p(d["argmax"])
+            d, o = _result_arrays(mr.n_cands[r], mr.n_fields[r], outs[r])
             if debug:
-                d["lse"] = np.zeros(max(1, counts[r][0]), np.float32)
-                d["z"] = np.zeros(max(1, counts[r][1]), np.float32)
-                o.readout_lse, o.gather_logit = _f32p(d["lse"]), _f32p(d["z"])
+                _debug_arrays(d, o, counts[r][0], counts[r][1])
             res.append(d)
         hs = (c_void_p * len(states))(*[s.handle for s in states])
         _check(self.lib.pcd_decide_many(hs, mr.reqs, len(states), temperature, outs, _stream_handle(self.torch)))
