@@ -38,10 +38,11 @@ constexpr uint64_t STATE_MAGIC = 0x70636473746174ull;
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
 // Attention workgroups per launch (about one per compute unit: more splits
-// cost more in partial writes and the merge than they gain in parallelism;
-// measured on the 1.5B shape, 256 beats 512 and 1024 on the single-pass
-// request and ties on the two-pass one), and the shortest key range worth a
-// workgroup of its own.
+// cost more in partial writes and the merge than they gain in parallelism,
+// fewer leave the longest blocks on the critical path; measured on the 1.5B
+// shape, 256 beats 512 and 1024 on the single-pass request and ties on the
+// two-pass one, 128 ties with 256, and no splits at all (64) is 1-2% slower
+// on both), and the shortest key range worth a workgroup of its own.
 constexpr int ATT_TARGET_BLOCKS = 256;
 constexpr int ATT_MIN_SPLIT_TILES = 2;  // 64-key tiles
 constexpr int MAX_PASS_ROWS = 1 << 18;  // token rows of one decoder pass
