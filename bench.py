@@ -10,6 +10,7 @@ the roofline position of the dominant kernel (timed live with hipEvents on
 the library's stream) and the CPU oracle timed on a bounded sample.
 """
 import argparse
+import collections
 import gc
 import json
 import os
@@ -266,6 +267,46 @@ def main():
     phases = dict(head["phases_ms"])
     dev_ms = sum(phases.values())
 
+    # Pipelined throughput: the next request is started (validated, planned,
+    # its plan uploaded and its pass enqueued) before the previous one is
+    # finished, so the host's per-request work runs while the device works.
+    # Each in-flight request has its own KV buffer; every request does the
+    # whole single pass and its readout.
+    pipelined = None
+    if "single-pass" in modes:
+        depth = 2
+        kvs = [kv] + [torch.empty_like(kv) for _ in range(depth - 1)]
+
+        def run_pipelined(n):
+            pend, outs = collections.deque(), []
+            for i in range(n):
+                st = model.new_state(len(req.prefix), kvs[i % depth])
+                pend.append((model.extend_decide_start(st, prompt, schema), st))
+                if len(pend) == depth:
+                    p_, s_ = pend.popleft()
+                    outs.append(p_.finish())
+                    s_.close()
+            while pend:
+                p_, s_ = pend.popleft()
+                outs.append(p_.finish())
+                s_.close()
+            return outs
+
+        run_pipelined(args.warmup)
+        torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
+        t0 = time.perf_counter()
+        pouts = run_pipelined(args.steps)
+        torch.cuda.synchronize()
+        pl_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        gc.enable()
+        ref_out = modes["single-pass"]["out"]
+        same = all(np.array_equal(o[k], ref_out[k]) for o in pouts for k in ("prob", "mass", "argmax"))
+        pipelined = {"depth": depth, "ms_per_request": round(pl_ms, 4), "fields_per_s": round(nf / (pl_ms / 1e3), 2),
+                     "same_results_as_one_at_a_time": bool(same)}
+        print(f"# pipelined (depth {depth}): {pl_ms:.3f} ms/request", file=sys.stderr, flush=True)
+
     # Warm requests: the prefix's first tokens are a cached head; each request
     # forks it, appends its own input tokens and decides (one extend + one
     # branch pass), or runs the first-field round on top (decide field 0,
@@ -379,14 +420,17 @@ def main():
         out["readout"] = {"ms": ro, "bytes": ro_bytes, "GB/s": round(ro_bytes / ro / 1e6, 1),
                           "hbm_frac": round(ro_bytes / ro / 1e6 / HBM_PEAK_GBS, 4)}
         return out
+    # whole-job throughput: the pipelined loop where it ran (every request
+    # still does all of its work), else the headline mode's steps
+    thr_ms = pipelined["ms_per_request"] if pipelined else ms_per_step
     res = {
         "metric": "schema fields decided/sec + p50 28-field request ms, 1.5B-shaped bf16",
-        "value": round(nf / (ms_per_step / 1e3), 2),
+        "value": round(nf / (thr_ms / 1e3), 2),
         "unit": "fields/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(thr_ms, 4),
         "p50_request_ms": round(p50, 4),
         "p90_request_ms": round(p90, 4),
         "higher_is_better": True,
@@ -398,7 +442,10 @@ def main():
                                f"prefix, {nf} fields, {Tb} branch tokens, {R} readouts, batch 1",
                    "layers": sh.n_layers, "prefix_tokens": len(req.prefix), "fields": nf,
                    "branch_tokens": Tb, "readouts": R, "mode": mode,
-                   "schema": "marshalled to C arrays once; validated and planned on every request"},
+                   "schema": "marshalled to C arrays once; validated and planned on every request",
+                   "throughput": (f"{pipelined['depth']} single-pass requests in flight (start/finish calls)"
+                                  if pipelined else f"{mode} requests one at a time"),
+                   "latency": f"{mode} requests one at a time"},
         "phases_ms": phases,
         "device_fields_per_s": round(nf / (dev_ms / 1e3), 2),
         "passes": dict({"fused": 1} if mode == "single-pass" else {"prefill": 1, "branch": 1},
@@ -413,6 +460,9 @@ def main():
                                                             "launches", "bound")} for c, e in kernels.items()},
         "kernel_timed_ms_per_step": round(timed_ms_per_step, 4),
     }
+    if pipelined is not None:
+        res["pipelined"] = pipelined
+        res["one_at_a_time_fields_per_s"] = round(nf / (ms_per_step / 1e3), 2)
     if token_by_token is not None:
         res["token_by_token"] = token_by_token
     if warm is not None:

@@ -22,10 +22,12 @@ PCD_OK = 0
 ERROR_NAMES = {-1: "ARG", -2: "TOKEN", -3: "NCAND", -4: "EMPTY", -5: "DUP", -6: "PREFIX", -7: "CAP",
                -8: "STATE", -9: "DEVICE", -10: "NOMEM"}
 DTYPE_F32, DTYPE_BF16 = 0, 1
+MAX_PENDING = 4  # started, unfinished calls one model holds at most
 
 EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_prefill_many",
            "pcd_extend",
            "pcd_fork", "pcd_state_tokens", "pcd_new_state", "pcd_decide", "pcd_extend_decide",
+           "pcd_extend_decide_start", "pcd_finish",
            "pcd_decide_sequenced", "pcd_decide_many",
            "pcd_debug_plan", "pcd_get_stats",
            "pcd_free_state", "pcd_free_model", "pcd_last_error", "pcd_set_kernel_timing", "pcd_get_kernel_times")
@@ -153,6 +155,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pcd_new_state": (c_int32, [c_void_p, c_void_p, c_size_t, P(c_void_p)]),
         "pcd_extend_decide": (c_int32, [c_void_p, P(c_int32), c_int32, P(pcd_field), c_int32, P(pcd_candidate),
                                         c_int32, c_float, P(pcd_outputs), c_void_p]),
+        "pcd_extend_decide_start": (c_int32, [c_void_p, P(c_int32), c_int32, P(pcd_field), c_int32,
+                                              P(pcd_candidate), c_int32, c_float, P(pcd_outputs), c_void_p,
+                                              P(c_void_p)]),
+        "pcd_finish": (c_int32, [c_void_p]),
         "pcd_decide_sequenced": (c_int32, [c_void_p, P(pcd_field), c_int32, P(pcd_candidate), c_int32, c_int32,
                                            c_float, P(pcd_outputs), c_void_p]),
         "pcd_decide": (c_int32, [c_void_p, P(pcd_field), c_int32, P(pcd_candidate), c_int32, c_float,
@@ -375,6 +381,28 @@ class PcdState:
             pass
 
 
+class PendingDecide:
+    """A started extend_decide call: finish() waits for it and returns its
+    results (the arrays the library fills)."""
+
+    def __init__(self, model: "PcdModel", handle: c_void_p, result: dict):
+        self.model, self.handle, self.result = model, handle, result
+
+    def finish(self) -> dict:
+        if self.handle is None:
+            raise RuntimeError("already finished")
+        h, self.handle = self.handle, None
+        _check(self.model.lib.pcd_finish(h))
+        return self.result
+
+    def __del__(self):
+        if getattr(self, "handle", None) is not None:
+            try:
+                self.model.lib.pcd_finish(self.handle)
+            except Exception:
+                pass
+
+
 class PcdModel:
     """A model over device weights (torch tensors) and a torch-allocated
     workspace.  `config` holds the pcd_config fields, `limits` the
@@ -469,6 +497,21 @@ class PcdModel:
                                           _stream_handle(self.torch)))
         state.n_tokens = int(self.lib.pcd_state_tokens(state.handle))
         return d
+
+    def extend_decide_start(self, state: PcdState, tokens: Sequence[int], fields,
+                            temperature: float = 1.0) -> "PendingDecide":
+        """pcd_extend_decide_start: enqueue the same work as extend_decide and
+        return at once; PendingDecide.finish() waits and returns the results."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        mr = _Marshalled([fields])
+        d, o = _result_arrays(mr.n_cands[0], mr.n_fields[0])
+        rq = mr.reqs[0]
+        h = c_void_p()
+        _check(self.lib.pcd_extend_decide_start(state.handle, _i32p(t), t.size, rq.fields, rq.n_fields,
+                                                rq.candidates, rq.n_candidates, temperature, ctypes.byref(o),
+                                                _stream_handle(self.torch), ctypes.byref(h)))
+        state.n_tokens = int(self.lib.pcd_state_tokens(state.handle))
+        return PendingDecide(self, h, d)
 
     def _outputs(self, mr, r, requests, debug_prefix):
         """Result arrays of request r and their pcd_outputs view (debug: sized

@@ -34,6 +34,7 @@ constexpr int ATT_ROWS = 64;          // query rows per attention workgroup
 constexpr int SPLITK_MAX = 8;
 constexpr int SPLITK_ROWS = 1024;     // split-K is only used below this many rows
 constexpr uint64_t STATE_MAGIC = 0x70636473746174ull;
+constexpr uint64_t PENDING_MAGIC = 0x70636470656e64ull;
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
@@ -159,8 +160,15 @@ struct pcd_model {
     const float *final_norm = nullptr;
     std::vector<const void *> wq, wk, wv, wo, wg, wu, wd;
     std::vector<const float *> an, mn;
-    char *plan_host = nullptr;  // pinned staging for the plan upload
-    char *outs_host = nullptr;  // pinned staging for the results
+    char *plan_host = nullptr;  // pinned staging for a prefill's plan upload
+    // Decide calls in flight: each holds one slot, with its own pinned plan
+    // and result staging and its events, from its start to its finish.
+    struct Slot {
+        char *plan_host = nullptr, *outs_host = nullptr;
+        hipEvent_t ev[4] = {};  // pass start (plan uploaded), pass end, readout end, results on the host
+        bool busy = false;
+    };
+    Slot slots[PCD_MAX_PENDING];
     hipEvent_t ev[6] = {};  // branch start/end, readout end, prefill start/end, plan upload done
     pcd_stats stats{};
     bool prefill_pending = false;  // last_prefill_ms not yet read from ev[3], ev[4]
@@ -217,6 +225,19 @@ struct pcd_state {
     void *kv;
     int32_t P;    // tokens held
     int32_t cap;  // tokens per (layer, K|V, KV head) slab of the buffer: its layout stride
+};
+
+// A decide call between its start and its finish: its slot, where the
+// results go and how they are laid out in the slot's staging.
+struct pcd_pending {
+    uint64_t magic;
+    pcd_model *m;
+    int slot;
+    hipStream_t st;
+    int n_req, Tb, R, G;
+    std::vector<pcd_outputs> outs;
+    std::vector<int32_t> r_cand, r_field, r_ro, r_g;
+    size_t o_prob, o_ls, o_mass, o_marg, o_arg, o_lse, o_z;
 };
 
 namespace {
@@ -425,9 +446,15 @@ int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_wei
         pcd_free_model(m);
         return fail(code, msg);
     };
-    if (hipHostMalloc((void **)&m->plan_host, lay.plan_bytes, hipHostMallocDefault) != hipSuccess ||
-        hipHostMalloc((void **)&m->outs_host, lay.outs_bytes, hipHostMallocDefault) != hipSuccess)
+    if (hipHostMalloc((void **)&m->plan_host, lay.plan_bytes, hipHostMallocDefault) != hipSuccess)
         return cleanup(PCD_E_DEVICE, "pinned staging allocation failed");
+    for (auto &sl : m->slots) {
+        if (hipHostMalloc((void **)&sl.plan_host, lay.plan_bytes, hipHostMallocDefault) != hipSuccess ||
+            hipHostMalloc((void **)&sl.outs_host, lay.outs_bytes, hipHostMallocDefault) != hipSuccess)
+            return cleanup(PCD_E_DEVICE, "pinned staging allocation failed");
+        for (auto &e : sl.ev)
+            if (hipEventCreate(&e) != hipSuccess) return cleanup(PCD_E_DEVICE, "event creation failed");
+    }
     for (auto &e : m->ev)
         if (hipEventCreate(&e) != hipSuccess) return cleanup(PCD_E_DEVICE, "event creation failed");
     // RoPE table: (cos, sin) of pos * theta^(-2j/hd), computed in double
@@ -858,8 +885,10 @@ namespace {
 // buffer; the branch rows then see the whole extended prefix.  One pass thus
 // does the work of pcd_extend followed by pcd_decide, streaming every weight
 // matrix once.
-int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float T, pcd_outputs *outs,
-                void *stream, const int32_t *new_tok, int32_t n_new) {
+// The pass is enqueued on `stream` and the call returns with a pending
+// handle; decide_finish waits for it and writes the outputs.
+int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float T, const pcd_outputs *outs,
+                 void *stream, const int32_t *new_tok, int32_t n_new, pcd_pending **pend) {
     if (!states || !reqs || !outs || n_req <= 0) return fail(PCD_E_ARG, "null argument or no requests");
     if (!(T > 0.f) || !std::isfinite(T)) return fail(PCD_E_ARG, "temperature must be positive and finite");
     for (int r = 0; r < n_req; ++r)
@@ -962,7 +991,13 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
     if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    Packer pk{m->plan_host, m->ws + m->L.plan, m->L.plan_bytes};
+    int si = -1;
+    for (int k = 0; k < PCD_MAX_PENDING && si < 0; ++k)
+        if (!m->slots[k].busy) si = k;
+    if (si < 0)
+        return fail(PCD_E_CAP, std::to_string(PCD_MAX_PENDING) + " decide calls of this model are already in flight");
+    auto &slot = m->slots[si];
+    Packer pk{slot.plan_host, m->ws + m->L.plan, m->L.plan_bytes};
     std::vector<int32_t> toks(M), poss(M);
     for (int i = 0; i < n_new; ++i) {
         toks[i] = new_tok[i];
@@ -1020,8 +1055,8 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                  o_z = oslot((size_t)G * 4);
     if (oo > m->L.outs_bytes) return fail(PCD_E_CAP, "output staging overflow");
 
-    HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
-    HIP_TRY(hipEventRecord(m->ev[0], st));
+    HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, slot.plan_host, pk.off, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipEventRecord(slot.ev[0], st));
     float *x = reinterpret_cast<float *>(m->ws + m->L.x);
     m->tbegin(PCD_KC_OTHER, st);
     embed(c.dtype, d_tok, M, m->embed, d, x, m->an[0], c.rms_eps, m->ws + m->L.h, st);
@@ -1097,7 +1132,7 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
                                n_keep);
         if (rc != PCD_OK) return rc;
     }
-    HIP_TRY(hipEventRecord(m->ev[1], st));
+    HIP_TRY(hipEventRecord(slot.ev[1], st));
     // readout: final norm of the readout rows, LM head with online log-sum-exp, combine
     void *hr = m->ws + m->L.hr;
     m->tbegin(PCD_KC_OTHER, st);
@@ -1146,40 +1181,93 @@ int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req
     cc.argmax = reinterpret_cast<int32_t *>(ob + o_arg);
     combine(cc, st);
     m->tend(st);
-    HIP_TRY(hipEventRecord(m->ev[2], st));
+    HIP_TRY(hipEventRecord(slot.ev[2], st));
     HIP_TRY(hipGetLastError());
-    HIP_TRY(hipMemcpyAsync(m->outs_host, ob, oo, hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipStreamSynchronize(st));
-    m->tcollect();
-    m->settle_prefill();
+    HIP_TRY(hipMemcpyAsync(slot.outs_host, ob, oo, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipEventRecord(slot.ev[3], st));
 
-    const char *oh = m->outs_host;
-    for (int r = 0; r < n_req; ++r) {
-        const pcd_outputs &o = outs[r];
-        const int c0 = p.r_cand[r], nc = p.r_cand[r + 1] - c0;
-        const int f0 = p.r_field[r], nf = p.r_field[r + 1] - f0;
-        const int r0 = p.r_ro[r], nr = p.r_ro[r + 1] - r0;
-        const int g0 = p.r_g[r], ng = p.r_g[r + 1] - g0;
-        std::memcpy(o.cand_prob, oh + o_prob + (size_t)c0 * 4, (size_t)nc * 4);
-        if (o.cand_logscore) std::memcpy(o.cand_logscore, oh + o_ls + (size_t)c0 * 4, (size_t)nc * 4);
-        std::memcpy(o.field_mass, oh + o_mass + (size_t)f0 * 4, (size_t)nf * 4);
-        std::memcpy(o.field_margin, oh + o_marg + (size_t)f0 * 4, (size_t)nf * 4);
-        std::memcpy(o.field_argmax, oh + o_arg + (size_t)f0 * 4, (size_t)nf * 4);
-        if (o.readout_lse) std::memcpy(o.readout_lse, oh + o_lse + (size_t)r0 * 4, (size_t)nr * 4);
-        if (o.gather_logit) std::memcpy(o.gather_logit, oh + o_z + (size_t)g0 * 4, (size_t)ng * 4);
+    auto *pd = new (std::nothrow) pcd_pending{};
+    if (!pd) {
+        (void)hipEventSynchronize(slot.ev[3]);
+        return fail(PCD_E_NOMEM, "pending call allocation");
     }
-    float ms_b = 0.f, ms_r = 0.f;
-    (void)hipEventElapsedTime(&ms_b, m->ev[0], m->ev[1]);
-    (void)hipEventElapsedTime(&ms_r, m->ev[1], m->ev[2]);
+    pd->magic = PENDING_MAGIC;
+    pd->m = m;
+    pd->slot = si;
+    pd->st = st;
+    pd->n_req = n_req;
+    pd->Tb = Tb;
+    pd->R = R;
+    pd->G = G;
+    pd->outs.assign(outs, outs + n_req);
+    pd->r_cand = p.r_cand;
+    pd->r_field = p.r_field;
+    pd->r_ro = p.r_ro;
+    pd->r_g = p.r_g;
+    pd->o_prob = o_prob;
+    pd->o_ls = o_ls;
+    pd->o_mass = o_mass;
+    pd->o_marg = o_marg;
+    pd->o_arg = o_arg;
+    pd->o_lse = o_lse;
+    pd->o_z = o_z;
+    slot.busy = true;
+    // the new tokens are the state's from now on: later calls on the stream see them
     if (n_new > 0) states[0]->P += n_new;
     m->stats.branch_passes += 1;
+    *pend = pd;
+    return PCD_OK;
+}
+
+// Wait for a started call, copy its results out of its slot, free the slot.
+int decide_finish(pcd_pending *pd) {
+    if (!pd || pd->magic != PENDING_MAGIC) return fail(PCD_E_ARG, "invalid pending call");
+    pcd_model *m = pd->m;
+    auto &slot = m->slots[pd->slot];
+    pd->magic = 0;
+    const hipError_t e = hipEventSynchronize(slot.ev[3]);
+    if (m->timing && e == hipSuccess) {
+        (void)hipStreamSynchronize(pd->st);  // every timed kernel of the stream has run
+        m->tcollect();
+    }
+    m->settle_prefill();
+    const char *oh = slot.outs_host;
+    if (e == hipSuccess)
+        for (int r = 0; r < pd->n_req; ++r) {
+            const pcd_outputs &o = pd->outs[r];
+            const int c0 = pd->r_cand[r], nc = pd->r_cand[r + 1] - c0;
+            const int f0 = pd->r_field[r], nf = pd->r_field[r + 1] - f0;
+            const int r0 = pd->r_ro[r], nr = pd->r_ro[r + 1] - r0;
+            const int g0 = pd->r_g[r], ng = pd->r_g[r + 1] - g0;
+            std::memcpy(o.cand_prob, oh + pd->o_prob + (size_t)c0 * 4, (size_t)nc * 4);
+            if (o.cand_logscore) std::memcpy(o.cand_logscore, oh + pd->o_ls + (size_t)c0 * 4, (size_t)nc * 4);
+            std::memcpy(o.field_mass, oh + pd->o_mass + (size_t)f0 * 4, (size_t)nf * 4);
+            std::memcpy(o.field_margin, oh + pd->o_marg + (size_t)f0 * 4, (size_t)nf * 4);
+            std::memcpy(o.field_argmax, oh + pd->o_arg + (size_t)f0 * 4, (size_t)nf * 4);
+            if (o.readout_lse) std::memcpy(o.readout_lse, oh + pd->o_lse + (size_t)r0 * 4, (size_t)nr * 4);
+            if (o.gather_logit) std::memcpy(o.gather_logit, oh + pd->o_z + (size_t)g0 * 4, (size_t)ng * 4);
+        }
+    float ms_b = 0.f, ms_r = 0.f;
+    (void)hipEventElapsedTime(&ms_b, slot.ev[0], slot.ev[1]);
+    (void)hipEventElapsedTime(&ms_r, slot.ev[1], slot.ev[2]);
     m->stats.last_branch_ms = ms_b;
     m->stats.last_readout_ms = ms_r;
-    m->stats.last_branch_tokens = Tb;
-    m->stats.last_readouts = R;
-    m->stats.last_gathers = G;
-    m->stats.last_requests = n_req;
+    m->stats.last_branch_tokens = pd->Tb;
+    m->stats.last_readouts = pd->R;
+    m->stats.last_gathers = pd->G;
+    m->stats.last_requests = pd->n_req;
+    slot.busy = false;
+    delete pd;
+    if (e != hipSuccess) return fail(PCD_E_DEVICE, std::string("decide pass: ") + hipGetErrorString(e));
     return PCD_OK;
+}
+
+int decide_impl(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float T, const pcd_outputs *outs,
+                void *stream, const int32_t *new_tok, int32_t n_new) {
+    pcd_pending *pd = nullptr;
+    const int rc = decide_start(states, reqs, n_req, T, outs, stream, new_tok, n_new, &pd);
+    if (rc != PCD_OK) return rc;
+    return decide_finish(pd);
 }
 
 }  // namespace
@@ -1196,6 +1284,17 @@ int pcd_extend_decide(pcd_state *s, const int32_t *tokens, int32_t n_tokens, con
     pcd_request r{fields, n_fields, candidates, n_candidates};
     return decide_impl(&s, &r, 1, temperature, out, stream, tokens, n_tokens);
 }
+
+int pcd_extend_decide_start(pcd_state *s, const int32_t *tokens, int32_t n_tokens, const pcd_field *fields,
+                            int32_t n_fields, const pcd_candidate *candidates, int32_t n_candidates,
+                            float temperature, const pcd_outputs *out, void *stream, pcd_pending **p) {
+    if (!p) return fail(PCD_E_ARG, "null argument");
+    if (n_tokens < 0) return fail(PCD_E_ARG, "negative token count");
+    pcd_request r{fields, n_fields, candidates, n_candidates};
+    return decide_start(&s, &r, 1, temperature, out, stream, tokens, n_tokens, p);
+}
+
+int pcd_finish(pcd_pending *p) { return decide_finish(p); }
 
 int pcd_new_state(pcd_model *m, void *kv_buf, size_t kv_bytes, pcd_state **out) {
     if (!m || !kv_buf || !out) return fail(PCD_E_ARG, "null argument");
@@ -1316,7 +1415,13 @@ void pcd_free_model(pcd_model *m) {
     if (!m) return;
     m->settle_prefill();
     if (m->plan_host) (void)hipHostFree(m->plan_host);
-    if (m->outs_host) (void)hipHostFree(m->outs_host);
+    for (auto &sl : m->slots) {
+        if (sl.busy && sl.ev[3]) (void)hipEventSynchronize(sl.ev[3]);  // an unfinished call's copies end first
+        if (sl.plan_host) (void)hipHostFree(sl.plan_host);
+        if (sl.outs_host) (void)hipHostFree(sl.outs_host);
+        for (auto &e : sl.ev)
+            if (e) (void)hipEventDestroy(e);
+    }
     for (auto &e : m->ev)
         if (e) (void)hipEventDestroy(e);
     for (auto &e : m->tev) (void)hipEventDestroy(e);

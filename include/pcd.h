@@ -196,6 +196,11 @@ typedef struct {
 
 typedef struct pcd_model pcd_model;  /* opaque, library-owned host object */
 typedef struct pcd_state pcd_state;  /* opaque: a prefilled prefix over a caller-owned KV buffer */
+typedef struct pcd_pending pcd_pending;  /* opaque: a started decide call, until pcd_finish */
+
+/* Decide calls of one model that may be in flight at once (started and not
+ * yet finished). */
+#define PCD_MAX_PENDING 4
 
 /* Bytes of device workspace a model with this config and these limits needs.
  * Returns 0 on invalid arguments. */
@@ -302,6 +307,29 @@ int pcd_decide(pcd_state *s, const pcd_field *fields, int32_t n_fields, const pc
 int pcd_extend_decide(pcd_state *s, const int32_t *tokens, int32_t n_tokens, const pcd_field *fields,
                       int32_t n_fields, const pcd_candidate *candidates, int32_t n_candidates, float temperature,
                       pcd_outputs *out, void *stream);
+
+/* pcd_extend_decide in two halves, so that a caller can prepare its next
+ * request while the device runs this one (the pages' engines keep one request
+ * in flight; a server keeps the device busy across requests).
+ *
+ * pcd_extend_decide_start validates, plans and enqueues exactly the work of
+ * pcd_extend_decide on `stream`, then returns *p without waiting for the
+ * device.  The state holds the new tokens at once, so later calls on the
+ * same stream may use it.  The arrays of *out (copied by value) receive the
+ * results only in pcd_finish(*p); until then they must stay valid and
+ * unread.  The token, field and candidate arrays are not read after the call
+ * returns.  At most PCD_MAX_PENDING calls of a model are in flight: one more
+ * fails with PCD_E_CAP before any device work.  Other errors as for
+ * pcd_extend_decide.
+ *
+ * pcd_finish waits for the call's results, writes them to its output arrays,
+ * updates the model's statistics and frees p (also on error).  Calls may be
+ * finished in any order.  Every started call must be finished before
+ * pcd_free_model. */
+int pcd_extend_decide_start(pcd_state *s, const int32_t *tokens, int32_t n_tokens, const pcd_field *fields,
+                            int32_t n_fields, const pcd_candidate *candidates, int32_t n_candidates,
+                            float temperature, const pcd_outputs *out, void *stream, pcd_pending **p);
+int pcd_finish(pcd_pending *p);
 
 /* An empty state (0 tokens) over the caller's device buffer kv_buf (capacity
  * as for pcd_prefill), for pcd_extend / pcd_extend_decide to fill: a cold

@@ -288,3 +288,43 @@ def test_bf16_two_layer_fused_cold(q15_l2):
         _compare(f"q15-L2-fused-{name}", got, ref, ref.plan, "bf16")
         st.close()
         m.close()
+
+
+def test_tiny_started_calls_match_extend_decide(tiny_w):
+    """extend_decide_start + finish returns what extend_decide does, bit for
+    bit, with MAX_PENDING calls in flight on as many states and finished in
+    reverse order; one more start while they are pending is refused (CAP)
+    and leaves its state as it was."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(35)
+    n = cpd.MAX_PENDING + 1
+    prefixes = [_tokens(rng, sh.vocab_size, 40 + 9 * i) for i in range(n)]
+    reqs = [pi.random_trie_fields(960 + i, sh.vocab_size, 2 + i % 2) for i in range(n)]
+    p_all = cpd.debug_plan(sh.vocab_size, sh.max_seq, [len(p) for p in prefixes], reqs)
+    m = _model(sh, tiny_w, [len(p) for p in prefixes], reqs, max(map(len, prefixes)) + len(p_all["tok"]))
+    want = []
+    for p, f in zip(prefixes, reqs):
+        st = m.new_state(len(p))
+        want.append(m.extend_decide(st, p, f))
+        st.close()
+    states = [m.new_state(len(p)) for p in prefixes]
+    pend = [m.extend_decide_start(states[i], prefixes[i], reqs[i]) for i in range(n - 1)]
+    with pytest.raises(cpd.PcdError) as e:
+        m.extend_decide_start(states[-1], prefixes[-1], reqs[-1])
+    assert e.value.name == "CAP"
+    assert int(m.lib.pcd_state_tokens(states[-1].handle)) == 0
+    got = [None] * n
+    for i in reversed(range(n - 1)):
+        got[i] = pend[i].finish()
+    with pytest.raises(RuntimeError):
+        pend[0].finish()
+    # the refused call goes through once a slot is free
+    got[-1] = m.extend_decide_start(states[-1], prefixes[-1], reqs[-1]).finish()
+    for i in range(n):
+        assert states[i].n_tokens == len(prefixes[i])
+        for k in ("prob", "logscore", "mass", "margin", "argmax"):
+            assert np.array_equal(got[i][k], want[i][k]), (i, k)
+    assert m.stats()["branch_passes"] == 2 * n
+    for st in states:
+        st.close()
+    m.close()

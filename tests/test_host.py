@@ -31,6 +31,11 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_binding_constants_match_the_header():
+    hdr = open(os.path.join(ROOT, "include", "pcd.h")).read()
+    assert int(re.search(r"#define PCD_MAX_PENDING (\d+)", hdr).group(1)) == cpd.MAX_PENDING
+
+
 def _compare_plans(requests, V, max_seq=1 << 20):
     lens = [len(p) for p, _ in requests]
     ours = cpd.debug_plan(V, max_seq, lens, [f for _, f in requests])
