@@ -37,7 +37,11 @@
  *     use it.  Handles are library-owned host objects, freed with pcd_free_*.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call that
  *     takes a stream enqueues its device work there and returns after that
- *     stream has drained: the API is synchronous.
+ *     stream has drained, except pcd_prefill, pcd_prefill_many and
+ *     pcd_extend_decide_start, which return once their work is enqueued.
+ *   - A model's passes share its workspace: while a call of the model is
+ *     still running on the device, the model's other calls go on the same
+ *     stream.
  *   - A model is used from one host thread at a time.
  */
 #ifndef PCD_H
