@@ -12,6 +12,7 @@ from itertools import chain
 import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
 from typing import Dict, List, Optional, Sequence
+import weakref
 
 import numpy as np
 
@@ -350,6 +351,7 @@ class PcdState:
 
     def __init__(self, model: "PcdModel", handle: c_void_p, kv, n_tokens: int):
         self.model, self.handle, self.kv, self.n_tokens = model, handle, kv, n_tokens
+        model._states.add(self)
 
     def extend(self, tokens: Sequence[int]) -> "PcdState":
         """pcd_extend: append tokens (the buffer must have the capacity)."""
@@ -387,11 +389,13 @@ class PendingDecide:
 
     def __init__(self, model: "PcdModel", handle: c_void_p, result: dict):
         self.model, self.handle, self.result = model, handle, result
+        model._pending.add(self)
 
     def finish(self) -> dict:
         if self.handle is None:
             raise RuntimeError("already finished")
         h, self.handle = self.handle, None
+        self.model._pending.discard(self)
         _check(self.model.lib.pcd_finish(h))
         return self.result
 
@@ -412,6 +416,8 @@ class PcdModel:
         import torch
         self.torch = torch
         self.lib = load_library()
+        self._pending = weakref.WeakSet()  # started, unfinished calls (PendingDecide)
+        self._states = weakref.WeakSet()   # open states (PcdState)
         self.cfg = pcd_config(**config)
         self.lim = pcd_limits(**limits)
         L = self.cfg.n_layers
@@ -577,6 +583,15 @@ class PcdModel:
 
     def close(self):
         if getattr(self, "handle", None):
+            # the library's handles of started calls point into the model
+            for p in list(self._pending):
+                if p.handle is not None:
+                    h, p.handle = p.handle, None
+                    self.lib.pcd_finish(h)
+            self._pending.clear()
+            # the library frees states before their model
+            for st in list(self._states):
+                st.close()
             self.lib.pcd_free_model(self.handle)
             self.handle = None
 

@@ -325,6 +325,8 @@ def test_tiny_started_calls_match_extend_decide(tiny_w):
         for k in ("prob", "logscore", "mass", "margin", "argmax"):
             assert np.array_equal(got[i][k], want[i][k]), (i, k)
     assert m.stats()["branch_passes"] == 2 * n
-    for st in states:
-        st.close()
+    # a call still pending when the model is closed is finished first
+    # and the states still open are freed before the model
+    late = m.extend_decide_start(states[0], [], reqs[0])
     m.close()
+    assert late.handle is None and all(st.handle is None for st in states)
