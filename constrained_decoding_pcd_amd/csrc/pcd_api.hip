@@ -37,6 +37,8 @@ constexpr uint64_t STATE_MAGIC = 0x70636473746174ull;
 constexpr uint64_t PENDING_MAGIC = 0x70636470656e64ull;
 
 size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+// device buffers are read and written in 16-byte vectors
+bool misaligned(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
 
 // Attention workgroups per launch (about one per compute unit: more splits
 // cost more in partial writes and the merge than they gain in parallelism,
@@ -419,6 +421,13 @@ int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_wei
         if (!w->attn_norm[l] || !w->mlp_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->w_gate[l] ||
             !w->w_up[l] || !w->w_down[l])
             return fail(PCD_E_ARG, "null per-layer weight pointer");
+    bool mis = misaligned(w->embed) || misaligned(w->lm_head) || misaligned(w->final_norm) ||
+               reinterpret_cast<uintptr_t>(workspace) % 256 != 0;
+    for (int l = 0; l < L; ++l)
+        mis = mis || misaligned(w->attn_norm[l]) || misaligned(w->mlp_norm[l]) || misaligned(w->wq[l]) ||
+              misaligned(w->wk[l]) || misaligned(w->wv[l]) || misaligned(w->wo[l]) || misaligned(w->w_gate[l]) ||
+              misaligned(w->w_up[l]) || misaligned(w->w_down[l]);
+    if (mis) return fail(PCD_E_ARG, "weights must be 16-byte aligned and the workspace 256-byte aligned");
     Layout lay = layout(*cfg, *lim);
     if (ws_bytes < lay.total)
         return fail(PCD_E_CAP, "workspace of " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(lay.total));
@@ -736,7 +745,8 @@ int pcd_prefill_many(pcd_model *m, int32_t n_seqs, const int32_t *tokens, const 
     std::vector<std::pair<uint64_t, uint64_t>> spans(n_seqs);
     for (int r = 0; r < n_seqs; ++r) {
         if (lens[r] <= 0) return fail(PCD_E_ARG, "sequence " + std::to_string(r) + " is empty");
-        if (!kv_bufs[r]) return fail(PCD_E_ARG, "null KV buffer for sequence " + std::to_string(r));
+        if (!kv_bufs[r] || misaligned(kv_bufs[r]))
+            return fail(PCD_E_ARG, "null or misaligned KV buffer for sequence " + std::to_string(r));
         if (lens[r] > c.max_seq) return fail(PCD_E_CAP, "sequence " + std::to_string(r) + " exceeds max_seq");
         if (kv_bytes[r] < pcd_state_bytes(m, lens[r]))
             return fail(PCD_E_CAP, "KV buffer of sequence " + std::to_string(r) + " too small");
@@ -776,6 +786,7 @@ int pcd_prefill_many(pcd_model *m, int32_t n_seqs, const int32_t *tokens, const 
 int pcd_prefill(pcd_model *m, const int32_t *tokens, int32_t n, void *kv_buf, size_t kv_bytes, void *stream,
                 pcd_state **out) {
     if (!m || !tokens || !kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+    if (misaligned(kv_buf)) return fail(PCD_E_ARG, "the KV buffer must be 16-byte aligned");
     const pcd_config &c = m->cfg;
     if (n <= 0) return fail(PCD_E_ARG, "empty prefix");
     if (n > m->lim.max_prefill_tokens || n > c.max_seq)
@@ -819,6 +830,7 @@ int pcd_extend(pcd_state *s, const int32_t *tokens, int32_t n, void *stream) {
 int pcd_fork(const pcd_state *s, void *kv_buf, size_t kv_bytes, void *stream, pcd_state **out) {
     if (!s || s->magic != STATE_MAGIC) return fail(PCD_E_STATE, "invalid state handle");
     if (!kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+    if (misaligned(kv_buf)) return fail(PCD_E_ARG, "the KV buffer must be 16-byte aligned");
     pcd_model *m = s->m;
     if (kv_bytes < pcd_state_bytes(m, s->P)) return fail(PCD_E_CAP, "KV buffer too small");
     const int32_t cap = (int32_t)std::min<size_t>(kv_bytes / per_token_bytes(m), (size_t)m->cfg.max_seq);
@@ -1298,6 +1310,7 @@ int pcd_finish(pcd_pending *p) { return decide_finish(p); }
 
 int pcd_new_state(pcd_model *m, void *kv_buf, size_t kv_bytes, pcd_state **out) {
     if (!m || !kv_buf || !out) return fail(PCD_E_ARG, "null argument");
+    if (misaligned(kv_buf)) return fail(PCD_E_ARG, "the KV buffer must be 16-byte aligned");
     if (kv_bytes < per_token_bytes(m)) return fail(PCD_E_CAP, "KV buffer smaller than one token");
     const int32_t cap = (int32_t)std::min<size_t>(kv_bytes / per_token_bytes(m), (size_t)m->cfg.max_seq);
     pcd_state *s = new (std::nothrow) pcd_state{STATE_MAGIC, m, kv_buf, 0, cap};

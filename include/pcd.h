@@ -106,7 +106,9 @@ typedef struct {
 /* Device pointers to the weights, elements of cfg.dtype (bf16 = raw 16-bit
  * patterns), every matrix [out][in] row-major.  The per-layer fields are HOST
  * arrays of n_layers DEVICE pointers; the library copies the arrays.  Norm
- * weights are fp32 vectors of d_model. */
+ * weights are fp32 vectors of d_model.  Every pointer is 16-byte aligned
+ * (PCD_E_ARG otherwise), as are KV buffers; the workspace is 256-byte
+ * aligned. */
 typedef struct {
     const void *embed;          /* [vocab][d] */
     const void *lm_head;        /* [vocab][d]; NULL when tied_lm_head */

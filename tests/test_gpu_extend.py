@@ -330,3 +330,18 @@ def test_tiny_started_calls_match_extend_decide(tiny_w):
     late = m.extend_decide_start(states[0], [], reqs[0])
     m.close()
     assert late.handle is None and all(st.handle is None for st in states)
+
+
+def test_misaligned_buffers_are_refused(tiny_w):
+    """Device buffers are accessed in 16-byte vectors: a KV buffer off that
+    alignment is refused before any device work (PCD_E_ARG)."""
+    sh = pi.SHAPES["tiny"]
+    fields = pi.random_trie_fields(970, sh.vocab_size, 2)
+    m = _model(sh, tiny_w, [16], [fields], 16)
+    kv = torch.empty(m.state_bytes(16) + 16, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(cpd.PcdError) as e:
+        m.new_state(16, kv[8:])
+    assert e.value.name == "ARG"
+    st = m.new_state(16, kv[16:])
+    assert st.n_tokens == 0
+    m.close()
