@@ -325,6 +325,20 @@ def test_tiny_started_calls_match_extend_decide(tiny_w):
         for k in ("prob", "logscore", "mass", "margin", "argmax"):
             assert np.array_equal(got[i][k], want[i][k]), (i, k)
     assert m.stats()["branch_passes"] == 2 * n
+    # a prefill enqueued between started calls (the workspace is shared; the
+    # stream orders the passes): the same results as the calls one by one
+    hs = m.prefill(prefixes[1])
+    want_b = m.extend_decide(hs, [], reqs[1])
+    hs.close()
+    sa = m.new_state(len(prefixes[0]))
+    pa = m.extend_decide_start(sa, prefixes[0], reqs[0])
+    hb = m.prefill(prefixes[1])
+    pb = m.extend_decide_start(hb, [], reqs[1])
+    got_b, got_a = pb.finish(), pa.finish()
+    for k in ("prob", "logscore", "mass", "margin", "argmax"):
+        assert np.array_equal(got_a[k], want[0][k]) and np.array_equal(got_b[k], want_b[k]), k
+    sa.close()
+    hb.close()
     # a call still pending when the model is closed is finished first
     # and the states still open are freed before the model
     late = m.extend_decide_start(states[0], [], reqs[0])
