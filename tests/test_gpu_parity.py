@@ -358,6 +358,36 @@ def test_bf16_two_layer_prefill_many(q15_l2):
     m.close()
 
 
+def test_bf16_two_layer_large_prefill_tiles(q15_l2):
+    """Ten prompts of the throughput workload (10 x 1024 = 10,240 rows) in
+    one prefill pass: at this row count the residual GEMMs take 256x256 tiles
+    and gate/up 256-row tiles.  The first, a middle and the last prompt's
+    states are then decided against the oracle (rows at the start, middle and
+    end of the pass)."""
+    sh, w, dec = q15_l2
+    reqs = _reqs(pi.make_workload("cfg3"))[:10]
+    m = _model(sh, w, reqs, max_prefill=sum(len(p) for p, _ in reqs))
+    states = m.prefill_many([p for p, _ in reqs])
+    pick = [0, 5, 9]
+    got = m.decide_many([states[i] for i in pick], [reqs[i][1] for i in pick], debug=True)
+    ref = opcd.decide(dec, [reqs[i] for i in pick])
+    _compare("q15-L2-prefill-10240", got, ref, ref.plan, "bf16")
+    for st in states:
+        st.close()
+    m.close()
+
+
+def test_bf16_two_layer_wide_readout_tiles(q15_l2):
+    """1,100 fields with one-token labels after a 32-token prefix: 1,100
+    readout rows, above which the LM-head GEMM takes 128x256 tiles, the last
+    one ragged at the 151,936-token vocabulary."""
+    sh, w, dec = q15_l2
+    prefix = [int(t) for t in np.random.default_rng(12).integers(0, sh.vocab_size, size=32)]
+    fields = pi.random_trie_fields(1700, sh.vocab_size, 1100, max_cands=3, max_len=1, scaffold_len=(1, 2))
+    got, ref = _run_case("q15-L2-readout-1100", sh, w, [(prefix, fields)], dec=dec)
+    assert len(ref.plan.ro_tok) > 1024
+
+
 def test_bf16_two_layer_cfg2_id_field(q15_l2):
     """2048-token prefix; 3 booleans and one 255-option 3-token ID field whose
     options share their lead token (18 trie readouts)."""
