@@ -359,22 +359,34 @@ def test_bf16_two_layer_prefill_many(q15_l2):
 
 
 def test_bf16_two_layer_large_prefill_tiles(q15_l2):
-    """Ten prompts of the throughput workload (10 x 1024 = 10,240 rows) in
-    one prefill pass: at this row count the residual GEMMs take 256x256 tiles
-    and gate/up 256-row tiles.  The first, a middle and the last prompt's
-    states are then decided against the oracle (rows at the start, middle and
-    end of the pass)."""
+    """Ten prompts of the throughput workload, the last one token longer
+    (10,241 rows), in one prefill pass: at this row count the residual GEMMs
+    take 256x256 tiles and gate/up 256-row tiles, the last row tile holding
+    one row.  The first, a middle and the last prompt's states are then
+    decided against the oracle (rows at the start, middle and end of the
+    pass)."""
     sh, w, dec = q15_l2
     reqs = _reqs(pi.make_workload("cfg3"))[:10]
+    reqs[9] = (list(reqs[9][0]) + [7], reqs[9][1])
     m = _model(sh, w, reqs, max_prefill=sum(len(p) for p, _ in reqs))
     states = m.prefill_many([p for p, _ in reqs])
     pick = [0, 5, 9]
     got = m.decide_many([states[i] for i in pick], [reqs[i][1] for i in pick], debug=True)
     ref = opcd.decide(dec, [reqs[i] for i in pick])
-    _compare("q15-L2-prefill-10240", got, ref, ref.plan, "bf16")
+    _compare("q15-L2-prefill-10241", got, ref, ref.plan, "bf16")
     for st in states:
         st.close()
     m.close()
+
+
+def test_bf16_two_layer_prefill_past_tile_switch(q15_l2):
+    """A 1,025-token prompt: one row past the count where the GEMMs switch
+    to their large-row tiles, so the last 128- and 256-row tiles hold a
+    single row; then the 28-field decide."""
+    sh, w, dec = q15_l2
+    wl = pi.make_workload("cfg3")
+    prefix = list(wl.requests[1].prefix) + [11]
+    _run_case("q15-L2-prefill-1025", sh, w, [(prefix, wl.requests[1].fields)], dec=dec)
 
 
 def test_bf16_two_layer_wide_readout_tiles(q15_l2):
