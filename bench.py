@@ -5,9 +5,11 @@ One step = one whole request through the C ABI: pcd_prefill of the shared
 prefix, then pcd_decide of every field in one batched branch pass + readout.
 Default workload: the Qwen2.5-1.5B-shaped random-init bf16 decoder, a
 512-token prefix and a 28-field schema (10 booleans, 18 four-way enums).
-Prints one JSON line: fields decided per second and p50 request latency,
-the roofline position of the dominant kernel (timed live with hipEvents on
-the library's stream) and the CPU oracle timed on a bounded sample.
+Prints one JSON line: fields decided per second (value: independent
+single-pass requests on three streams at once, one in flight per stream)
+and p50 request latency (one request at a time), the roofline position of
+the dominant kernel (timed live with hipEvents on the library's stream) and
+the CPU oracle timed on a bounded sample.
 """
 import argparse
 import collections
@@ -173,6 +175,9 @@ def main():
     ap.add_argument("--mode", choices=("both", "single-pass", "two-pass"), default="both",
                     help="request modes to time; the faster timed mode is the headline")
     ap.add_argument("--no-token-by-token", action="store_true", help="skip the token-by-token baseline")
+    ap.add_argument("--concurrent-streams", type=int, default=3,
+                    help="streams of the throughput loop (0: skip it; value is then one request at a time). "
+                         "Profiles of kernel durations use 0, so that no two kernels overlap")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -307,6 +312,54 @@ def main():
                      "same_results_as_one_at_a_time": bool(same)}
         print(f"# pipelined (depth {depth}): {pl_ms:.3f} ms/request", file=sys.stderr, flush=True)
 
+    # Concurrent throughput: independent requests on three streams at once,
+    # each stream with its own model (its own workspace and start/finish
+    # slots) over the same device weights, one request in flight per stream.
+    # The kernels of one request fill the compute units that another's leave
+    # idle (launch ramps, the tails of partial last rounds, latency-bound
+    # attention).  Each request still does its whole single pass and readout.
+    concurrent = None
+    if "single-pass" in modes and args.concurrent_streams > 0:
+        # 3 by default: a fourth stream was slower (4 request streams + torch's exceed 4 hardware queues)
+        n_conc = args.concurrent_streams
+        cmodels = [model] + [cpd.PcdModel(cpd.config_of(sh), dev, lim) for _ in range(n_conc - 1)]
+        cschemas = [schema] + [m_.compile_fields(req.fields) for m_ in cmodels[1:]]
+        cstreams = [torch.cuda.Stream() for _ in range(n_conc)]
+        ckvs = kvs + [torch.empty_like(kv) for _ in range(n_conc - len(kvs))]
+
+        def run_concurrent(n):
+            pend, outs = collections.deque(), []
+            for i in range(n):
+                k = i % n_conc
+                with torch.cuda.stream(cstreams[k]):
+                    st = cmodels[k].new_state(len(req.prefix), ckvs[k])
+                    pend.append((cmodels[k].extend_decide_start(st, prompt, cschemas[k]), st))
+                if len(pend) == n_conc:
+                    p_, s_ = pend.popleft()
+                    outs.append(p_.finish())
+                    s_.close()
+            while pend:
+                p_, s_ = pend.popleft()
+                outs.append(p_.finish())
+                s_.close()
+            return outs
+
+        run_concurrent(max(args.warmup, n_conc))
+        torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
+        t0 = time.perf_counter()
+        couts = run_concurrent(args.steps)
+        torch.cuda.synchronize()
+        cc_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        gc.enable()
+        same = all(np.array_equal(o[k], ref_out[k]) for o in couts for k in ("prob", "mass", "argmax"))
+        concurrent = {"streams": n_conc, "ms_per_request": round(cc_ms, 4),
+                      "fields_per_s": round(nf / (cc_ms / 1e3), 2), "same_results_as_one_at_a_time": bool(same)}
+        print(f"# concurrent ({n_conc} streams): {cc_ms:.3f} ms/request", file=sys.stderr, flush=True)
+        for m_ in cmodels[1:]:
+            m_.close()
+
     # Warm requests: the prefix's first tokens are a cached head; each request
     # forks it, appends its own input tokens and decides (one extend + one
     # branch pass), or runs the first-field round on top (decide field 0,
@@ -420,9 +473,9 @@ def main():
         out["readout"] = {"ms": ro, "bytes": ro_bytes, "GB/s": round(ro_bytes / ro / 1e6, 1),
                           "hbm_frac": round(ro_bytes / ro / 1e6 / HBM_PEAK_GBS, 4)}
         return out
-    # whole-job throughput: the pipelined loop where it ran (every request
+    # whole-job throughput: the concurrent loop where it ran (every request
     # still does all of its work), else the headline mode's steps
-    thr_ms = pipelined["ms_per_request"] if pipelined else ms_per_step
+    thr_ms = concurrent["ms_per_request"] if concurrent else ms_per_step
     res = {
         "metric": "schema fields decided/sec + p50 28-field request ms, 1.5B-shaped bf16",
         "value": round(nf / (thr_ms / 1e3), 2),
@@ -443,8 +496,9 @@ def main():
                    "layers": sh.n_layers, "prefix_tokens": len(req.prefix), "fields": nf,
                    "branch_tokens": Tb, "readouts": R, "mode": mode,
                    "schema": "marshalled to C arrays once; validated and planned on every request",
-                   "throughput": (f"{pipelined['depth']} single-pass requests in flight (start/finish calls)"
-                                  if pipelined else f"{mode} requests one at a time"),
+                   "throughput": (f"single-pass requests on {concurrent['streams']} streams at once, one in "
+                                  f"flight per stream (start/finish calls)" if concurrent
+                                  else f"{mode} requests one at a time"),
                    "latency": f"{mode} requests one at a time"},
         "phases_ms": phases,
         "device_fields_per_s": round(nf / (dev_ms / 1e3), 2),
@@ -460,6 +514,8 @@ def main():
                                                             "launches", "bound")} for c, e in kernels.items()},
         "kernel_timed_ms_per_step": round(timed_ms_per_step, 4),
     }
+    if concurrent is not None:
+        res["concurrent"] = concurrent
     if pipelined is not None:
         res["pipelined"] = pipelined
         res["one_at_a_time_fields_per_s"] = round(nf / (ms_per_step / 1e3), 2)
