@@ -359,3 +359,37 @@ def test_misaligned_buffers_are_refused(tiny_w):
     st = m.new_state(16, kv[16:])
     assert st.n_tokens == 0
     m.close()
+
+
+def test_tiny_models_on_two_streams_share_weights(tiny_w):
+    """Two models over the same device weights, each with its own workspace,
+    run started calls on two streams at once: every result equals the one
+    the first model gives one call at a time."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(36)
+    prefixes = [_tokens(rng, sh.vocab_size, 60 + 7 * i) for i in range(6)]
+    reqs = [pi.random_trie_fields(980 + i, sh.vocab_size, 3) for i in range(6)]
+    p_all = cpd.debug_plan(sh.vocab_size, sh.max_seq, [len(p) for p in prefixes], reqs)
+    lim = cpd.limits_for(sh.vocab_size, sh.max_seq, [len(p) for p in prefixes], reqs,
+                         max(map(len, prefixes)) + len(p_all["tok"]))
+    dev = cpd.upload_weights(tiny_w.mats, sh.n_layers, sh.d_model, "cuda:0")
+    models = [cpd.PcdModel(cpd.config_of(sh), dev, lim) for _ in range(2)]
+    want = []
+    for p, f in zip(prefixes, reqs):
+        st = models[0].new_state(len(p))
+        want.append(models[0].extend_decide(st, p, f))
+        st.close()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    pend = []
+    for i, (p, f) in enumerate(zip(prefixes, reqs)):
+        k = i % 2
+        with torch.cuda.stream(streams[k]):
+            st = models[k].new_state(len(p))
+            pend.append((models[k].extend_decide_start(st, p, f), st))
+    for i, (pd, st) in enumerate(pend):
+        got = pd.finish()
+        st.close()
+        for key in ("prob", "logscore", "mass", "margin", "argmax"):
+            assert np.array_equal(got[key], want[i][key]), (i, key)
+    for m in models:
+        m.close()
