@@ -320,7 +320,7 @@ def main():
     # attention).  Each request still does its whole single pass and readout.
     concurrent = None
     if "single-pass" in modes and args.concurrent_streams > 0:
-        # 3 by default: a fourth stream was slower (4 request streams + torch's exceed 4 hardware queues)
+        # 3 by default: a fourth stream gained 1% on one box and lost 6% on another
         n_conc = args.concurrent_streams
         cmodels = [model] + [cpd.PcdModel(cpd.config_of(sh), dev, lim) for _ in range(n_conc - 1)]
         cschemas = [schema] + [m_.compile_fields(req.fields) for m_ in cmodels[1:]]
