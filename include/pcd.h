@@ -215,7 +215,11 @@ size_t pcd_workspace_bytes(const pcd_config *cfg, const pcd_limits *lim);
 /* Create a model over caller-owned device weights and a caller-owned device
  * workspace of ws_bytes >= pcd_workspace_bytes(cfg, lim).  Uploads the RoPE
  * cos/sin table (computed on the host in double precision, stored as fp32)
- * into the workspace on `stream`.  The weights are only read, never written. */
+ * into the workspace on `stream`.  The weights are only read, never written,
+ * so several models may borrow the same weights: each with its own workspace
+ * and on its own stream, their calls run on the device at once (independent
+ * requests overlap, and one request's kernels use the compute units another's
+ * leave idle). */
 int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w,
                      void *workspace, size_t ws_bytes, void *stream, pcd_model **out);
 
