@@ -40,13 +40,15 @@ size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 // device buffers are read and written in 16-byte vectors
 bool misaligned(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
 
-// Attention workgroups per launch (about one per compute unit: more splits
-// cost more in partial writes and the merge than they gain in parallelism,
-// fewer leave the longest blocks on the critical path; measured on the 1.5B
-// shape, 256 beats 512 and 1024 on the single-pass request and ties on the
-// two-pass one, 128 ties with 256, and no splits at all (64) is 1-2% slower
-// on both), and the shortest key range worth a workgroup of its own.
-constexpr int ATT_TARGET_BLOCKS = 256;
+// Attention workgroups per launch below which keys are split over
+// workgroups, and the shortest key range worth a workgroup of its own.  Key
+// splits cost partial writes and a merge kernel; they pay when few row
+// blocks would leave most compute units idle on a long prefix.  On the 1.5B
+// shape's 799-row single pass (150 row blocks), a target of 64 (no splits)
+// and one of 256 (2 splits, then the merge) give the same time for one
+// request at a time, and 64 is 2% faster with three requests running
+// concurrently (less total work); 512 and 1024 were slower.
+constexpr int ATT_TARGET_BLOCKS = 64;
 constexpr int ATT_MIN_SPLIT_TILES = 2;  // 64-key tiles
 constexpr int MAX_PASS_ROWS = 1 << 18;  // token rows of one decoder pass
 // Key splits of a row block: enough for `row_blocks` blocks to reach the
