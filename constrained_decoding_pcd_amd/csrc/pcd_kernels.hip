@@ -931,13 +931,68 @@ __global__ __launch_bounds__(256) void k_resid_norm_n(const float *__restrict__ 
     }
 }
 
+// The same for N = 512 * NE, one workgroup per row (2 values per thread per
+// 512 columns): for the wider rows (3584) one wave per row would hold every
+// split's slice of the row in a lane's registers, up to 512 of them with
+// spills at 8 splits.  Every load still goes out before the first use.
+template <typename T, int SMAX, int NE>
+__global__ __launch_bounds__(256) void k_resid_norm_wg(const float *__restrict__ part, int32_t splits, int32_t M,
+                                                      float *__restrict__ x, const float *__restrict__ w, float eps,
+                                                      T *__restrict__ h) {
+    constexpr int N = 512 * NE;
+    __shared__ float red[4];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    float *xr = x + (size_t)m * N;
+    const size_t pstride = (size_t)M * N;
+    const float *prow = part + (size_t)m * N;
+    float2 v[NE], wv[NE], pv[NE][SMAX];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int j = tid + 256 * i;
+        v[i] = reinterpret_cast<const float2 *>(xr)[j];
+        if (w) wv[i] = reinterpret_cast<const float2 *>(w)[j];
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s)
+            pv[i][s] = reinterpret_cast<const float2 *>(prow + (size_t)min(s, splits - 1) * pstride)[j];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s)
+            if (s < splits) {
+                v[i].x += pv[i][s].x;
+                v[i].y += pv[i][s].y;
+            }
+        reinterpret_cast<float2 *>(xr)[tid + 256 * i] = v[i];
+        ss += v[i].x * v[i].x + v[i].y * v[i].y;
+    }
+    if (!w) return;
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int j = tid + 256 * i;
+        T *hp = h + (size_t)m * N + 2 * j;
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t lo = __builtin_bit_cast(uint16_t, from_f<T>(v[i].x * inv * wv[i].x));
+            const uint32_t hi = __builtin_bit_cast(uint16_t, from_f<T>(v[i].y * inv * wv[i].y));
+            *reinterpret_cast<uint32_t *>(hp) = lo | (hi << 16);
+        } else {
+            *reinterpret_cast<float2 *>(hp) = make_float2(v[i].x * inv * wv[i].x, v[i].y * inv * wv[i].y);
+        }
+    }
+}
+
 template <typename T, int SMAX>
 static void resid_norm_t(const float *part, int32_t splits, int32_t M, int32_t N, float *x, const float *w, float eps,
                          void *h, hipStream_t st) {
     if (N == 1536)
         hipLaunchKernelGGL((k_resid_norm_n<T, SMAX, 3>), dim3((M + 3) / 4), dim3(256), 0, st, part, splits, M, x, w, eps, (T *)h);
     else if (N == 3584)
-        hipLaunchKernelGGL((k_resid_norm_n<T, SMAX, 7>), dim3((M + 3) / 4), dim3(256), 0, st, part, splits, M, x, w, eps, (T *)h);
+        hipLaunchKernelGGL((k_resid_norm_wg<T, SMAX, 7>), dim3(M), dim3(256), 0, st, part, splits, M, x, w, eps, (T *)h);
     else if (N % 512 == 0 && N <= 8192)
         hipLaunchKernelGGL((k_resid_norm<T, SMAX, true>), dim3(M), dim3(256), 0, st, part, splits, M, N, x, w, eps,
                            (T *)h);
