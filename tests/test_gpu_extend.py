@@ -393,3 +393,35 @@ def test_tiny_models_on_two_streams_share_weights(tiny_w):
             assert np.array_equal(got[key], want[i][key]), (i, key)
     for m in models:
         m.close()
+
+
+def test_tiny_started_calls_with_kernel_timing(tiny_w):
+    """With per-kernel timing on, two started calls finished in reverse
+    order give the untimed results, and every launch of both passes is
+    counted."""
+    sh = pi.SHAPES["tiny"]
+    rng = np.random.default_rng(37)
+    prefixes = [_tokens(rng, sh.vocab_size, 50 + 20 * i) for i in range(2)]
+    reqs = [pi.random_trie_fields(990 + i, sh.vocab_size, 2) for i in range(2)]
+    p_all = cpd.debug_plan(sh.vocab_size, sh.max_seq, [len(p) for p in prefixes], reqs)
+    m = _model(sh, tiny_w, [len(p) for p in prefixes], reqs, max(map(len, prefixes)) + len(p_all["tok"]))
+    want, counts = [], []
+    for p, f in zip(prefixes, reqs):
+        st = m.new_state(len(p))
+        m.set_kernel_timing(True)
+        want.append(m.extend_decide(st, p, f))
+        counts.append(sum(n for _, n in m.kernel_times().values()))
+        m.set_kernel_timing(False)
+        st.close()
+    m.set_kernel_timing(True)
+    states = [m.new_state(len(p)) for p in prefixes]
+    pend = [m.extend_decide_start(states[i], prefixes[i], reqs[i]) for i in range(2)]
+    got = [None, pend[1].finish(), None]
+    got[0] = pend[0].finish()
+    kt = m.kernel_times()
+    assert sum(n for _, n in kt.values()) == sum(counts)
+    assert all(ms >= 0 for ms, _ in kt.values())
+    for i in range(2):
+        for k in ("prob", "logscore", "mass", "margin", "argmax"):
+            assert np.array_equal(got[i][k], want[i][k]), (i, k)
+    m.close()
