@@ -7,16 +7,13 @@ two of its requests are re-computed by the oracle and compared one by one.
 The 7B shape runs with 2 layers against the oracle, and at full depth with
 its 16384-token prefix against properties that hold at any size.
 
-Full-depth bf16 tolerances: the GPU rounds normalised activations, q/k/v,
-attention probabilities and outputs, SwiGLU outputs and the readout rows to
-bf16 (relative error <= 2^-9 each), at 7 points per layer.  An fp32 CPU
-emulation of those rounding points against the fp64 oracle gives gathered-
-logit errors up to 2.3e-2 at 2 layers and 3.2e-2 at 28 layers; the GPU
-measures 2.3e-2 and 3.3e-2 to 4.2e-2 (the realisation moves with the GEMM
-accumulation order).  The bound is 6e-2 on logits, log-sum-exps and
-per-token log-scores (1.5x the largest measured), 2.5e-2 on probabilities,
-5e-2 relative on mass.  The argmax must match wherever the oracle's top-2
-margin is at least 0.05 nats.
+Full-depth bf16 tolerances (tests/tolerances.py): the 2-layer bounds scaled
+by the growth of the logit error with depth in a model of the device's bf16
+rounding points (test_bf16_bound.py derives the factor, sigma_28 / sigma_2 =
+2.65, on the 28-field request): 6.6e-2 on logits, 2.7e-3 on log-sum-exps,
+6.9e-2 on per-token log-scores, 3.5e-2 on probabilities, 7.1e-2 relative on
+mass; the argmax must match wherever the oracle's top-2 margin is at least
+2 z (0.13 nats) for single-token fields, 2 ls per token on deeper paths.
 """
 import numpy as np
 import pytest
@@ -24,15 +21,15 @@ import pytest
 import pcd_inputs as pi
 from oracle import decoder as odec
 from oracle import pcd as opcd
-from test_gpu_parity import cand_depth
+from test_gpu_parity import cand_depth, check_argmax
+import tolerances as tl
 
 cpd = pytest.importorskip("constrained_decoding_pcd_amd")
 torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
 
-DEEP = dict(z=6e-2, ls=6e-2, prob=2.5e-2, mass=5e-2)
-MARGIN_WAIVER = 0.05
+DEEP = tl.BF16_L28
 
 
 def _errors(got, ref_fields, ref_lse, ref_z, plan):
@@ -58,13 +55,11 @@ def _check(name, got, ref, tol=DEEP):
     agree = sum(int(a == f.argmax) for a, f in zip(arg, ref.fields))
     print(f"[{name}] max errors: " + ", ".join(f"{k} {v:.3e}" for k, v in d.items()) +
           f"; argmax {agree}/{len(ref.fields)}, min margin {min(f.margin for f in ref.fields):.3f}", flush=True)
-    assert d["lse"] <= tol["z"] and d["z"] <= tol["z"]
+    assert d["lse"] <= tol["lse"] and d["z"] <= tol["z"]
     assert d["ls/len"] <= tol["ls"]
     assert d["prob"] <= tol["prob"]
     assert d["mass_rel"] <= tol["mass"]
-    for a, f in zip(arg, ref.fields):
-        if f.margin >= MARGIN_WAIVER:
-            assert int(a) == f.argmax
+    check_argmax(arg, ref.fields, ref.plan, tol, name)
     _invariants(got)
 
 
@@ -187,7 +182,7 @@ def test_7b_two_layer_parity(q7_two_layer):
     st = m.prefill(req[0])
     got = [m.decide(st, req[1], debug=True)]
     ref = opcd.decide(odec.Decoder(w, np.float64), [req])
-    _check("cfg4-L2-P2048", got, ref)
+    _check("cfg4-L2-P2048", got, ref, tl.BF16_7B_L2)
     st.close()
     m.close()
 

@@ -6,16 +6,18 @@ gathered candidate logits, candidate log-scores and probabilities, candidate
 mass and argmax.  Integer work (the plan) is checked bit-exactly on the CPU
 (test_host.py); here the plan's effect is checked through the outputs.
 
-Tolerances (GPU minus fp64 oracle on the same weights):
+Tolerances (GPU minus fp64 oracle on the same weights), from
+tests/tolerances.py:
   fp32 model:  lse, z, logscore <= 1e-4 abs;  prob <= 1e-5 abs;  mass <= 1e-4 rel
-  bf16 models: lse, z <= 2.5e-2 abs; logscore <= 2.5e-2 x path length;
-               prob <= 1.25e-2 abs; mass <= 5e-2 rel
-  argmax equal unless the oracle's top-2 margin is under 0.05 nats (two
-  logits each off by the 2.5e-2 bound can swap at most that margin).
+  bf16 models at 2 layers: lse, z <= 2.5e-2 abs; logscore <= 2.6e-2 x path
+               length; prob <= 1.3e-2 abs; mass <= 2.6e-2 rel
+  argmax equal unless the oracle's top-2 margin is under the waiver: 2 z for
+  single-token fields (0.05 nats in bf16: two logits each off by 2.5e-2 can
+  swap at most that margin), 2 ls per token of the field's deepest path.
 The bf16 bounds come from rounding the GEMM inputs (normalised activations,
-attention outputs, SwiGLU outputs) and the KV cache to bf16, a relative
-error of 2^-9 per element; over 2 to 28 layers the measured spread is well
-inside them.
+attention probabilities and outputs, SwiGLU outputs) and the KV cache to
+bf16, a relative error of 2^-9 per element; test_bf16_bound.py relates them
+to a model of those rounding points.
 """
 import numpy as np
 import pytest
@@ -23,17 +25,14 @@ import pytest
 import pcd_inputs as pi
 from oracle import decoder as odec
 from oracle import pcd as opcd
+import tolerances as tl
 
 cpd = pytest.importorskip("constrained_decoding_pcd_amd")
 torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
 
-TOL = {
-    "f32": dict(z=1e-4, ls=1e-4, prob=1e-5, mass=1e-4),
-    "bf16": dict(z=2.5e-2, ls=2.5e-2, prob=1.25e-2, mass=5e-2),
-}
-MARGIN_WAIVER = 0.05
+TOL = {"f32": tl.F32, "bf16": tl.BF16_L2}
 
 
 def _model(shape, weights, requests, max_prefill=0):
@@ -48,6 +47,20 @@ def cand_depth(plan) -> np.ndarray:
     slen = np.diff(plan.s_path_off)
     return np.array([slen[plan.c_spell_off[c]:plan.c_spell_off[c + 1]].max()
                      for c in range(len(plan.c_spell_off) - 1)])
+
+
+def field_depth(plan) -> np.ndarray:
+    """Per field, the longest scored path of its candidates."""
+    cd = cand_depth(plan)
+    return np.array([cd[plan.f_cand_off[f]:plan.f_cand_off[f + 1]].max() for f in range(len(plan.f_cand_off) - 1)])
+
+
+def check_argmax(arg, ref_fields, plan, bounds, name=""):
+    """The argmax must equal the oracle's wherever the oracle's top-2 margin
+    is at least the field's waiver."""
+    for i, (a, f, dep) in enumerate(zip(arg, ref_fields, field_depth(plan))):
+        if f.margin >= tl.margin_waiver(bounds, int(dep)):
+            assert int(a) == f.argmax, (name, i, f.margin)
 
 
 def _compare(name, got, ref, plan, dtype, label=""):
@@ -72,13 +85,11 @@ def _compare(name, got, ref, plan, dtype, label=""):
         "mass_rel": float(np.max(np.abs(mass - rmass) / rmass)),
     }
     print(f"[{name}{label}] max errors: " + ", ".join(f"{k} {v:.3e}" for k, v in d.items()), flush=True)
-    assert d["lse"] <= tol["z"] and d["z"] <= tol["z"]
+    assert d["lse"] <= tol.get("lse", tol["z"]) and d["z"] <= tol["z"]
     assert d["ls/len"] <= tol["ls"]
     assert d["prob"] <= tol["prob"]
     assert d["mass_rel"] <= tol["mass"]
-    for i, f in enumerate(ref.fields):
-        if f.margin >= MARGIN_WAIVER:
-            assert int(arg[i]) == f.argmax, (i, f.margin)
+    check_argmax(arg, ref.fields, plan, tol, name)
     # invariants of every field
     off = 0
     for g in got:
