@@ -170,12 +170,32 @@ struct pcd_model {
     struct Slot {
         char *plan_host = nullptr, *outs_host = nullptr;
         hipEvent_t ev[4] = {};  // pass start (plan uploaded), pass end, readout end, results on the host
+        hipStream_t st = nullptr;  // stream of the call holding the slot
         bool busy = false;
     };
     Slot slots[PCD_MAX_PENDING];
     hipEvent_t ev[6] = {};  // branch start/end, readout end, prefill start/end, plan upload done
     pcd_stats stats{};
     bool prefill_pending = false;  // last_prefill_ms not yet read from ev[3], ev[4]
+    hipStream_t prefill_st = nullptr;  // stream of the last prefill or extend pass
+    // Every pass reads and writes the one workspace (plan, activations,
+    // branch K/V, partials, results), so a call may go on another stream only
+    // once the model's earlier calls have left the device: a started decide
+    // call until its results are on the host (slot event 3), a prefill or
+    // extend until its pass has ended (ev[4]).  Refuses, before any device
+    // work, a call on a stream other than that of a call still running.
+    int check_stream(hipStream_t st) {
+        for (int k = 0; k < PCD_MAX_PENDING; ++k) {
+            const Slot &sl = slots[k];
+            if (sl.busy && sl.st != st && hipEventQuery(sl.ev[3]) == hipErrorNotReady)
+                return fail(PCD_E_ARG, "a started decide call of this model is still running on another stream; "
+                                       "use that stream or finish the call first");
+        }
+        if (prefill_pending && prefill_st != st && hipEventQuery(ev[4]) == hipErrorNotReady)
+            return fail(PCD_E_ARG, "a prefill or extend pass of this model is still running on another stream; "
+                                   "use that stream or wait for it first");
+        return PCD_OK;
+    }
     // fold a finished prefill's event time into the stats (waits for it)
     void settle_prefill() {
         if (!prefill_pending) return;
@@ -537,6 +557,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     const int32_t *d_tsp = pk.put(tok_splits.data(), n);
     const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
     if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
+    if (int rc = m->check_stream(st)) return rc;
     m->settle_prefill();
     HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
     HIP_TRY(hipEventRecord(m->ev[5], st));
@@ -601,6 +622,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     // pinned staging buffer before the next call refills it.
     HIP_TRY(hipEventSynchronize(m->ev[5]));
     m->prefill_pending = true;
+    m->prefill_st = st;
     if (m->timing) {
         HIP_TRY(hipStreamSynchronize(st));
         m->tcollect();
@@ -661,6 +683,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
     const AttnBlock *d_blk = pk.put(blocks.data(), blocks.size());
     if (pk.overflow) return fail(PCD_E_CAP, "plan staging overflow");
     const KvRows kr{d_req, d_pos, d_stride, d_kv};  // a token's slot in its buffer is its position
+    if (int rc = m->check_stream(st)) return rc;
     m->settle_prefill();
     HIP_TRY(hipMemcpyAsync(m->ws + m->L.plan, m->plan_host, pk.off, hipMemcpyHostToDevice, st));
     HIP_TRY(hipEventRecord(m->ev[5], st));
@@ -718,6 +741,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
     HIP_TRY(hipGetLastError());
     HIP_TRY(hipEventSynchronize(m->ev[5]));
     m->prefill_pending = true;
+    m->prefill_st = st;
     if (m->timing) {
         HIP_TRY(hipStreamSynchronize(st));
         m->tcollect();
@@ -1005,6 +1029,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (int rc = m->check_stream(st)) return rc;
     int si = -1;
     for (int k = 0; k < PCD_MAX_PENDING && si < 0; ++k)
         if (!m->slots[k].busy) si = k;
@@ -1226,6 +1251,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     pd->o_lse = o_lse;
     pd->o_z = o_z;
     slot.busy = true;
+    slot.st = st;
     // the new tokens are the state's from now on: later calls on the stream see them
     if (n_new > 0) states[0]->P += n_new;
     m->stats.branch_passes += 1;

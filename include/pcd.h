@@ -41,7 +41,9 @@
  *     pcd_extend_decide_start, which return once their work is enqueued.
  *   - A model's passes share its workspace: while a call of the model is
  *     still running on the device, the model's other calls go on the same
- *     stream.
+ *     stream.  A prefill, extend or decide call on another stream fails with
+ *     PCD_E_ARG (before any device work) while a started decide call or a
+ *     prefill / extend pass of the same model has not left the device.
  *   - A model is used from one host thread at a time.
  */
 #ifndef PCD_H
@@ -288,7 +290,15 @@ int pcd_fork(const pcd_state *s, void *kv_buf, size_t kv_bytes, void *stream, pc
 int pcd_state_tokens(const pcd_state *s);
 
 /* Decide every field of one request against a prefilled state in ONE batched
- * decoder pass.  Each field's row is its scaffold, placed right after the
+ * decoder pass ("Parallel Constrained Decoding from Scratch", "The idea:
+ * parallel constrained decoding", steps 2-3: one short row per field that
+ * ends where the field's labels part ways, all rows in one batched pass over
+ * the shared prompt's cache, the next-token distribution at each row's end
+ * restricted to the allowed first tokens and renormalised; the same page,
+ * "And you get confidence for free", for the candidate mass; the
+ * "Parallel Constrained Decoding" engine README, "The technique": broadcast
+ * of the cached prefix, one batched pass, softmax over the candidate tokens
+ * only).  Each field's row is its scaffold, placed right after the
  * state's prefix (positions P, P+1, ...).  Candidates whose leading tokens
  * are shared by other candidates are extended by teacher-forced continuation
  * tokens in the same pass (a trie per field); a candidate's logscore sums
@@ -362,7 +372,17 @@ int pcd_decide_sequenced(pcd_state *s, const pcd_field *fields, int32_t n_fields
                          int32_t n_candidates, int32_t n_first, float temperature, pcd_outputs *out, void *stream);
 
 /* Several requests, each on its own state, in ONE batched pass; outs[i]
- * receives request i's results (arrays indexed within that request). */
+ * receives request i's results (arrays indexed within that request).  Each
+ * request is decided exactly as pcd_decide decides it ("Parallel Constrained
+ * Decoding from Scratch", "The idea: parallel constrained decoding", steps
+ * 2-3; the engine README, "The technique"): the rows of all requests share
+ * one pass over the weights, and every row attends only its own request's
+ * cached prefix, its own scaffold and its trie ancestors.  reqs[i] has the
+ * same layout as pcd_decide's arguments; the whole call is validated (every
+ * request, and the sum of their rows, readouts, gathers, fields, candidates
+ * and spellings against the model's limits, n_req <= max_requests) before
+ * any device work, and on error no output is written.  The states' KV
+ * buffers are only read. */
 int pcd_decide_many(pcd_state *const *states, const pcd_request *reqs, int32_t n_req, float temperature,
                     pcd_outputs *outs, void *stream);
 
