@@ -430,13 +430,15 @@ def test_tiny_started_calls_with_kernel_timing(tiny_w):
     m.close()
 
 
-def test_call_on_another_stream_is_refused_while_a_call_runs(tiny_w):
+def test_call_on_another_stream_is_refused_while_a_call_runs(tiny_w, q15_l2):
     """A model's passes share its workspace, so while one of its calls is
     still on the device another call of the same model on a different stream
     is refused (PCD_E_ARG, before any device work); on the same stream, or
-    once the call has left the device, it runs.  A bounded spin kernel
-    (torch.cuda._sleep) ahead of the first call keeps it on the device while
-    the host makes the second."""
+    once the call has left the device, it runs.  A started decide call is
+    kept on the device by a bounded spin kernel (torch.cuda._sleep) ahead of
+    it; a prefill is kept there by its own length (4,000 tokens at the 1.5B
+    widths, 2 layers: milliseconds, against the microseconds the host takes
+    to make the next call)."""
     sh = pi.SHAPES["tiny"]
     rng = np.random.default_rng(37)
     prefix = _tokens(rng, sh.vocab_size, 70)
@@ -464,19 +466,29 @@ def test_call_on_another_stream_is_refused_while_a_call_runs(tiny_w):
     got_a = pa.finish()
     with torch.cuda.stream(s2):  # the call has left the device
         other = m.decide(st, fields)
-    # a prefill on s1 still running
-    with torch.cuda.stream(s1):
-        torch.cuda._sleep(50_000_000)
-        hb = m.prefill(prefix)
-    with torch.cuda.stream(s2):
-        with pytest.raises(cpd.PcdError) as e:
-            m.decide(hb, fields)
-        assert e.value.name == "ARG"
-    s1.synchronize()
-    with torch.cuda.stream(s2):
-        after = m.decide(hb, fields)
-    for got in (got_a, same, other, after):
+    for got in (got_a, same, other):
         for k in ("prob", "logscore", "mass", "margin", "argmax"):
             assert np.array_equal(got[k], want[k]), k
     torch.cuda.synchronize()
     m.close()
+    # a prefill pass still running on s1
+    sh2, w2, _ = q15_l2
+    wl = pi.make_workload("cfg1")
+    f2 = wl.requests[0].fields
+    long_prefix = _tokens(rng, sh2.vocab_size, 4000)
+    m2 = _model(sh2, w2, [len(long_prefix)], [f2], len(long_prefix))
+    with torch.cuda.stream(s1):
+        hb = m2.prefill(long_prefix)
+    with torch.cuda.stream(s2):
+        with pytest.raises(cpd.PcdError) as e:
+            m2.decide(hb, f2)
+        assert e.value.name == "ARG"
+    s1.synchronize()
+    with torch.cuda.stream(s2):
+        after = m2.decide(hb, f2)
+    with torch.cuda.stream(s1):
+        again = m2.decide(hb, f2)
+    for k in ("prob", "logscore", "mass", "margin", "argmax"):
+        assert np.array_equal(after[k], again[k]), k
+    torch.cuda.synchronize()
+    m2.close()
