@@ -25,7 +25,7 @@ ERROR_NAMES = {-1: "ARG", -2: "TOKEN", -3: "NCAND", -4: "EMPTY", -5: "DUP", -6: 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAX_PENDING = 4  # started, unfinished calls one model holds at most
 
-EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_state_bytes", "pcd_prefill", "pcd_prefill_many",
+EXPORTS = ("pcd_workspace_bytes", "pcd_load_weights", "pcd_load_weights_noalloc", "pcd_state_bytes", "pcd_prefill", "pcd_prefill_many",
            "pcd_extend",
            "pcd_fork", "pcd_state_tokens", "pcd_new_state", "pcd_decide", "pcd_extend_decide",
            "pcd_extend_decide_start", "pcd_finish",
@@ -146,6 +146,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pcd_workspace_bytes": (c_size_t, [P(pcd_config), P(pcd_limits)]),
         "pcd_load_weights": (c_int32, [P(pcd_config), P(pcd_limits), P(pcd_weights), c_void_p, c_size_t, c_void_p,
                                        P(c_void_p)]),
+        "pcd_load_weights_noalloc": (c_int32, [P(pcd_config), P(pcd_limits), P(pcd_weights), c_void_p,
+                                               P(c_void_p)]),
         "pcd_state_bytes": (c_size_t, [c_void_p, c_int32]),
         "pcd_prefill": (c_int32, [c_void_p, P(c_int32), c_int32, c_void_p, c_size_t, c_void_p, P(c_void_p)]),
         "pcd_prefill_many": (c_int32, [c_void_p, c_int32, P(c_int32), P(c_int32), P(c_void_p), P(c_size_t),
@@ -365,7 +367,7 @@ class PcdState:
         m = self.model
         if kv is None:
             kv = m.torch.empty(max(m.state_bytes(capacity or self.n_tokens), 1), dtype=m.torch.uint8,
-                               device=m.workspace.device)
+                               device=m.device)
         h = c_void_p()
         _check(m.lib.pcd_fork(self.handle, c_void_p(kv.data_ptr()), kv.numel(), _stream_handle(m.torch),
                               ctypes.byref(h)))
@@ -407,12 +409,16 @@ class PendingDecide:
                 pass
 
 
+NOALLOC_WORKSPACE_MAX = 128 << 20  # PCD_NOALLOC_WORKSPACE_MAX
+
+
 class PcdModel:
     """A model over device weights (torch tensors) and a torch-allocated
-    workspace.  `config` holds the pcd_config fields, `limits` the
-    pcd_limits fields."""
+    workspace (or, with noalloc=True, the library's static workspace:
+    pcd_load_weights_noalloc).  `config` holds the pcd_config fields,
+    `limits` the pcd_limits fields."""
 
-    def __init__(self, config: dict, weights: Dict[str, "object"], limits: dict):
+    def __init__(self, config: dict, weights: Dict[str, "object"], limits: dict, noalloc: bool = False):
         import torch
         self.torch = torch
         self.lib = load_library()
@@ -431,14 +437,20 @@ class PcdModel:
         w.final_norm = weights["final_norm"].data_ptr()
         for n, a in self._arrays.items():
             setattr(w, n, a)
-        nbytes = self.lib.pcd_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(self.lim))
-        if nbytes == 0:
-            raise PcdError(-1, self.lib.pcd_last_error().decode())
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=weights["embed"].device)
+        self.device = weights["embed"].device
         h = c_void_p()
-        _check(self.lib.pcd_load_weights(ctypes.byref(self.cfg), ctypes.byref(self.lim), ctypes.byref(w),
-                                         c_void_p(self.workspace.data_ptr()), nbytes, _stream_handle(torch),
-                                         ctypes.byref(h)))
+        if noalloc:
+            self.workspace = None
+            _check(self.lib.pcd_load_weights_noalloc(ctypes.byref(self.cfg), ctypes.byref(self.lim), ctypes.byref(w),
+                                                     _stream_handle(torch), ctypes.byref(h)))
+        else:
+            nbytes = self.lib.pcd_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(self.lim))
+            if nbytes == 0:
+                raise PcdError(-1, self.lib.pcd_last_error().decode())
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            _check(self.lib.pcd_load_weights(ctypes.byref(self.cfg), ctypes.byref(self.lim), ctypes.byref(w),
+                                             c_void_p(self.workspace.data_ptr()), nbytes, _stream_handle(torch),
+                                             ctypes.byref(h)))
         self.handle = h
 
     def state_bytes(self, n_tokens: int) -> int:
@@ -450,7 +462,7 @@ class PcdModel:
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         nb = self.state_bytes(max(t.size, capacity or 0))
         if kv is None:
-            kv = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.workspace.device)
+            kv = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.device)
         h = c_void_p()
         _check(self.lib.pcd_prefill(self.handle, _i32p(t), t.size, c_void_p(kv.data_ptr()), kv.numel(),
                                     _stream_handle(torch), ctypes.byref(h)))
@@ -464,7 +476,7 @@ class PcdModel:
         toks = np.ascontiguousarray(np.concatenate(arrs) if arrs else np.zeros(0, np.int32), dtype=np.int32)
         lens = np.ascontiguousarray([a.size for a in arrs], dtype=np.int32)
         if kvs is None:
-            kvs = [torch.empty(max(self.state_bytes(a.size), 1), dtype=torch.uint8, device=self.workspace.device)
+            kvs = [torch.empty(max(self.state_bytes(a.size), 1), dtype=torch.uint8, device=self.device)
                    for a in arrs]
         n = len(arrs)
         bufs = (c_void_p * max(1, n))(*[kv.data_ptr() for kv in kvs])
@@ -486,7 +498,7 @@ class PcdModel:
         """pcd_new_state: an empty state whose buffer holds `capacity` tokens."""
         torch = self.torch
         if kv is None:
-            kv = torch.empty(max(self.state_bytes(capacity), 1), dtype=torch.uint8, device=self.workspace.device)
+            kv = torch.empty(max(self.state_bytes(capacity), 1), dtype=torch.uint8, device=self.device)
         h = c_void_p()
         _check(self.lib.pcd_new_state(self.handle, c_void_p(kv.data_ptr()), kv.numel(), ctypes.byref(h)))
         return PcdState(self, h, kv, 0)

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -164,7 +165,12 @@ struct pcd_model {
     const float *final_norm = nullptr;
     std::vector<const void *> wq, wk, wv, wo, wg, wu, wd;
     std::vector<const float *> an, mn;
-    char *plan_host = nullptr;  // pinned staging for a prefill's plan upload
+    // The workspace is the library's static scratch of this device
+    // (pcd_load_weights_noalloc); its host staging is then pageable memory
+    // from new[] instead of pinned memory.
+    bool static_ws = false;
+    int ws_device = -1;
+    char *plan_host = nullptr;  // staging for a prefill's plan upload (pinned unless static_ws)
     // Decide calls in flight: each holds one slot, with its own pinned plan
     // and result staging and its events, from its start to its finish.
     struct Slot {
@@ -421,6 +427,72 @@ struct Packer {
 
 }  // namespace
 
+// Workspace of the no-allocation models (pcd_load_weights_noalloc): one
+// static array per device, in the library's code object, so that creating
+// such a model allocates no device memory.  Host code never passes `scratch`
+// itself (in host code it names a host-side stand-in): once per device, with
+// that device current, its device address is read with hipGetSymbolAddress
+// and kept here; models use that address like a caller's workspace.
+static __device__ __align__(256) char scratch[PCD_NOALLOC_WORKSPACE_MAX];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+struct ScratchDev {
+    void *ptr = nullptr;             // device address of `scratch` on this device
+    const pcd_model *owner = nullptr;  // the live model using it
+};
+std::mutex g_scratch_mu;
+ScratchDev g_scratch[MAX_DEVICES];
+
+// Claims the current device's scratch for model m (one model per device at
+// a time): its device address in *ptr.
+int claim_scratch(const pcd_model *m, int *dev_out, void **ptr) {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(PCD_E_DEVICE, "device index out of range");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    ScratchDev &sd = g_scratch[dev];
+    if (sd.owner) return fail(PCD_E_ARG, "another model on this device already uses the static workspace; free it first");
+    if (!sd.ptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PCD_E_DEVICE, std::string("address of the static workspace: ") + hipGetErrorString(e));
+        sd.ptr = p;
+    }
+    sd.owner = m;
+    *dev_out = dev;
+    *ptr = sd.ptr;
+    return PCD_OK;
+}
+
+void release_scratch(const pcd_model *m) {
+    if (!m->static_ws || m->ws_device < 0) return;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch[m->ws_device].owner == m) g_scratch[m->ws_device].owner = nullptr;
+}
+
+// pinned (hipHostMalloc) or, for a static-workspace model, pageable staging
+bool host_alloc(const pcd_model *m, char **p, size_t bytes) {
+    if (m->static_ws) {
+        *p = new (std::nothrow) char[bytes];
+        return *p != nullptr;
+    }
+    return hipHostMalloc((void **)p, bytes, hipHostMallocDefault) == hipSuccess;
+}
+
+void host_free(const pcd_model *m, char *p) {
+    if (!p) return;
+    if (m->static_ws) delete[] p;
+    else (void)hipHostFree(p);
+}
+
+int load_model(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w, void *workspace, size_t ws_bytes,
+               void *stream, pcd_model **out, bool noalloc);
+
+}  // namespace
+
 extern "C" {
 
 const char *pcd_last_error(void) { return g_err.c_str(); }
@@ -432,9 +504,23 @@ size_t pcd_workspace_bytes(const pcd_config *cfg, const pcd_limits *lim) {
 
 int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w, void *workspace,
                      size_t ws_bytes, void *stream, pcd_model **out) {
+    return load_model(cfg, lim, w, workspace, ws_bytes, stream, out, false);
+}
+
+int pcd_load_weights_noalloc(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w, void *stream,
+                             pcd_model **out) {
+    return load_model(cfg, lim, w, nullptr, PCD_NOALLOC_WORKSPACE_MAX, stream, out, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int load_model(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w, void *workspace, size_t ws_bytes,
+               void *stream, pcd_model **out, bool noalloc) {
     int rc = check_config(cfg, lim);
     if (rc != PCD_OK) return rc;
-    if (!w || !workspace || !out) return fail(PCD_E_ARG, "null weights, workspace or out");
+    if (!w || (!workspace && !noalloc) || !out) return fail(PCD_E_ARG, "null weights, workspace or out");
     const int L = cfg->n_layers;
     if (!w->embed || !w->final_norm || !w->attn_norm || !w->mlp_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
         !w->w_gate || !w->w_up || !w->w_down || (!cfg->tied_lm_head && !w->lm_head))
@@ -444,7 +530,7 @@ int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_wei
             !w->w_up[l] || !w->w_down[l])
             return fail(PCD_E_ARG, "null per-layer weight pointer");
     bool mis = misaligned(w->embed) || misaligned(w->lm_head) || misaligned(w->final_norm) ||
-               reinterpret_cast<uintptr_t>(workspace) % 256 != 0;
+               (!noalloc && reinterpret_cast<uintptr_t>(workspace) % 256 != 0);
     for (int l = 0; l < L; ++l)
         mis = mis || misaligned(w->attn_norm[l]) || misaligned(w->mlp_norm[l]) || misaligned(w->wq[l]) ||
               misaligned(w->wk[l]) || misaligned(w->wv[l]) || misaligned(w->wo[l]) || misaligned(w->w_gate[l]) ||
@@ -452,9 +538,18 @@ int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_wei
     if (mis) return fail(PCD_E_ARG, "weights must be 16-byte aligned and the workspace 256-byte aligned");
     Layout lay = layout(*cfg, *lim);
     if (ws_bytes < lay.total)
-        return fail(PCD_E_CAP, "workspace of " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(lay.total));
+        return fail(PCD_E_CAP, (noalloc ? "the static workspace holds " : "workspace of ") + std::to_string(ws_bytes) +
+                                   " bytes, these limits need " + std::to_string(lay.total));
     pcd_model *m = new (std::nothrow) pcd_model();
     if (!m) return fail(PCD_E_NOMEM, "model allocation");
+    if (noalloc) {
+        rc = claim_scratch(m, &m->ws_device, &workspace);
+        if (rc != PCD_OK) {
+            delete m;
+            return rc;
+        }
+        m->static_ws = true;
+    }
     m->cfg = *cfg;
     m->lim = *lim;
     m->L = lay;
@@ -477,12 +572,10 @@ int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_wei
         pcd_free_model(m);
         return fail(code, msg);
     };
-    if (hipHostMalloc((void **)&m->plan_host, lay.plan_bytes, hipHostMallocDefault) != hipSuccess)
-        return cleanup(PCD_E_DEVICE, "pinned staging allocation failed");
+    if (!host_alloc(m, &m->plan_host, lay.plan_bytes)) return cleanup(PCD_E_NOMEM, "staging allocation failed");
     for (auto &sl : m->slots) {
-        if (hipHostMalloc((void **)&sl.plan_host, lay.plan_bytes, hipHostMallocDefault) != hipSuccess ||
-            hipHostMalloc((void **)&sl.outs_host, lay.outs_bytes, hipHostMallocDefault) != hipSuccess)
-            return cleanup(PCD_E_DEVICE, "pinned staging allocation failed");
+        if (!host_alloc(m, &sl.plan_host, lay.plan_bytes) || !host_alloc(m, &sl.outs_host, lay.outs_bytes))
+            return cleanup(PCD_E_NOMEM, "staging allocation failed");
         for (auto &e : sl.ev)
             if (hipEventCreate(&e) != hipSuccess) return cleanup(PCD_E_DEVICE, "event creation failed");
     }
@@ -505,6 +598,10 @@ int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_wei
     *out = m;
     return PCD_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t pcd_state_bytes(const pcd_model *m, int32_t n) {
     if (!m || n < 0) return 0;
@@ -1455,11 +1552,13 @@ void pcd_free_state(pcd_state *s) {
 void pcd_free_model(pcd_model *m) {
     if (!m) return;
     m->settle_prefill();
-    if (m->plan_host) (void)hipHostFree(m->plan_host);
-    for (auto &sl : m->slots) {
+    for (auto &sl : m->slots)
         if (sl.busy && sl.ev[3]) (void)hipEventSynchronize(sl.ev[3]);  // an unfinished call's copies end first
-        if (sl.plan_host) (void)hipHostFree(sl.plan_host);
-        if (sl.outs_host) (void)hipHostFree(sl.outs_host);
+    host_free(m, m->plan_host);
+    release_scratch(m);
+    for (auto &sl : m->slots) {
+        host_free(m, sl.plan_host);
+        host_free(m, sl.outs_host);
         for (auto &e : sl.ev)
             if (e) (void)hipEventDestroy(e);
     }

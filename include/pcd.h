@@ -225,6 +225,26 @@ size_t pcd_workspace_bytes(const pcd_config *cfg, const pcd_limits *lim);
 int pcd_load_weights(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w,
                      void *workspace, size_t ws_bytes, void *stream, pcd_model **out);
 
+/* pcd_load_weights for callers that cannot allocate device memory: code
+ * that must not call hipMalloc (under HIP graph capture, in tight serving
+ * loops, in harnesses that forbid it).  The model's workspace is the
+ * library's static device array of PCD_NOALLOC_WORKSPACE_MAX bytes (one per
+ * GPU, in the library's code object, held until the process ends), so this
+ * call allocates no device or pinned memory: its plan and result staging are
+ * pageable host memory, and its calls run the same kernels as a model from
+ * pcd_load_weights.  Weights, KV buffers and result arrays stay the
+ * caller's.  Fails with PCD_E_CAP when the config and limits need a larger
+ * workspace (pcd_workspace_bytes), and with PCD_E_ARG while another model
+ * on the same device (the current one at this call) uses the static array:
+ * one such model per GPU at a time, freed with pcd_free_model like any
+ * other.  The array keeps the contents of the last call; every pass writes
+ * what it reads first, as with a caller's workspace.  Its calls follow the
+ * model's stream rule; calls on one GPU that overlap in time race on the
+ * array.  Arguments, errors and everything else as for pcd_load_weights. */
+#define PCD_NOALLOC_WORKSPACE_MAX ((size_t)128 << 20)
+int pcd_load_weights_noalloc(const pcd_config *cfg, const pcd_limits *lim, const pcd_weights *w, void *stream,
+                             pcd_model **out);
+
 /* Bytes of the KV buffer a state of n_tokens needs:
  * n_tokens x n_layers x 2 (K, V) x n_kv_heads x head_dim x element size
  * ("Parallel Constrained Decoding from Scratch", "the KV cache").
