@@ -4,8 +4,10 @@ The bench request (28 layers, 512-token prefix, 28 fields) and the
 255-option ID workload run whole through the library and through the fp64
 oracle.  The 64-request throughput batch runs in one branch pass on the GPU;
 two of its requests are re-computed by the oracle and compared one by one.
-The 7B shape runs with 2 layers against the oracle, and at full depth with
-its 16384-token prefix against properties that hold at any size.
+The 7B shape runs with 2 layers against the oracle (on the first 2,048
+prefix tokens live, and on the whole 16,384-token prefix against the
+oracle's stored values), and at full depth with its 16,384-token prefix
+against properties that hold at any size.
 
 Full-depth bf16 tolerances (tests/tolerances.py): the 2-layer bounds scaled
 by the growth of the logit error with depth in a model of the device's bf16
@@ -15,6 +17,10 @@ rounding points (test_bf16_bound.py derives the factor, sigma_28 / sigma_2 =
 mass; the argmax must match wherever the oracle's top-2 margin is at least
 2 z (0.13 nats) for single-token fields, 2 ls per token on deeper paths.
 """
+import importlib.util
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -211,5 +217,57 @@ def test_7b_full_depth_long_prefix_invariants():
     assert s["prefill_passes"] == 1 and s["branch_passes"] == 2
     print(f"[cfg4-full] prefill {s['last_prefill_ms']:.1f} ms, branch {s['last_branch_ms']:.2f} ms, "
           f"readout {s['last_readout_ms']:.2f} ms, {s['last_branch_tokens']} branch tokens", flush=True)
+    st.close()
+    m.close()
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_7b_two_layer_full_prefix_against_stored_oracle():
+    """The 7B shape on its first 2 layers with the WHOLE 16,384-token
+    prefix and all 64 fields (one 200-option 3-token ID field): every
+    readout's log-sum-exp and gathered logits, every candidate's log-score
+    and probability, every field's mass and argmax against the fp64
+    oracle's values, stored by tests/golden/make_cfg4_l2_golden.py (which
+    calls only the oracle; it needs about 12 minutes of CPU).  The long-key
+    path (256 key tiles of the prefix per attention row block) is compared
+    element by element here.  A cached prefix gives the exact result for
+    any continuation ("Parallel Constrained Decoding from Scratch", "The
+    piece of plumbing you need: the KV cache")."""
+    with open(os.path.join(GOLDEN, "cfg4_l2_full_prefix.json")) as fh:
+        g = json.load(fh)
+    spec = importlib.util.spec_from_file_location("mk", os.path.join(GOLDEN, "make_cfg4_l2_golden.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    wl = pi.make_workload("cfg4")
+    req = wl.requests[0]
+    assert mk.tokens_sha(req.prefix, req.fields) == g["tokens_sha256"], "the input generators changed"
+    w = pi.make_weights(pi.SHAPES["qwen2.5-7b"], g["weight_seed"], n_layers=g["n_layers"])
+    sh = w.shape
+    m, dev = _model(sh, w, [req.prefix], [req.fields])
+    del w
+    st = m.prefill(req.prefix)
+    got = m.decide(st, req.fields, debug=True)
+    tol = tl.BF16_7B_L2
+    depth = np.array(g["cand_depth"])
+    d = {"lse": float(np.max(np.abs(got["lse"] - np.array(g["lse"])))),
+         "z": float(np.max(np.abs(got["z"] - np.array(g["z"])))),
+         "ls/len": float(np.max(np.abs(got["logscore"] - np.array(g["logscore"])) / depth)),
+         "prob": float(np.max(np.abs(got["prob"] - np.array(g["prob"])))),
+         "mass_rel": float(np.max(np.abs(got["mass"] - np.array(g["mass"])) / np.array(g["mass"])))}
+    agree = sum(int(a == b) for a, b in zip(got["argmax"], g["argmax"]))
+    print("[cfg4-L2-P16384] max errors: " + ", ".join(f"{k} {v:.3e}" for k, v in d.items()) +
+          f"; argmax {agree}/{len(g['argmax'])}, min margin {min(g['margin']):.3f}", flush=True)
+    assert len(got["lse"]) == len(g["lse"]) and len(got["z"]) == len(g["z"])
+    assert d["lse"] <= tol["lse"] and d["z"] <= tol["z"]
+    assert d["ls/len"] <= tol["ls"] and d["prob"] <= tol["prob"] and d["mass_rel"] <= tol["mass"]
+    off = g["field_cand_off"]
+    for f in range(len(g["argmax"])):
+        fd = int(depth[off[f]:off[f + 1]].max())
+        if g["margin"][f] >= tl.margin_waiver(tol, fd):
+            assert int(got["argmax"][f]) == g["argmax"][f], (f, g["margin"][f])
+    _invariants([got])
+    _field_sums_to_one([got], [req.fields])
     st.close()
     m.close()
