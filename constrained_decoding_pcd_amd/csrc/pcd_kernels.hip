@@ -1750,9 +1750,13 @@ void readout_lse(const float2 *part, int32_t n_tiles, int32_t R, float *lse, hip
 // divides the sum by the path length.  A label's score is the log-sum-exp of
 // its spellings' scores.  The scores are written to c.logscore first and read
 // back from there (same thread).
-__global__ void k_combine(CombineCall c) {
-    const int f = blockIdx.x * blockDim.x + threadIdx.x;
-    if (f >= c.n_fields) return;
+// One wave per field: lane l scores candidates c0 + l, c0 + l + 64, ...
+// (each with its own spellings and paths), then the wave reduces the
+// maximum (ties to the lowest candidate index), the runner-up, the softmax
+// denominator and the mass.  The 255-option ID field is 4 candidates per
+// lane instead of a serial loop of 255.
+__global__ __launch_bounds__(64) void k_combine(CombineCall c) {
+    const int f = blockIdx.x, lane = threadIdx.x;
     const int c0 = c.f_cand_off[f], c1 = c.f_cand_off[f + 1];
     const int mode = c.f_mode[f];
     auto norm = [&](int r) {
@@ -1772,9 +1776,10 @@ __global__ void k_combine(CombineCall c) {
         }
         return mode == SCORE_MEAN ? s / (float)(i1 - i0) : s;
     };
-    float best = -INFINITY, second = -INFINITY;
-    int arg = 0;
-    for (int k = c0; k < c1; ++k) {
+    // this lane's candidates: their scores, the lane's best (first on ties)
+    float best = -INFINITY;
+    int arg = c1;  // past the field: no candidate on this lane
+    for (int k = c0 + lane; k < c1; k += 64) {
         const int s0 = c.c_spell_off[k], s1 = c.c_spell_off[k + 1];
         float s = spelling(s0);
         if (s1 - s0 > 1) {
@@ -1786,28 +1791,45 @@ __global__ void k_combine(CombineCall c) {
         }
         c.logscore[k] = s;
         if (s > best) {
-            second = best;
             best = s;
-            arg = k - c0;
-        } else if (s > second) {
-            second = s;
+            arg = k;
         }
     }
+    // wave maximum; equal values go to the lower candidate index
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o);
+        const int oa = __shfl_xor(arg, o);
+        if (ob > best || (ob == best && oa < arg)) {
+            best = ob;
+            arg = oa;
+        }
+    }
+    // the runner-up: the largest score of every other candidate (equal to the
+    // best when two candidates tie); the lane's own writes are visible to it
+    float second = -INFINITY;
+    for (int k = c0 + lane; k < c1; k += 64)
+        if (k != arg) second = fmaxf(second, c.logscore[k]);
+    second = wave_max(second);
     const float invT = 1.0f / c.temperature;
     float den = 0.f;
-    for (int k = c0; k < c1; ++k) den += __expf((c.logscore[k] - best) * invT);
-    for (int k = c0; k < c1; ++k) c.prob[k] = __expf((c.logscore[k] - best) * invT) / den;
+    for (int k = c0 + lane; k < c1; k += 64) den += __expf((c.logscore[k] - best) * invT);
+    den = wave_sum(den);
+    for (int k = c0 + lane; k < c1; k += 64) c.prob[k] = __expf((c.logscore[k] - best) * invT) / den;
     const int root = c.f_ro_root[f];
     float mass = 0.f;
-    for (int gi = c.g_off[root]; gi < c.g_off[root + 1]; ++gi) mass += __expf(c.z[gi] - c.lse[root]);
-    c.mass[f] = mass;
-    c.margin[f] = best - second;
-    c.argmax[f] = arg;
+    for (int gi = c.g_off[root] + lane; gi < c.g_off[root + 1]; gi += 64) mass += __expf(c.z[gi] - c.lse[root]);
+    mass = wave_sum(mass);
+    if (lane == 0) {
+        c.mass[f] = mass;
+        c.margin[f] = best - second;
+        c.argmax[f] = arg - c0;
+    }
 }
 
 void combine(const CombineCall &c, hipStream_t st) {
     if (c.n_fields <= 0) return;
-    hipLaunchKernelGGL(k_combine, dim3((c.n_fields + 63) / 64), dim3(64), 0, st, c);
+    hipLaunchKernelGGL(k_combine, dim3(c.n_fields), dim3(64), 0, st, c);
 }
 
 }  // namespace pcd
