@@ -140,6 +140,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    # torch ships its own HIP runtime under the same soname as the system's;
+    # whichever is loaded first serves the whole process.  Loading torch
+    # first makes the library share the runtime that owns torch's device
+    # memory and streams (loaded the other way round, pinned host allocations
+    # were seen to fail).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = POINTER
     sig = {

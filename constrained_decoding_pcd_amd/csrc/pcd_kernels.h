@@ -59,6 +59,7 @@ struct GemmCall {
     const int32_t *g_tok, *g_ro;  // Readout: gathered token ids and their readout rows
     int32_t n_gather;
     float *g_logit;          // Readout: [n_gather]
+    int32_t stagger;         // k-stage rotation per row tile (0: every tile in k order)
 };
 
 // Returns false (and does nothing) on a shape the kernels do not support.

@@ -128,6 +128,7 @@ template <int NB> struct GemmArgs {
     BSegs B[NB];
     int32_t M, N, K;
     int32_t tiles_m, tiles_n, splits, k_per_split, total, per_xcd;
+    int32_t stagger;  // k-stages by which each row tile's k order is rotated against the previous one
 };
 
 struct EpiArgs {
@@ -251,9 +252,15 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
             bsrc[q][i] = reinterpret_cast<const char *>(reinterpret_cast<const T *>(sg.ptr[s]) +
                                                          (size_t)(n - sg.begin[s]) * g.K + kbeg + c * CH);
         }
+    // The row tiles of one column slab run at once on one XCD and read the
+    // same weight lines; each starts its k loop `stagger` stages after the
+    // previous row tile's start (in a rotated order), so that most of them
+    // read lines another one fetched a few stages earlier, from L2.
+    const int rot = nkt > 0 ? (int)(((int64_t)tm * g.stagger) % nkt) : 0;
     auto issue = [&](int kt) {
         const uint32_t sb = lds_base + (uint32_t)((kt % S) * STAGE);
-        const size_t ko = (size_t)kt * KB;
+        const int kk = kt + rot;
+        const size_t ko = (size_t)(kk >= nkt ? kk - nkt : kk) * KB;
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + ko, sb + (uint32_t)((i * NW + w) * 1024));
 #pragma unroll
@@ -511,6 +518,7 @@ static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     g.k_per_split = c.K / splits;
     g.total = g.tiles_m * g.tiles_n * g.splits;
     g.per_xcd = (g.total + 7) / 8;
+    g.stagger = c.stagger;
     static_assert(BK > 0, "");
     EpiArgs e;
     e.x = c.x;
@@ -580,7 +588,24 @@ static void gemm_resid_cfg(const GemmCall &c, hipStream_t st) {
 // Tile shapes per row-count regime, chosen from measurements at the 1.5B
 // widths (d 1536, FFN 8960, vocabulary 151936) on MI355X.  fp32 models (the
 // tiny configuration) use 32-row tiles with 256-byte k-tiles throughout.
-template <typename T> static bool gemm_t(const GemmCall &c, hipStream_t st) {
+// k-order stagger of the row tiles (GemmArgs::stagger) per GEMM at up to
+// 1,024 rows, measured at the 1.5B widths with cold weights: QKV (9 to 13
+// row tiles per weight slab) 3 stages (13.4 -> 11.7 us at 287 rows, 16.3 ->
+// 14.4 us at 799); gate/up and down 1 stage (4-7% and 2-3%); the O
+// projection none (1 stage is 3% slower at 799 rows).
+static int stagger_for(const GemmCall &c) {
+    if (c.M > 1024) return 0;
+    switch (c.epi) {
+        case Epi::Qkv: return 3;
+        case Epi::SwiGlu: return 1;
+        case Epi::Resid: return c.K >= 4096 ? 1 : 0;
+        default: return 0;
+    }
+}
+
+template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
+    GemmCall c = c0;
+    if (sizeof(T) == 2) c.stagger = stagger_for(c0);
     constexpr int KB = sizeof(T) == 2 ? 128 : 256;
     constexpr int BK = KB / sizeof(T);
     if (c.M <= 0 || c.N % 128 || c.K % BK) return false;
