@@ -588,13 +588,14 @@ static void gemm_resid_cfg(const GemmCall &c, hipStream_t st) {
 // Tile shapes per row-count regime, chosen from measurements at the 1.5B
 // widths (d 1536, FFN 8960, vocabulary 151936) on MI355X.  fp32 models (the
 // tiny configuration) use 32-row tiles with 256-byte k-tiles throughout.
-// k-order stagger of the row tiles (GemmArgs::stagger) per GEMM at up to
-// 1,024 rows, measured at the 1.5B widths with cold weights: QKV (9 to 13
-// row tiles per weight slab) 3 stages (13.4 -> 11.7 us at 287 rows, 16.3 ->
-// 14.4 us at 799); gate/up and down 1 stage (4-7% and 2-3%); the O
-// projection none (1 stage is 3% slower at 799 rows).
+// k-order stagger of the row tiles (GemmArgs::stagger) per GEMM, measured
+// with cold weights at the 1.5B widths: QKV (9 to 25 row tiles per weight
+// slab) 3 stages (13.4 -> 11.7 us at 287 rows, 16.3 -> 14.4 us at 799);
+// gate/up and down 1 stage (4-7% and 2-3% at 287-799 rows); the O
+// projection none (1 stage is 3% slower at 799 rows).  In the 16,384-token
+// 7B prefill and the 64-request batch, gate/up gains 1.5-3% and the others
+// stay within 1%.
 static int stagger_for(const GemmCall &c) {
-    if (c.M > 1024) return 0;
     switch (c.epi) {
         case Epi::Qkv: return 3;
         case Epi::SwiGlu: return 1;
