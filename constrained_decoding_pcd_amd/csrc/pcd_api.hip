@@ -52,12 +52,44 @@ bool misaligned(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0
 constexpr int ATT_TARGET_BLOCKS = 64;
 constexpr int ATT_MIN_SPLIT_TILES = 2;  // 64-key tiles
 constexpr int MAX_PASS_ROWS = 1 << 18;  // token rows of one decoder pass
+// Long key ranges: a block's chain of key tiles is split when it is longer
+// than the whole launch's tile count spread over two blocks per compute unit
+// (the 7B shape's 668 branch rows over a 16,384-token prefix: 292 row
+// blocks of 256 tiles each, whose chains set the kernel's length), and no
+// split there is shorter than ATT_LONG_MIN_TILES.
+constexpr int ATT_SLOTS = 2 * 256;
+constexpr int ATT_LONG_MIN_TILES = 16;
 // Key splits of a row block: enough for `row_blocks` blocks to reach the
-// target count, no split shorter than the minimum, at most MAX_SPLITS.
-static int att_splits(int64_t row_blocks, int key_tiles) {
+// target count, no split shorter than the minimum, at most MAX_SPLITS; or,
+// for the equally long chains of branch rows (not causal ones, whose
+// lengths vary and whose long chains start first), enough that no chain
+// exceeds the per-slot share.
+static int att_splits(int64_t row_blocks, int key_tiles, bool causal) {
     const int64_t want = (ATT_TARGET_BLOCKS + row_blocks - 1) / std::max<int64_t>(1, row_blocks);
     const int by_len = std::max(1, key_tiles / ATT_MIN_SPLIT_TILES);
-    return (int)std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)MAX_SPLITS, (int64_t)by_len}));
+    const int64_t share = std::max<int64_t>(ATT_LONG_MIN_TILES,
+                                            (std::max<int64_t>(1, row_blocks) * key_tiles + ATT_SLOTS - 1) / ATT_SLOTS);
+    const int64_t want_long = causal ? 1 : (key_tiles + share - 1) / share;
+    return (int)std::max<int64_t>(1, std::min<int64_t>({std::max(want, want_long), (int64_t)MAX_SPLITS, (int64_t)by_len}));
+}
+
+// Key tiles a block walks (prefix part up to its last row's causal bound,
+// plus its branch keys).
+static int block_tiles(const AttnBlock &b, int grp) {
+    int kmax = b.key1;
+    if (b.causal) kmax = std::min(kmax, b.qoff + (b.row0 + b.nrows - 1) / grp + 1);
+    int n = kmax > b.key0 ? (kmax - b.key0 + 63) / 64 : 0;
+    if (b.sfx_hi > b.sfx_lo) n += (b.sfx_hi - b.sfx_lo + 63) / 64;
+    return n;
+}
+
+// Blocks with the longest key chains first.  Workgroups are handed out in
+// index order, so the longest chains start first and the short ones fill
+// the compute units behind them; in row order the longest causal rows
+// would start last and run alone at the end of the launch.
+static void longest_first(std::vector<AttnBlock> &v, size_t from, size_t to, int grp) {
+    std::stable_sort(v.begin() + from, v.begin() + to,
+                     [grp](const AttnBlock &a, const AttnBlock &b) { return block_tiles(a, grp) > block_tiles(b, grp); });
 }
 
 struct Layout {
@@ -628,7 +660,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     std::vector<AttnBlock> blocks;
     const int rows = n * grp;
     const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + ATT_ROWS - 1) / ATT_ROWS);
-    int ns = att_splits(row_blocks, (keys + 63) / 64);
+    int ns = att_splits(row_blocks, (keys + 63) / 64, true);
     const int slen = ((keys + ns - 1) / ns + 63) / 64 * 64;
     ns = (keys + slen - 1) / slen;
     for (int g = 0; g < c.n_kv_heads; ++g)
@@ -637,6 +669,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
             for (int k = 0; k < ns && k * slen <= t_last; ++k)
                 blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0, 1, P0});
         }
+    longest_first(blocks, 0, blocks.size(), grp);
     if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
     std::vector<int32_t> tok_splits(n);
     for (int t = 0; t < n; ++t) tok_splits[t] = (P0 + t) / slen + 1;
@@ -746,7 +779,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
         row_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + ATT_ROWS - 1) / ATT_ROWS);
     }
     const int n = t0[n_seqs];
-    int ns = att_splits(row_blocks, (max_len + 63) / 64);
+    int ns = att_splits(row_blocks, (max_len + 63) / 64, true);
     const int slen = ((max_len + ns - 1) / ns + 63) / 64 * 64;
     ns = (max_len + slen - 1) / slen;
     std::vector<AttnBlock> blocks;
@@ -759,6 +792,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
                     blocks.push_back(AttnBlock{r, g, r0, nr, k * slen, std::min(lens[r], (k + 1) * slen), k, ns, 0, 0,
                                                1, -t0[r]});
             }
+    longest_first(blocks, 0, blocks.size(), grp);
     if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
     std::vector<int32_t> tok_splits(n), pos(n), req(n);
     std::vector<uint64_t> base(n_seqs);
@@ -1081,8 +1115,8 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     int64_t row_blocks = (int64_t)c.n_kv_heads * (((int64_t)n_new * grp + ATT_ROWS - 1) / ATT_ROWS);
     for (int r = 0; r < n_req; ++r)
         row_blocks += (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
-    auto split_keys = [&](int keys, int &s, int &slen) {
-        s = att_splits(row_blocks, (keys + 63) / 64);
+    auto split_keys = [&](int keys, bool causal, int &s, int &slen) {
+        s = att_splits(row_blocks, (keys + 63) / 64, causal);
         if (keys == 0) {
             s = 1;
             slen = 0;
@@ -1091,25 +1125,12 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
         slen = ((keys + s - 1) / s + 63) / 64 * 64;
         s = (keys + slen - 1) / slen;
     };
-    if (n_new > 0) {
-        int s, slen;
-        split_keys(P0 + n_new, s, slen);
-        any_split |= s > 1;
-        for (int t = 0; t < n_new; ++t) tok_splits[t] = (P0 + t) / slen + 1;
-        const int rows = n_new * grp;
-        for (int g = 0; g < c.n_kv_heads; ++g)
-            for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
-                const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
-                for (int k = 0; k < s && k * slen <= t_last; ++k)
-                    blocks.push_back(
-                        AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1, P0});
-            }
-    }
-    const int n_new_blocks = (int)blocks.size();  // the new tokens' blocks come first
+    // The branch tokens' blocks come first (the last layer runs only them),
+    // then the new tokens' causal blocks; each group longest chain first.
     for (int r = 0; r < n_req; ++r) {
         const int P = lens[r];
         int s, slen;
-        split_keys(P, s, slen);
+        split_keys(P, false, s, slen);
         any_split |= s > 1;
         for (int t = p.r_tok[r]; t < p.r_tok[r + 1]; ++t) tok_splits[n_new + t] = s;
         req_kv[r] = reinterpret_cast<uint64_t>(states[r]->kv);
@@ -1122,6 +1143,23 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
                     blocks.push_back(AttnBlock{r, g, r0, nr, k * slen, std::min(P, (k + 1) * slen), k, s,
                                                k == s - 1 ? p.fs[b_first] : 0, k == s - 1 ? b_last + 1 : 0, 0, 0});
             }
+    }
+    const int n_branch_blocks = (int)blocks.size();
+    longest_first(blocks, 0, blocks.size(), grp);
+    if (n_new > 0) {
+        int s, slen;
+        split_keys(P0 + n_new, true, s, slen);
+        any_split |= s > 1;
+        for (int t = 0; t < n_new; ++t) tok_splits[t] = (P0 + t) / slen + 1;
+        const int rows = n_new * grp;
+        for (int g = 0; g < c.n_kv_heads; ++g)
+            for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
+                const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
+                for (int k = 0; k < s && k * slen <= t_last; ++k)
+                    blocks.push_back(
+                        AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1, P0});
+            }
+        longest_first(blocks, n_branch_blocks, blocks.size(), grp);
     }
     if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
 
@@ -1220,9 +1258,8 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
             a.req_kv = d_kv;
             a.req_stride = d_stride;
             // the last layer needs no attention output for the new tokens
-            const int b0 = last ? n_new_blocks : 0;
-            a.blocks = d_blk + b0;
-            a.n_blocks = (int)blocks.size() - b0;
+            a.blocks = d_blk;
+            a.n_blocks = last ? n_branch_blocks : (int)blocks.size();
             a.branch0 = n_new;
             a.tok_splits = d_tsp;
             a.out = ao;
