@@ -230,6 +230,43 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}))
 
 
+def vendor_blas(sh, dev, row_counts, reps=20):
+    """The vendor BLAS (torch.matmul, bf16) on the decoder's plain GEMMs at
+    the given row counts, without epilogues: QKV, O, gate and up as one
+    [M, d] x [d, 2F] product, down.  The weights are the model's own layers,
+    taken in turn (layer l, l+1, ...) so that they are as cold as in a pass.
+    Returns {rows: {gemm: us per call}} from hipEvents around `reps` calls."""
+    import torch
+    L = sh.n_layers
+    out = {}
+    for M in row_counts:
+        res = {}
+        mats = {
+            "qkv": [torch.cat([dev[f"l{l}.wq"], dev[f"l{l}.wk"], dev[f"l{l}.wv"]]).view(torch.bfloat16) for l in range(L)],
+            "o": [dev[f"l{l}.wo"].view(torch.bfloat16) for l in range(L)],
+            "gate_up": [torch.cat([dev[f"l{l}.w_gate"], dev[f"l{l}.w_up"]]).view(torch.bfloat16) for l in range(L)],
+            "down": [dev[f"l{l}.w_down"].view(torch.bfloat16) for l in range(L)],
+        }
+        for name, ws in mats.items():
+            K = ws[0].shape[1]
+            a = torch.randn(M, K, device="cuda:0", dtype=torch.float32).to(torch.bfloat16) * 0.1
+            for i in range(3):
+                torch.matmul(a, ws[i % L].t())
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(reps):
+                torch.matmul(a, ws[i % L].t())
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+            del a
+        del mats
+        out[str(M)] = res
+    torch.cuda.empty_cache()
+    return out
+
+
 def timed_loop(step, steps, warmup):
     """Warm-up steps, then `steps` timed ones with the collector off; returns
     per-step latencies (s), the mean ms per step and the last result."""
@@ -336,6 +373,8 @@ def main():
     ap.add_argument("--concurrent-streams", type=int, default=-1,
                     help="streams of the concurrent-throughput loop (0: skip; default 3, 0 for cfg3 and cfg4). "
                          "Profiles of kernel durations use 0, so that no two kernels overlap")
+    ap.add_argument("--vendor-blas", action="store_true",
+                    help="also time the vendor BLAS (torch.matmul) on the plain GEMMs at this workload's row counts")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -638,6 +677,10 @@ def main():
         res["token_by_token"] = token_by_token
     if warm is not None:
         res["warm"] = warm
+    if args.vendor_blas and sh.dtype == "bf16":
+        rows_v = sorted({sum(P_list), Tb} | ({P_list[0] + Tb} if not batch else set()))
+        res["vendor_blas_us"] = vendor_blas(sh, dev, rows_v)
+        print(f"# vendor BLAS: {res['vendor_blas_us']}", file=sys.stderr, flush=True)
     if args.cpu_layers > 0:
         print("# timing the CPU oracle sample", file=sys.stderr, flush=True)
         model.close()
