@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -90,6 +91,49 @@ static int block_tiles(const AttnBlock &b, int grp) {
 static void longest_first(std::vector<AttnBlock> &v, size_t from, size_t to, int grp) {
     std::stable_sort(v.begin() + from, v.begin() + to,
                      [grp](const AttnBlock &a, const AttnBlock &b) { return block_tiles(a, grp) > block_tiles(b, grp); });
+}
+
+// XCD-aware block order.  Workgroup b of a launch runs on XCD b % 8, and
+// each XCD has its own L2.  The blocks that read the same keys (one
+// request's KV head and key range) are given to the same XCD(s): G such
+// groups share the 8 XCDs (group i gets XCDs i, i + G, ... when G < 8, XCD
+// i % 8 otherwise), so an XCD streams one group's keys through its L2
+// instead of every group's.  Each XCD keeps the blocks' current order
+// (longest chain first); a slot whose XCD has no block left takes one from
+// the XCD with the most left, so no slot is wasted.
+static void xcd_order(std::vector<AttnBlock> &v, size_t from, size_t to) {
+    constexpr int NX = 8;
+    if (to - from <= (size_t)NX) return;
+    std::vector<std::array<int32_t, 3>> keys;
+    for (size_t i = from; i < to; ++i) keys.push_back({v[i].req, v[i].g, v[i].split});
+    std::vector<std::array<int32_t, 3>> groups = keys;
+    std::sort(groups.begin(), groups.end());
+    groups.erase(std::unique(groups.begin(), groups.end()), groups.end());
+    const int G = (int)groups.size();
+    std::vector<int> seen(G, 0);
+    std::vector<AttnBlock> q[NX];
+    for (size_t i = from; i < to; ++i) {
+        const int gi = (int)(std::lower_bound(groups.begin(), groups.end(), keys[i - from]) - groups.begin());
+        int x;
+        if (G >= NX) {
+            x = gi % NX;
+        } else {
+            const int per = (NX - gi + G - 1) / G;  // XCDs gi, gi + G, ... below NX
+            x = gi + G * (seen[gi]++ % per);
+        }
+        q[x].push_back(v[i]);
+    }
+    size_t head[NX] = {};
+    for (size_t p = from; p < to; ++p) {
+        int x = (int)((p - from) % NX);
+        if (head[x] == q[x].size()) {
+            int best = -1;
+            for (int y = 0; y < NX; ++y)
+                if (head[y] < q[y].size() && (best < 0 || q[y].size() - head[y] > q[best].size() - head[best])) best = y;
+            x = best;
+        }
+        v[p] = q[x][head[x]++];
+    }
 }
 
 struct Layout {
@@ -670,6 +714,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
                 blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0, 1, P0});
         }
     longest_first(blocks, 0, blocks.size(), grp);
+    xcd_order(blocks, 0, blocks.size());
     if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
     std::vector<int32_t> tok_splits(n);
     for (int t = 0; t < n; ++t) tok_splits[t] = (P0 + t) / slen + 1;
@@ -793,6 +838,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
                                                1, -t0[r]});
             }
     longest_first(blocks, 0, blocks.size(), grp);
+    xcd_order(blocks, 0, blocks.size());
     if ((int64_t)blocks.size() > plan_block_cap(c, m->lim)) return fail(PCD_E_CAP, "too many attention blocks");
     std::vector<int32_t> tok_splits(n), pos(n), req(n);
     std::vector<uint64_t> base(n_seqs);
@@ -1146,6 +1192,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     }
     const int n_branch_blocks = (int)blocks.size();
     longest_first(blocks, 0, blocks.size(), grp);
+    xcd_order(blocks, 0, blocks.size());
     if (n_new > 0) {
         int s, slen;
         split_keys(P0 + n_new, true, s, slen);
@@ -1160,6 +1207,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
                         AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1, P0});
             }
         longest_first(blocks, n_branch_blocks, blocks.size(), grp);
+        xcd_order(blocks, n_branch_blocks, blocks.size());
     }
     if ((int64_t)blocks.size() > plan_block_cap(c, lim)) return fail(PCD_E_CAP, "too many attention blocks");
 
