@@ -1405,6 +1405,8 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     const int rr = row_ok ? blk.row0 + w * 16 + lr : blk.row0;
     const int tq = rr / grp;
     const int kend_row = blk.causal ? min(blk.qoff + tq + 1, blk.key1) : blk.key1;
+    // keys below kend_lo are visible to every row of the block (its first row's bound)
+    const int kend_lo = blk.causal ? min(blk.qoff + blk.row0 / grp + 1, blk.key1) : blk.key1;
     int kmax = blk.key1;
     if (blk.causal) {
         const int last = blk.qoff + (blk.row0 + blk.nrows - 1) / grp + 1;
@@ -1490,20 +1492,30 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
 #pragma unroll
                 for (int kf = 0; kf < KT / 16; ++kf) mma(sc[kf], kfr[kf][st], qf[st]);
         }
+        // Row maximum of the raw scores (masked keys set to -inf), then scaled:
+        // the scale is positive, so this equals the maximum of the scaled
+        // scores.  A prefix tile below every row's causal bound needs no mask.
         float mx = -INFINITY;
+        if (!SFX && k0 + KT <= kend_lo) {
 #pragma unroll
-        for (int kf = 0; kf < KT / 16; ++kf)
+            for (int kf = 0; kf < KT / 16; ++kf)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kf * 16 + lg * 4 + r;
-                bool see;
-                if constexpr (SFX) see = row_ok && key < blk.sfx_hi && row_vis_sees(vis, c, key);
-                else see = key < kend_row;
-                const float v = see ? sc[kf][r] * qscale : -INFINITY;
-                sc[kf][r] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = rows_max(mx);
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kf][r]);
+        } else {
+#pragma unroll
+            for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = k0 + kf * 16 + lg * 4 + r;
+                    bool see;
+                    if constexpr (SFX) see = row_ok && key < blk.sfx_hi && row_vis_sees(vis, c, key);
+                    else see = key < kend_row;
+                    const float v = see ? sc[kf][r] : -INFINITY;
+                    sc[kf][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+        }
+        mx = rows_max(mx) * qscale;
         if (__any(mx > m_run + RESCALE_LOG2)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
@@ -1517,14 +1529,14 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
                 for (int j = 0; j < CF; ++j) o[j][r] *= a;
             }
         }
-        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+        const float m_neg = m_run == -INFINITY ? 0.f : -m_run;
         float psum = 0.f;
         float pr[KT / 16][4];
 #pragma unroll
         for (int kf = 0; kf < KT / 16; ++kf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[kf][r] = __builtin_amdgcn_exp2f(sc[kf][r] - m_ref);
+                pr[kf][r] = __builtin_amdgcn_exp2f(fmaf(sc[kf][r], qscale, m_neg));
                 psum += pr[kf][r];
             }
         l_run += psum;
