@@ -129,6 +129,7 @@ template <int NB> struct GemmArgs {
     int32_t M, N, K;
     int32_t tiles_m, tiles_n, splits, k_per_split, total, per_xcd;
     int32_t stagger;  // k-stages by which each row tile's k order is rotated against the previous one
+    int32_t b_once;   // one row tile: every B line is read once (non-temporal loads)
 };
 
 struct EpiArgs {
@@ -153,6 +154,11 @@ __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcp
 // it before every LDS read; completion is tracked by vm_wait below.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+// The same with the non-temporal hint: for data read once, which then
+// leaves L2 first instead of pushing out lines that will be read again.
+__device__ __forceinline__ void dma16_nt(const void *g, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
 // wait until at most N vector-memory operations of this wave are in flight
 template <int N> __device__ __forceinline__ void vm_wait() {
@@ -263,11 +269,23 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
         const size_t ko = (size_t)(kk >= nkt ? kk - nkt : kk) * KB;
 #pragma unroll
         for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + ko, sb + (uint32_t)((i * NW + w) * 1024));
+        auto issue_b = [&](auto NT) {
 #pragma unroll
-        for (int q = 0; q < NB; ++q)
+            for (int q = 0; q < NB; ++q)
 #pragma unroll
-            for (int i = 0; i < B_INS; ++i)
-                dma16(bsrc[q][i] + ko, sb + (uint32_t)(A_BYTES + q * B_BYTES + (i * NW + w) * 1024));
+                for (int i = 0; i < B_INS; ++i) {
+                    const uint32_t dst = sb + (uint32_t)(A_BYTES + q * B_BYTES + (i * NW + w) * 1024);
+                    if constexpr (decltype(NT)::value) dma16_nt(bsrc[q][i] + ko, dst);
+                    else dma16(bsrc[q][i] + ko, dst);
+                }
+        };
+        // the readout of a few rows (one row tile) streams the LM head once
+        if constexpr (E == Epi::Readout && BM <= 64) {
+            if (g.b_once) issue_b(std::true_type{});
+            else issue_b(std::false_type{});
+        } else {
+            issue_b(std::false_type{});
+        }
     };
     auto frag = [&](Frag<T> &f, const char *tile, int row, int chunk) {
         const char *p0 = tile + (row * CPR + (chunk ^ (row & 7))) * 16;
@@ -519,6 +537,12 @@ static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     g.total = g.tiles_m * g.tiles_n * g.splits;
     g.per_xcd = (g.total + 7) / 8;
     g.stagger = c.stagger;
+    // With a single row tile no workgroup reads another's B lines (the
+    // 28-row LM-head readout: 97 -> 80 us); with several, the non-temporal
+    // hint evicts lines the other row tiles still need (every GEMM of the
+    // passes 5-35% slower).  Only the readout GEMM uses it: in the other
+    // one-tile GEMMs the per-load choice cost more than it saved.
+    g.b_once = g.tiles_m == 1;
     static_assert(BK > 0, "");
     EpiArgs e;
     e.x = c.x;
