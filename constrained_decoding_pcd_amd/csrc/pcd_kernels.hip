@@ -601,10 +601,10 @@ static int pick_splits(const GemmCall &c, int tiles, int BK) {
 // small), then one kernel per row adds them into the residual stream and
 // writes the next RMSNorm's bf16 input.
 template <typename T, int BM, int BN, int WM, int WN, int S, int KB = 128>
-static void gemm_resid_cfg(const GemmCall &c, hipStream_t st) {
+static void gemm_resid_cfg(const GemmCall &c, hipStream_t st, int splits = 0) {
     constexpr int BK = KB / sizeof(T);
     const int tiles = (c.M + BM - 1) / BM * (c.N / BN);
-    const int s = pick_splits(c, tiles, BK);
+    const int s = splits > 0 ? splits : pick_splits(c, tiles, BK);
     launch_gemm<T, BM, BN, WM, WN, 1, S, Epi::Partial, KB>(c, s, st);
     resid_norm(c.dt, c.part, s, c.M, c.N, c.x, c.norm_w, c.eps, c.h_out, st);
 }
@@ -664,6 +664,10 @@ template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
                     const int tn = c.N / 128;
                     if ((c.M + 31) / 32 * tn > 256 && (c.M + 63) / 64 * tn <= 256)
                         launch_gemm<T, 64, 128, 2, 4, 1, 4, Epi::Qkv>(c, 1, st);
+                    // 128-row tiles where 64-row ones would need a second round and these
+                    // fit one (7B widths, 668 rows: 35.9 against 53.3 us with 32-row tiles)
+                    else if ((c.M + 63) / 64 * tn > 256 && (c.M + 127) / 128 * tn <= 256)
+                        launch_gemm<T, 128, 128, 2, 4, 1, 3, Epi::Qkv>(c, 1, st);
                     else launch_gemm<T, 32, 128, 1, 4, 1, 4, Epi::Qkv>(c, 1, st);
                 }
                 return true;
@@ -686,11 +690,22 @@ template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
                     // 96-row tiles where 64-row ones would need a second round of
                     // workgroups and 96-row ones fit one (799 rows: 17.4 us against 18.3 us
                     // with the residual kernel)
+                    // Unsplit 128x128 tiles where 96x64 ones would need a second round and
+                    // these fit one (7B widths, 668 rows: 37.9 against 49.9 us with 64x64).
                     const int tn = c.N / 64;
                     if ((c.M + 63) / 64 * tn > 256 && (c.M + 95) / 96 * tn <= 256)
                         gemm_resid_cfg<T, 96, 64, 2, 2, 4>(c, st);
+                    else if ((c.M + 95) / 96 * tn > 256 && (c.M + 127) / 128 * (c.N / 128) <= 256)
+                        gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st, 1);
                     else gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
                 }
+                // Very long K (the 7B down projection): 256x256 tiles in 4 K-splits once
+                // that gives 160 to 256 workgroups (668 rows: 118 against 200 us with
+                // 160x128 tiles in 2 splits, residual kernel included).
+                else if (c.M <= 1024 && c.N % 256 == 0 && c.K % (4 * BK) == 0 && c.K / 4 >= 2048 &&
+                         (c.M + 255) / 256 * (c.N / 256) * 4 >= 160 && (c.M + 255) / 256 * (c.N / 256) * 4 <= 256 &&
+                         (size_t)4 * c.M * c.N <= c.part_cap)
+                    gemm_resid_cfg<T, 256, 256, 2, 4, 2>(c, st, 4);
                 // 160-row tiles where they need fewer row tiles than 128-row ones
                 // (799 rows: 5 instead of 7, so the split-K grid fits one round)
                 else if (rg == Reg::Big && c.M <= 1024 && (c.M + 159) / 160 < (c.M + 127) / 128)
@@ -713,6 +728,10 @@ template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
                 // in the single pass)
                 else if (rows * (c.N / 128) > 256 && c.N % 256 == 0 && rows * (c.N / 256) <= 256)
                     launch_gemm<T, 128, 256, 2, 4, 2, 2, Epi::SwiGlu>(c, 1, st);
+                // 256-row tiles when 128-row ones would take more than two rounds (7B
+                // widths, 668 rows: 211 against 236 us)
+                else if (rows * (c.N / 128) > 2 * 256)
+                    launch_gemm<T, 256, 128, 2, 4, 2, 2, Epi::SwiGlu>(c, 1, st);
                 else launch_gemm<T, 128, 128, 2, 4, 2, 3, Epi::SwiGlu>(c, 1, st);
                 return true;
             }
