@@ -57,10 +57,16 @@ __device__ __forceinline__ void ld4x2(Frag<float> &f, const float *p0, const flo
     f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
+// 8 floats to bf16 (round to nearest even), two per packed conversion
+typedef float float2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void from8(Frag<bf16_t> &f, const float *x) {
     u32x4 u;
-    for (int i = 0; i < 4; ++i)
-        u[i] = (uint32_t)from_f<bf16_t>(x[2 * i]) | ((uint32_t)from_f<bf16_t>(x[2 * i + 1]) << 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float2v_t v = {x[2 * i], x[2 * i + 1]};
+        u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+    }
     f.v = __builtin_bit_cast(bf16x8_t, u);
 }
 __device__ __forceinline__ void from8(Frag<float> &f, const float *x) {
