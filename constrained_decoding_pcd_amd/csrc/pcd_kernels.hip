@@ -658,8 +658,10 @@ template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
             case Epi::Qkv:
                 if (128 % c.hd) return false;
                 // many rows: 256x128 tiles once they alone fill the chip (64 x 1,024-token
-                // batched prefill: 0.69 against 0.80 ms per layer)
-                if (c.M > 1024 && (c.M + 255) / 256 * (c.N / 128) >= 240) {
+                // batched prefill: 0.69 against 0.80 ms per layer), or where 128x128 would
+                // need a second round and 256x128 fits one
+                if (c.M > 1024 && ((c.M + 255) / 256 * (c.N / 128) >= 240 ||
+                                   ((c.M + 127) / 128 * (c.N / 128) > 256 && (c.M + 255) / 256 * (c.N / 128) <= 256))) {
                     launch_gemm<T, 256, 128, 2, 4, 1, 3, Epi::Qkv>(c, 1, st);
                 } else if (c.M > 1024) {
                     launch_gemm<T, 128, 128, 2, 4, 1, 3, Epi::Qkv>(c, 1, st);
