@@ -159,10 +159,13 @@ int64_t spell_cap(const pcd_limits &l) { return l.max_spellings > 0 ? l.max_spel
 int64_t path_cap(const pcd_limits &l) { return 8 * spell_cap(l) + l.max_gathers; }
 
 // partial sums of the residual GEMMs: up to SPLITK_MAX splits below
-// SPLITK_ROWS rows, one above
+// SPLITK_ROWS rows, 4 below 4 * SPLITK_ROWS (the long-K down projection at a
+// few thousand rows), one above
 size_t splitk_floats(const pcd_config &c, const pcd_limits &l) {
     const size_t rows = (size_t)std::max(l.max_prefill_tokens, l.max_branch_tokens);
-    return std::max((size_t)SPLITK_MAX * std::min(rows, (size_t)SPLITK_ROWS), rows) * c.d_model;
+    return std::max({(size_t)SPLITK_MAX * std::min(rows, (size_t)SPLITK_ROWS),
+                     (size_t)4 * std::min(rows, (size_t)4 * SPLITK_ROWS), rows}) *
+           c.d_model;
 }
 
 Layout layout(const pcd_config &c, const pcd_limits &l) {

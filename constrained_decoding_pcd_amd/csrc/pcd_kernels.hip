@@ -707,10 +707,10 @@ template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
                         gemm_resid_cfg<T, 128, 128, 2, 4, 3>(c, st, 1);
                     else gemm_resid_cfg<T, 64, 64, 2, 2, 4>(c, st);
                 }
-                // Very long K (the 7B down projection): 256x256 tiles in 4 K-splits once
-                // that gives 160 to 256 workgroups (668 rows: 118 against 200 us with
-                // 160x128 tiles in 2 splits, residual kernel included).
-                else if (c.M <= 1024 && c.N % 256 == 0 && c.K % (4 * BK) == 0 && c.K / 4 >= 2048 &&
+                // Long K (the down projection): 256x256 tiles in 4 K-splits once that
+                // gives 160 to 256 workgroups (7B widths, 668 rows: 118 against 200 us
+                // with 160x128 tiles in 2 splits, residual kernel included).
+                else if (c.N % 256 == 0 && c.K % (4 * BK) == 0 && c.K / 4 >= 2048 &&
                          (c.M + 255) / 256 * (c.N / 256) * 4 >= 160 && (c.M + 255) / 256 * (c.N / 256) * 4 <= 256 &&
                          (size_t)4 * c.M * c.N <= c.part_cap)
                     gemm_resid_cfg<T, 256, 256, 2, 4, 2>(c, st, 4);
