@@ -53,24 +53,38 @@ bool misaligned(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0
 constexpr int ATT_TARGET_BLOCKS = 64;
 constexpr int ATT_MIN_SPLIT_TILES = 2;  // 64-key tiles
 constexpr int MAX_PASS_ROWS = 1 << 18;  // token rows of one decoder pass
-// Long key ranges: a block's chain of key tiles is split when it is longer
-// than the whole launch's tile count spread over two blocks per compute unit
-// (the 7B shape's 668 branch rows over a 16,384-token prefix: 292 row
-// blocks of 256 tiles each, whose chains set the kernel's length), and no
-// split there is shorter than ATT_LONG_MIN_TILES.
+// Long key ranges (branch rows over a long prefix, whose chains are all
+// equally long): the split count s that minimises the launch's critical path,
+// the rounds of blocks over ATT_SLOTS (two blocks per compute unit) times the
+// tiles of one chain, ceil(row_blocks * s / ATT_SLOTS) * ceil(key_tiles / s);
+// no split shorter than ATT_LONG_MIN_TILES.  (The 7B shape's 668 branch rows
+// over a 16,384-token prefix: 296 row blocks of 256 tiles.)
 constexpr int ATT_SLOTS = 2 * 256;
 constexpr int ATT_LONG_MIN_TILES = 16;
+static int64_t long_chain_splits(int64_t row_blocks, int key_tiles) {
+    int64_t best_s = 1, best = -1;
+    for (int s = 1; s <= MAX_SPLITS; ++s) {
+        const int64_t chain = (key_tiles + s - 1) / s;
+        if (s > 1 && chain < ATT_LONG_MIN_TILES) break;
+        const int64_t cost = (std::max<int64_t>(1, row_blocks) * s + ATT_SLOTS - 1) / ATT_SLOTS * chain;
+        if (best < 0 || cost < best) {
+            best = cost;
+            best_s = s;
+        }
+    }
+    return best_s;
+}
 // Key splits of a row block: enough for `row_blocks` blocks to reach the
 // target count, no split shorter than the minimum, at most MAX_SPLITS; or,
-// for the equally long chains of branch rows (not causal ones, whose
-// lengths vary and whose long chains start first), enough that no chain
-// exceeds the per-slot share.
-static int att_splits(int64_t row_blocks, int key_tiles, bool causal) {
+// in a launch of branch rows only (`equal_chains`: causal rows' lengths vary,
+// and their long chains start first), the long-chain count above if larger.
+// In a pass that also runs new tokens' causal rows, those fill the slots and
+// splitting the branch rows only adds blocks and partials (the 7B single
+// pass: 3.07 -> 3.13 ms per layer with 5 splits).
+static int att_splits(int64_t row_blocks, int key_tiles, bool equal_chains) {
     const int64_t want = (ATT_TARGET_BLOCKS + row_blocks - 1) / std::max<int64_t>(1, row_blocks);
     const int by_len = std::max(1, key_tiles / ATT_MIN_SPLIT_TILES);
-    const int64_t share = std::max<int64_t>(ATT_LONG_MIN_TILES,
-                                            (std::max<int64_t>(1, row_blocks) * key_tiles + ATT_SLOTS - 1) / ATT_SLOTS);
-    const int64_t want_long = causal ? 1 : (key_tiles + share - 1) / share;
+    const int64_t want_long = equal_chains ? long_chain_splits(row_blocks, key_tiles) : 1;
     return (int)std::max<int64_t>(1, std::min<int64_t>({std::max(want, want_long), (int64_t)MAX_SPLITS, (int64_t)by_len}));
 }
 
@@ -707,7 +721,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     std::vector<AttnBlock> blocks;
     const int rows = n * grp;
     const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + ATT_ROWS - 1) / ATT_ROWS);
-    int ns = att_splits(row_blocks, (keys + 63) / 64, true);
+    int ns = att_splits(row_blocks, (keys + 63) / 64, false);
     const int slen = ((keys + ns - 1) / ns + 63) / 64 * 64;
     ns = (keys + slen - 1) / slen;
     for (int g = 0; g < c.n_kv_heads; ++g)
@@ -827,7 +841,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
         row_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + ATT_ROWS - 1) / ATT_ROWS);
     }
     const int n = t0[n_seqs];
-    int ns = att_splits(row_blocks, (max_len + 63) / 64, true);
+    int ns = att_splits(row_blocks, (max_len + 63) / 64, false);
     const int slen = ((max_len + ns - 1) / ns + 63) / 64 * 64;
     ns = (max_len + slen - 1) / slen;
     std::vector<AttnBlock> blocks;
@@ -1165,7 +1179,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     for (int r = 0; r < n_req; ++r)
         row_blocks += (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
     auto split_keys = [&](int keys, bool causal, int &s, int &slen) {
-        s = att_splits(row_blocks, (keys + 63) / 64, causal);
+        s = att_splits(row_blocks, (keys + 63) / 64, !causal && n_new == 0);
         if (keys == 0) {
             s = 1;
             slen = 0;
