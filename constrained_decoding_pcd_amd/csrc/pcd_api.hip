@@ -80,7 +80,7 @@ static int64_t long_chain_splits(int64_t row_blocks, int key_tiles) {
 // and their long chains start first), the long-chain count above if larger.
 // In a pass that also runs new tokens' causal rows, those fill the slots and
 // splitting the branch rows only adds blocks and partials (the 7B single
-// pass: 3.07 -> 3.13 ms per layer with 5 splits).
+// pass with 5 splits: 283.1 -> 284.9 ms per request).
 static int att_splits(int64_t row_blocks, int key_tiles, bool equal_chains) {
     const int64_t want = (ATT_TARGET_BLOCKS + row_blocks - 1) / std::max<int64_t>(1, row_blocks);
     const int by_len = std::max(1, key_tiles / ATT_MIN_SPLIT_TILES);
