@@ -798,7 +798,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
                 t.part_ml = part_ml;
                 t.tok_splits = d_tsp;
                 t.out = ao;
-                m->tbegin(PCD_KC_PREFILL_ATTN, st);
+                m->tbegin(PCD_KC_OTHER, st);
                 attention_merge(t, st);
                 m->tend(st);
             }
@@ -921,7 +921,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
                 t.part_ml = part_ml;
                 t.tok_splits = d_tsp;
                 t.out = ao;
-                m->tbegin(PCD_KC_PREFILL_ATTN, st);
+                m->tbegin(PCD_KC_OTHER, st);
                 attention_merge(t, st);
                 m->tend(st);
             }
@@ -1354,7 +1354,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
                 t.part_ml = part_ml;
                 t.tok_splits = d_tsp;
                 t.out = ao;
-                m->tbegin(last ? PCD_KC_OTHER : n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_TAIL, st);
+                m->tbegin(last || n_new > 0 ? PCD_KC_OTHER : PCD_KC_BRANCH_TAIL, st);
                 attention_merge(t, st);
                 m->tend(st);
             }

@@ -419,7 +419,7 @@ int pcd_get_stats(const pcd_model *m, pcd_stats *out);
  * call's stream, and after each call the elapsed times are added to
  * per-class totals.  Enabling resets the totals. */
 #define PCD_KC_PREFILL_QKV 0     /* prefill: QKV projection + RoPE + KV write */
-#define PCD_KC_PREFILL_ATTN 1    /* prefill: causal attention */
+#define PCD_KC_PREFILL_ATTN 1    /* prefill: causal attention (its split merge counts as OTHER) */
 #define PCD_KC_PREFILL_O 2       /* prefill: O projection + residual */
 #define PCD_KC_PREFILL_GATEUP 3  /* prefill: gate/up projection + SwiGLU */
 #define PCD_KC_PREFILL_DOWN 4    /* prefill: down projection + residual */
@@ -430,9 +430,9 @@ int pcd_get_stats(const pcd_model *m, pcd_stats *out);
 #define PCD_KC_BRANCH_GATEUP 9
 #define PCD_KC_BRANCH_DOWN 10
 #define PCD_KC_READOUT_LMHEAD 11 /* LM head with online log-sum-exp and candidate gather */
-#define PCD_KC_OTHER 12          /* embedding, RMSNorm, log-sum-exp merge, combine */
+#define PCD_KC_OTHER 12          /* embedding, RMSNorm, log-sum-exp merge, combine, split merges outside the branch pass */
 #define PCD_KC_FUSED_QKV 13      /* single-pass mode (pcd_extend_decide): new and branch rows together */
-#define PCD_KC_FUSED_ATTN 14     /* single-pass mode: causal and shared-prefix attention + split merge */
+#define PCD_KC_FUSED_ATTN 14     /* single-pass mode: causal and shared-prefix attention (split merge: OTHER) */
 #define PCD_KC_FUSED_O 15
 #define PCD_KC_FUSED_GATEUP 16
 #define PCD_KC_FUSED_DOWN 17
