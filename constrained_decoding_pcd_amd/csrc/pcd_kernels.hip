@@ -211,16 +211,21 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
     constexpr int CPR = KB / 16;        // chunks per tile row per stage
     constexpr int BK = CPR * CH;        // K elements per stage
     constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB, STAGE = A_BYTES + NB * B_BYTES;
-    constexpr int A_INS = BM * CPR / (64 * NW), B_INS = BN * CPR / (64 * NW);  // DMA instructions per wave per stage
-    constexpr int LPS = A_INS + NB * B_INS;
+    // DMA instructions per wave per stage.  A tile whose rows do not split
+    // evenly over the waves (BM a multiple of 8, not of 8 NW) leaves the last
+    // instruction to the first A_GRP % NW waves only; the waits count the
+    // smaller number, which can only make a wave wait longer than it must.
+    constexpr int A_GRP = BM * CPR / 64;  // 64-lane groups of 16-byte chunks in one A stage
+    constexpr int A_INS = (A_GRP + NW - 1) / NW, B_INS = BN * CPR / (64 * NW);
+    constexpr int LPS = A_GRP / NW + NB * B_INS;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16;
     constexpr int KSTEPS = BK / 32;
     constexpr int CPL = 8 / CH;  // chunks holding one lane's 8 k-elements
     constexpr bool LDS_EPI = GemmLds<T, BM, BN, NB, E, KB>::LDS_EPI;
     static_assert((NW == 4 || NW == 8) && (KB == 128 || KB == 256), "workgroup shape");
-    static_assert(A_INS * 64 * NW == BM * CPR && B_INS * 64 * NW == BN * CPR, "tile rows per DMA instruction");
+    static_assert(A_GRP * 64 == BM * CPR && B_INS * 64 * NW == BN * CPR, "tile rows per DMA instruction");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(S >= 2 && S <= 8 && (S - 1) * LPS < 64, "pipeline depth");
+    static_assert(S >= 2 && S <= 8 && (S - 1) * (A_INS + NB * B_INS) < 64, "pipeline depth");
     static_assert(S * STAGE <= 160 * 1024, "operand ring exceeds the 160 KB of LDS");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
@@ -274,7 +279,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
         const int kk = kt + rot;
         const size_t ko = (size_t)(kk >= nkt ? kk - nkt : kk) * KB;
 #pragma unroll
-        for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + ko, sb + (uint32_t)((i * NW + w) * 1024));
+        for (int i = 0; i < A_INS; ++i)
+            if (A_GRP % NW == 0 || i * NW + w < A_GRP) dma16(asrc[i] + ko, sb + (uint32_t)((i * NW + w) * 1024));
         auto issue_b = [&](auto NT) {
 #pragma unroll
             for (int q = 0; q < NB; ++q)
@@ -732,6 +738,11 @@ template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
                 if (rg == Reg::Small) launch_gemm<T, 32, 64, 1, 4, 2, 4, Epi::SwiGlu>(c, 1, st);
                 // many rows: 256-row tiles (2,048 rows: 115 against 120 us; 65,536: 2.76 against 3.12 ms)
                 else if (c.M > 1024) launch_gemm<T, 256, 128, 2, 4, 2, 2, Epi::SwiGlu>(c, 1, st);
+                // 192-row tiles where 128-row ones would need a second round and these
+                // fit one: as many operand bytes per workgroup as 128x160, in 8 waves
+                // instead of 4 (512 rows: 39.1 against 41.7 us with cold weights)
+                else if (rows * (c.N / 128) > 256 && (c.M + 191) / 192 * (c.N / 128) <= 256)
+                    launch_gemm<T, 192, 128, 2, 4, 2, 2, Epi::SwiGlu>(c, 1, st);
                 else if (rows * (c.N / 128) > 256 && c.N % 160 == 0 && rows * (c.N / 160) <= 256)
                     launch_gemm<T, 128, 160, 2, 2, 2, 2, Epi::SwiGlu>(c, 1, st);
                 // 128x256 when that fits one round (each workgroup reads its rows of the
