@@ -1447,11 +1447,19 @@ constexpr float RESCALE_LOG2 = 8.0f;
 template <int HD> struct RingLds {
     static constexpr int KT = 64, RB = HD * 2, CPR = RB / 16, TILE = KT * RB;
     static constexpr int Q_BYTES = TILE;  // 64 query rows
-    static int bytes(int S) { return Q_BYTES + S * 2 * TILE; }
+    // H key rings (one per half of the workgroup) behind the query rows
+    static int bytes(int S, int H = 1) { return Q_BYTES + H * S * 2 * TILE; }
 };
 
-template <int HD, int S>
-__global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
+// H = 2: a workgroup of 8 waves, whose halves (waves 0-3 and 4-7) walk the
+// first and the second half of the block's key tiles, each through its own
+// ring, for the same 64 query rows; at the end the second half's (max, sum,
+// O) go through LDS to the first, which merges them and writes the rows.
+// Each key chain is half as long, two waves share each SIMD, and no merge
+// kernel runs.  Used for launches of at most 256 blocks, where each block
+// has a compute unit to itself anyway (the two rings fill 144 KB of LDS).
+template <int HD, int S, int H = 1>
+__global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
     using T = bf16_t;
     using L = RingLds<HD>;
     constexpr int KT = L::KT, RB = L::RB, CPR = L::CPR, TILE = L::TILE, STAGE = 2 * TILE;
@@ -1460,13 +1468,16 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     constexpr int HS = HD / 32, CF = HD / 16;
     static_assert(INS >= 1 && INS * 4 * 1024 == TILE, "tile / DMA mapping");
     static_assert(S >= 2 && (S - 1) * LPS + INS < 64, "vmcnt range");
+    static_assert(H == 1 || (H == 2 && S == 2), "two halves with two-stage rings");
     extern __shared__ __attribute__((aligned(16))) char attn_lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)attn_lds;
     const char *Qs = attn_lds;
-    const uint32_t ring_base = lds_base + L::Q_BYTES;
 
     const AttnBlock blk = c.blocks[blockIdx.x];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int half = (tid >> 6) / 4, w = (tid >> 6) % 4;  // w: the block's 16-row query group of this wave
+    const uint32_t ring_off = (uint32_t)(L::Q_BYTES + half * S * STAGE);  // this half's key ring
+    const uint32_t ring_base = lds_base + ring_off;
     const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
     const int P = c.req_stride[blk.req];  // slab stride (the buffer's token capacity)
     const char *kvbase = reinterpret_cast<const char *>(c.req_kv[blk.req]);
@@ -1491,6 +1502,10 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;
     const int n_sfx = blk.sfx_hi > blk.sfx_lo ? (blk.sfx_hi - blk.sfx_lo + KT - 1) / KT : 0;
     const int n_tiles = n_pre + n_sfx;
+    // this half's tiles: global indices [t_base, t_base + t_cnt); both halves
+    // run n_iter loop steps, so they meet every barrier the same number of times
+    const int n_iter = H == 1 ? n_tiles : (n_tiles + 1) / 2;
+    const int t_base = half * n_iter, t_cnt = half == 0 ? n_iter : n_tiles - n_iter;
     RowVis vis{};
     if (n_sfx > 0) {
         row_vis_init(vis, c, tq - c.branch0);
@@ -1508,7 +1523,8 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
         dcv[i] = pc ^ ((2 * drow[i]) & (CPR - 1));
     }
     // query rows: (token, head) pairs of this block; rows past nrows re-read row0
-    {
+    // (loaded by the first half; the second reads them after the first barrier)
+    if (half == 0) {
         const char *Q = reinterpret_cast<const char *>(c.q);
 #pragma unroll
         for (int i = 0; i < INS; ++i) {
@@ -1517,12 +1533,12 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
             dma16(Q + qrow * RB + dck[i] * 16, lds_base + (uint32_t)((i * 4 + w) * 1024));
         }
     }
-    auto issue = [&](int i) {
+    auto issue = [&](int i, int it) {  // tile i into ring slot it % S
         const bool sfx = i >= n_pre;
         const int k0 = sfx ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
         const int kl = sfx ? blk.sfx_hi : kmax;
         const char *Ksrc = sfx ? Kb : Kg, *Vsrc = sfx ? Vb : Vg;
-        const uint32_t sb = ring_base + (uint32_t)((i % S) * STAGE);
+        const uint32_t sb = ring_base + (uint32_t)((it % S) * STAGE);
 #pragma unroll
         for (int u = 0; u < INS; ++u) {
             const size_t key = (size_t)min(k0 + drow[u], kl - 1);  // keys past the range: a valid key, masked below
@@ -1532,7 +1548,7 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
     };
 #pragma unroll
     for (int s = 0; s + 1 < S; ++s)
-        if (s < n_tiles) issue(s);
+        if (s < t_cnt) issue(t_base + s, s);
 
     float m_run = -INFINITY, l_run = 0.f;  // reference max of query row lr (replicated over lg); this lane's share of the sum
     f32x4 o[CF];
@@ -1547,9 +1563,9 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
 
     // One key tile from ring slot i % S: prefix keys (SFX false: visible below
     // kend_row) or branch keys (SFX true: the row's scaffold and trie ancestors).
-    auto tile = [&](auto SFXC, int i) {
+    auto tile = [&](auto SFXC, int i, int it) {  // tile i from ring slot it % S
         constexpr bool SFX = decltype(SFXC)::value;
-        const char *Kt = attn_lds + L::Q_BYTES + (i % S) * STAGE, *Vt = Kt + TILE;
+        const char *Kt = attn_lds + ring_off + (it % S) * STAGE, *Vt = Kt + TILE;
         const int k0 = SFX ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
 
         // S^T tile: sc[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r)
@@ -1648,32 +1664,81 @@ __global__ __launch_bounds__(256) void k_attn_ring(AttnCall c) {
         }
     };
 
-    for (int i = 0; i < n_tiles; ++i) {
-        // tile i (and the query rows) landed: later tiles issued so far may stay in flight
-        vm_wait_ahead<LPS, S - 2>(min(S - 2, n_tiles - 1 - i));
+    for (int it = 0; it < n_iter; ++it) {
+        // this step's tile (and the query rows) landed: later tiles issued so far may stay in flight
+        vm_wait_ahead<LPS, S - 2>(max(0, min(S - 2, t_cnt - 1 - it)));
         barrier_keep_loads();
-        if (i == 0) {
+        if (it == 0) {
 #pragma unroll
             for (int st = 0; st < HS; ++st) qf[st] = frag16(Qs, w * 16 + lr, st * 4 + lg);
         }
-        // slot (i - 1) % S was read by every wave before the barrier
-        if (i + S - 1 < n_tiles) issue(i + S - 1);
-        if (i < n_pre) tile(std::false_type{}, i);
-        else tile(std::true_type{}, i);
+        // slot (it - 1) % S was read by every wave of this half before the barrier
+        if (it + S - 1 < t_cnt) issue(t_base + it + S - 1, it + S - 1);
+        if (it < t_cnt) {
+            const int i = t_base + it;
+            if (i < n_pre) tile(std::false_type{}, i, it);
+            else tile(std::true_type{}, i, it);
+        }
         lds_reads_done();
+    }
+    if constexpr (H == 2) {
+        // the second half hands its (O, max, sum share) per lane to the
+        // same lane of the first half's wave with the same query rows,
+        // through its own ring (free once every wave has passed this barrier)
+        constexpr int NV = 4 * CF + 2;
+        float *xs = reinterpret_cast<float *>(attn_lds + L::Q_BYTES + S * STAGE) + w * NV * 64 + lane;
+        static_assert(4 * NV * 64 * 4 <= S * STAGE, "hand-over area");
+        __syncthreads();
+        if (half == 1) {
+#pragma unroll
+            for (int j = 0; j < CF; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xs[(j * 4 + r) * 64] = o[j][r];
+            xs[4 * CF * 64] = m_run;
+            xs[(4 * CF + 1) * 64] = l_run;
+        }
+        __syncthreads();
+        if (half == 1) return;
+        // merge: the common reference is the larger maximum (log2 units)
+        const float m1 = xs[4 * CF * 64], l1 = xs[(4 * CF + 1) * 64];
+        const float mm = fmaxf(m_run, m1);
+        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+        l_run = l_run * a0 + l1 * a1;
+        m_run = mm;
+        // O rows are queries 4*lg + r, whose factors sit in lane 4*lg + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float b0 = __shfl(a0, lg * 4 + r), b1 = __shfl(a1, lg * 4 + r);
+#pragma unroll
+            for (int j = 0; j < CF; ++j) o[j][r] = o[j][r] * b0 + xs[(j * 4 + r) * 64] * b1;
+        }
     }
     attn_write<T, HD>(c, blk, o, m_run, rows_sum(l_run), w, lr, lg);
 }
 
-template <int HD, int S> static void launch_attn_ring(const AttnCall &c, hipStream_t st) {
-    const int shmem = RingLds<HD>::bytes(S);
+template <int HD, int S, int H> static void launch_attn_ring_h(const AttnCall &c, hipStream_t st) {
+    const int shmem = RingLds<HD>::bytes(S, H);
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_attn_ring<HD, S>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_attn_ring<HD, S, H>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_attn_ring<HD, S>), dim3(c.n_blocks), dim3(256), shmem, st, c);
+    hipLaunchKernelGGL((k_attn_ring<HD, S, H>), dim3(c.n_blocks), dim3(256 * H), shmem, st, c);
+}
+// Launches of at most one block per compute unit split each block's key
+// chain over two halves of one workgroup; larger ones keep 4-wave blocks,
+// two of which share a compute unit.
+constexpr int ATT_HALVES_MAX_BLOCKS = 256;
+template <int HD, int S> static void launch_attn_ring(const AttnCall &c, hipStream_t st) {
+    if constexpr (S == 2) {
+        if (c.n_blocks <= ATT_HALVES_MAX_BLOCKS) {
+            launch_attn_ring_h<HD, S, 2>(c, st);
+            return;
+        }
+    }
+    launch_attn_ring_h<HD, S, 1>(c, st);
 }
 
 template <typename T, int HD> static int attn_lds_bytes() {
