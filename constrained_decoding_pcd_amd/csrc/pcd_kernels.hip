@@ -13,6 +13,7 @@
 
 #include <cstdint>
 #include <type_traits>
+#include <utility>
 
 namespace pcd {
 
@@ -166,6 +167,14 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
 __device__ __forceinline__ void dma16_nt(const void *g, uint32_t lds_addr) {
     asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int... Is, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F &&f) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
 // wait until at most N vector-memory operations of this wave are in flight
 template <int N> __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
@@ -203,7 +212,7 @@ template <typename T, int BM, int BN, int NB, Epi E, int KB = 128> struct GemmLd
     static int bytes(int S) { return S * STAGE > C_BYTES ? S * STAGE : C_BYTES; }
 };
 
-template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E, int KB = 128>
+template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E, int KB = 128, bool ILV = false>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e) {
     constexpr int NW = WM * WN;         // waves per workgroup
     constexpr int NT = NW * 64;
@@ -244,7 +253,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
     const int kbeg = ks * g.k_per_split;
     const int nkt = g.k_per_split / BK;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform: LDS addresses of the DMAs stay in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w % WM, wn = w / WM;
     const int lr = lane & 15, lg = lane >> 4;
 
@@ -297,6 +307,26 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
             else issue_b(std::false_type{});
         } else {
             issue_b(std::false_type{});
+        }
+    };
+    // DMA instruction d of stage kt alone: A rows first, then each B operand's rows
+    constexpr int LPI = A_INS + NB * B_INS;  // this wave's DMA instructions per stage, at most
+    auto issue_one = [&](int kt, auto D) {
+        constexpr int d = decltype(D)::value;
+        const uint32_t sb = lds_base + (uint32_t)((kt % S) * STAGE);
+        const int kk = kt + rot;
+        const size_t ko = (size_t)(kk >= nkt ? kk - nkt : kk) * KB;
+        if constexpr (d < A_INS) {
+            if (A_GRP % NW == 0 || d * NW + w < A_GRP) dma16(asrc[d] + ko, sb + (uint32_t)((d * NW + w) * 1024));
+        } else {
+            constexpr int q = (d - A_INS) / B_INS, i = (d - A_INS) % B_INS;
+            const uint32_t dst = sb + (uint32_t)(A_BYTES + q * B_BYTES + (i * NW + w) * 1024);
+            if constexpr (E == Epi::Readout && BM <= 64) {
+                if (g.b_once) dma16_nt(bsrc[q][i] + ko, dst);
+                else dma16(bsrc[q][i] + ko, dst);
+            } else {
+                dma16(bsrc[q][i] + ko, dst);
+            }
         }
     };
     auto frag = [&](Frag<T> &f, const char *tile, int row, int chunk) {
@@ -383,11 +413,28 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
                 if constexpr (kind == 0) vm_wait<(S - 2) * LPS>();
                 else vm_wait<0>();
                 barrier_keep_loads();
-                if constexpr (kind == 0) issue(kt + S);
+                if constexpr (kind == 0 && !ILV) issue(kt + S);
                 read_frags(B0{}, kt + 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(B1{}, M0{}, MN{});
+            if constexpr (ILV && kind == 0) {
+                if (s + 2 >= KSTEPS) {
+                    // the refill's DMA instructions one at a time between runs of
+                    // buffer 1's matrix instructions, not in one burst ahead of them
+                    static_for<LPI>([&](auto D) {
+                        constexpr int d = decltype(D)::value;
+                        mfmas(B1{}, std::integral_constant<int, d * NM / LPI>{},
+                              std::integral_constant<int, (d + 1) * NM / LPI>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_one(kt + S, D);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                } else {
+                    mfmas(B1{}, M0{}, MN{});
+                }
+            } else {
+                mfmas(B1{}, M0{}, MN{});
+            }
         }
     };
 
@@ -533,7 +580,14 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
     }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E, int KB = 128>
+// ILV: the refill of each stage goes out one DMA instruction at a time
+// between runs of matrix instructions instead of in one burst ahead of them
+// (bit-identical results).  With three or more stages the refill has a
+// stage of slack and this is faster (799 rows: down 34.8 -> 32.1 us, O 11.0
+// -> 10.2 us; down at 512 rows 24.9 -> 23.9 us); with two stages it is
+// slower for 192x128 tiles (39.3 -> 41.9 us) and slightly faster for the
+// 128x256 gate/up tile (54.6 -> 54.1 us), which turns it on itself.
+template <typename T, int BM, int BN, int WM, int WN, int NB, int S, Epi E, int KB = 128, bool ILV = (S >= 3)>
 static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     constexpr int BK = KB / sizeof(T);
     GemmArgs<NB> g;
@@ -583,7 +637,7 @@ static void launch_gemm(const GemmCall &c, int splits, hipStream_t st) {
     e.n_gather = c.n_gather;
     e.g_logit = c.g_logit;
     const int shmem = GemmLds<T, BM, BN, NB, E, KB>::bytes(S);
-    auto kern = k_gemm<T, BM, BN, WM, WN, NB, S, E, KB>;
+    auto kern = k_gemm<T, BM, BN, WM, WN, NB, S, E, KB, ILV>;
     static bool attr_set = false;  // one model per thread at a time; a repeated set is harmless
     if (!attr_set) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -750,7 +804,7 @@ template <typename T> static bool gemm_t(const GemmCall &c0, hipStream_t st) {
                 // 799 rows: 54.2 against 58.6 us with cold weights, 51.9 against 53.0 us
                 // in the single pass)
                 else if (rows * (c.N / 128) > 256 && c.N % 256 == 0 && rows * (c.N / 256) <= 256)
-                    launch_gemm<T, 128, 256, 2, 4, 2, 2, Epi::SwiGlu>(c, 1, st);
+                    launch_gemm<T, 128, 256, 2, 4, 2, 2, Epi::SwiGlu, 128, true>(c, 1, st);
                 // 256-row tiles when 128-row ones would take more than two rounds (7B
                 // widths, 668 rows: 211 against 236 us)
                 else if (rows * (c.N / 128) > 2 * 256)
