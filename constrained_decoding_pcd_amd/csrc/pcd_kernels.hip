@@ -74,6 +74,17 @@ __device__ __forceinline__ void from8(Frag<float> &f, const float *x) {
     for (int i = 0; i < 8; ++i) f.v[i] = x[i];
 }
 
+// 8 floats to 8 consecutive elements at p (16-byte aligned), in 16-byte stores
+__device__ __forceinline__ void store8(bf16_t *p, const float *x) {
+    Frag<bf16_t> f;
+    from8(f, x);
+    *reinterpret_cast<bf16x8_t *>(p) = f.v;
+}
+__device__ __forceinline__ void store8(float *p, const float *x) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
 __device__ __forceinline__ void mma(f32x4 &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
 }
@@ -525,31 +536,48 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(GemmArgs<NB> g, EpiArgs e
                 s_dst[r * 4 + hh] = reinterpret_cast<uint64_t>(dst);
             }
             __syncthreads();
-            constexpr int PAIRS = BM * (BN / 2), IT = PAIRS / NT;
-            static_assert(IT * NT == PAIRS && BN == 128, "pairs per thread");
-            float2 cs[IT];
+            // Each item is a run of 8 pairs (j .. j+7 with j + hd/2 ..): its
+            // (cos, sin) values and both 8-column runs of the tile row are read
+            // in 16-byte vectors and the two runs go out as 16-byte stores
+            // (hd/2 is a multiple of 8 for head dims 32, 64 and 128).
+            constexpr int RUN = 8, RPR = BN / 2 / RUN, ITEMS = BM * RPR, IT = ITEMS / NT;
+            static_assert(IT * NT == ITEMS && BN == 128, "runs per thread");
+            float4 cs[IT][RUN / 2];  // (cos, sin) of pairs j + 2q and j + 2q + 1
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
-                const int idx = tid + it * NT, r = idx / (BN / 2), c = idx % (BN / 2);
+                const int idx = tid + it * NT, r = idx / RPR, c = (idx % RPR) * RUN;
                 const int hh = c / half, j = c % half;
                 const bool rot = m0 + r < g.M && n0 + hh * hd < e.n_q + e.n_k;
-                cs[it] = rot ? e.rope[(size_t)s_pos[r] * half + j] : make_float2(1.f, 0.f);
+                const float4 *src = reinterpret_cast<const float4 *>(e.rope + (size_t)(rot ? s_pos[r] : 0) * half + j);
+#pragma unroll
+                for (int q = 0; q < RUN / 2; ++q) cs[it][q] = rot ? src[q] : make_float4(1.f, 0.f, 1.f, 0.f);
             }
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
-                const int idx = tid + it * NT, r = idx / (BN / 2), c = idx % (BN / 2);
+                const int idx = tid + it * NT, r = idx / RPR, c = (idx % RPR) * RUN;
                 const int hh = c / half, j = c % half;
                 T *dst = reinterpret_cast<T *>(s_dst[r * 4 + hh]);
                 if (!dst) continue;  // row past M
-                const int col = hh * hd + j;
-                float v1 = Cs[r * LDC + col], v2 = Cs[r * LDC + col + half];
-                if (n0 + hh * hd < e.n_q + e.n_k) {
-                    const float o1 = v1 * cs[it].x - v2 * cs[it].y, o2 = v2 * cs[it].x + v1 * cs[it].y;
-                    v1 = o1;
-                    v2 = o2;
+                const float *c1 = Cs + r * LDC + hh * hd + j, *c2 = c1 + half;
+                float v1[RUN], v2[RUN];
+#pragma unroll
+                for (int q = 0; q < RUN / 4; ++q) {
+                    const float4 a = reinterpret_cast<const float4 *>(c1)[q], b = reinterpret_cast<const float4 *>(c2)[q];
+                    v1[4 * q] = a.x; v1[4 * q + 1] = a.y; v1[4 * q + 2] = a.z; v1[4 * q + 3] = a.w;
+                    v2[4 * q] = b.x; v2[4 * q + 1] = b.y; v2[4 * q + 2] = b.z; v2[4 * q + 3] = b.w;
                 }
-                dst[j] = from_f<T>(v1);
-                dst[j + half] = from_f<T>(v2);
+                if (n0 + hh * hd < e.n_q + e.n_k) {
+#pragma unroll
+                    for (int k = 0; k < RUN; ++k) {
+                        const float4 t = cs[it][k / 2];
+                        const float co = (k & 1) ? t.z : t.x, si = (k & 1) ? t.w : t.y;
+                        const float o1 = v1[k] * co - v2[k] * si, o2 = v2[k] * co + v1[k] * si;
+                        v1[k] = o1;
+                        v2[k] = o2;
+                    }
+                }
+                store8(dst + j, v1);
+                store8(dst + j + half, v2);
             }
         } else if constexpr (E == Epi::Readout) {
             // per readout row: max and sum of exp over each 128 vocab columns of
