@@ -1290,6 +1290,37 @@ __device__ __forceinline__ void attn_write(const AttnCall &c, const AttnBlock &b
     }
 }
 
+// The same for an O whose lane holds its own query row lr, columns
+// 16 j + 4 lg .. + 3 (P*V with V's fragment as the first operand): four
+// adjacent outputs per store, and the row's (max, sum) already in the lane.
+template <typename T, int HD>
+__device__ __forceinline__ void attn_write_rows(const AttnCall &c, const AttnBlock &blk, const f32x4 (&o)[HD / 16],
+                                                float m_run, float l_run, int w, int lr, int lg) {
+    constexpr int CF = HD / 16;
+    const int Hq = c.n_heads, grp = Hq / c.n_kv_heads;
+    if (w * 16 + lr >= blk.nrows) return;
+    const int row = blk.row0 + w * 16 + lr;
+    const int t = row / grp, h = blk.g * grp + row % grp;
+    if (blk.causal && blk.qoff + t < blk.key0) return;  // causal row with no key in this split
+    if (c.tok_splits[t] <= 1) {
+        T *out = reinterpret_cast<T *>(c.out) + ((size_t)t * Hq + h) * HD + 4 * lg;
+        const float inv = 1.0f / l_run;
+#pragma unroll
+        for (int j = 0; j < CF; ++j) {
+            const float2v_t lo = {o[j][0] * inv, o[j][1] * inv}, hi = {o[j][2] * inv, o[j][3] * inv};
+            const uint2 u = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v_t)),
+                             __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v_t))};
+            *reinterpret_cast<uint2 *>(out + j * 16) = u;
+        }
+    } else {
+        const size_t pi = ((size_t)blk.split * c.n_tokens + t) * Hq + h;
+        float *po = c.part_o + pi * HD + 4 * lg;
+#pragma unroll
+        for (int j = 0; j < CF; ++j) *reinterpret_cast<f32x4 *>(po + j * 16) = o[j];
+        if (lg == 0) c.part_ml[pi] = make_float2(m_run, l_run);
+    }
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnCall c) {
     constexpr int KT = 64;
@@ -1695,13 +1726,11 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
             l_run *= alpha;
             m_run = m_new;
-            // O rows are queries 4*lg + r, whose factor sits in lane 4*lg + r
+            // o holds this lane's own query row lr (columns 16 j + 4 lg + r)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float a = __shfl(alpha, lg * 4 + r);
+            for (int j = 0; j < CF; ++j)
 #pragma unroll
-                for (int j = 0; j < CF; ++j) o[j][r] *= a;
-            }
+                for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
         }
         const float m_neg = m_run == -INFINITY ? 0.f : -m_run;
         float psum = 0.f;
@@ -1742,7 +1771,7 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
             Frag<T> pa;
             from8(pa, pv);
 #pragma unroll
-            for (int j = 0; j < CF; ++j) mma(o[j], pa, vfr[st][j]);
+            for (int j = 0; j < CF; ++j) mma(o[j], vfr[st][j], pa);  // V first: o[j] is O^T's layout
         }
     };
 
@@ -1788,15 +1817,12 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
         const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
         l_run = l_run * a0 + l1 * a1;
         m_run = mm;
-        // O rows are queries 4*lg + r, whose factors sit in lane 4*lg + r
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float b0 = __shfl(a0, lg * 4 + r), b1 = __shfl(a1, lg * 4 + r);
+        for (int j = 0; j < CF; ++j)
 #pragma unroll
-            for (int j = 0; j < CF; ++j) o[j][r] = o[j][r] * b0 + xs[(j * 4 + r) * 64] * b1;
-        }
+            for (int r = 0; r < 4; ++r) o[j][r] = o[j][r] * a0 + xs[(j * 4 + r) * 64] * a1;
     }
-    attn_write<T, HD>(c, blk, o, m_run, rows_sum(l_run), w, lr, lg);
+    attn_write_rows<T, HD>(c, blk, o, m_run, rows_sum(l_run), w, lr, lg);
 }
 
 template <int HD, int S, int H> static void launch_attn_ring_h(const AttnCall &c, hipStream_t st) {
