@@ -19,6 +19,8 @@ attention probabilities and outputs, SwiGLU outputs) and the KV cache to
 bf16, a relative error of 2^-9 per element; test_bf16_bound.py relates them
 to a model of those rounding points.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -321,6 +323,43 @@ def test_tiny_errors_before_device_work(tiny_w):
     assert np.all(np.isfinite(got["prob"]))
     st.close()
     m.close()
+
+
+# ---------------------------------------------------------------------------
+# bf16 at head dims 32 and 64 (the bf16 workloads all use 128)
+# ---------------------------------------------------------------------------
+
+def _small_bf16_shape(hd):
+    """The tiny widths (d 128, FFN 384, vocabulary 2048) in bf16 with 32- or
+    64-wide heads (4 query / 2 KV heads, or 2 / 1), room for 8,448 tokens."""
+    heads = {32: (4, 2), 64: (2, 1)}[hd]
+    return dataclasses.replace(pi.SHAPES["tiny"], name=f"tiny-bf16-hd{hd}", dtype="bf16", head_dim=hd,
+                               n_heads=heads[0], n_kv_heads=heads[1], max_seq=8448)
+
+
+@pytest.mark.parametrize("hd", [32, 64])
+def test_bf16_small_head_dims(hd):
+    """The attention kernel's 32- and 64-wide instances and the GEMM tiles at
+    width 128 in bf16.  Three ragged requests with deep tries in one branch
+    pass (launches of a few blocks: two key chains per workgroup), then one
+    long prefix whose prefill launch has more than 256 row blocks (4-wave
+    blocks) and whose branch rows split their keys over workgroups."""
+    sh = _small_bf16_shape(hd)
+    w = pi.make_weights(sh, 1003)
+    dec = odec.Decoder(w, np.float64)
+    V = sh.vocab_size
+    rng = np.random.default_rng(40 + hd)
+    reqs = []
+    for k, P in enumerate((1, 65, 130)):
+        prefix = [int(t) for t in rng.integers(0, V, size=P)]
+        reqs.append((prefix, pi.random_trie_fields(4000 + k, V, 3, max_cands=8, max_len=3)))
+    _run_case(f"bf16-hd{hd}-multi", sh, w, reqs, dec=dec)
+    # row blocks of the prefill: tokens x (query heads per KV head) / 64 x KV heads > 256
+    P = {32: 4200, 64: 8300}[hd]
+    assert P * (sh.n_heads // sh.n_kv_heads) // 64 * sh.n_kv_heads > 256
+    prefix = [int(t) for t in rng.integers(0, V, size=P)]
+    _run_case(f"bf16-hd{hd}-long", sh, w, [(prefix, pi.random_trie_fields(4100, V, 3, max_cands=6, max_len=3))],
+              dec=dec)
 
 
 # ---------------------------------------------------------------------------
