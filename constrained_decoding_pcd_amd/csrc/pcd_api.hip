@@ -33,6 +33,14 @@ int fail(int code, const std::string &msg) {
 
 constexpr int MAX_SPLITS = ATT_MAX_SPLITS;  // key splits of one attention row block
 constexpr int ATT_ROWS = 64;          // query rows per attention workgroup
+// Causal prefill launches (no branch keys) in bf16 use blocks of 128 query
+// rows, two 16-row groups per wave, when those alone give at least
+// ATT_WIDE_MIN_BLOCKS workgroups (two per compute unit): each K and V
+// fragment read from LDS then feeds twice the matrix work.
+constexpr int ATT_WIDE_ROWS = 128;
+#ifndef ATT_WIDE_MIN_BLOCKS
+#define ATT_WIDE_MIN_BLOCKS 512
+#endif
 constexpr int SPLITK_MAX = 8;
 constexpr int SPLITK_ROWS = 1024;     // split-K is only used below this many rows
 constexpr uint64_t STATE_MAGIC = 0x70636473746174ull;
@@ -720,13 +728,16 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     const int keys = P0 + n;
     std::vector<AttnBlock> blocks;
     const int rows = n * grp;
-    const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + ATT_ROWS - 1) / ATT_ROWS);
+    const bool wide = c.dtype == PCD_DTYPE_BF16 &&
+                      (int64_t)c.n_kv_heads * ((rows + ATT_WIDE_ROWS - 1) / ATT_WIDE_ROWS) >= ATT_WIDE_MIN_BLOCKS;
+    const int arows = wide ? ATT_WIDE_ROWS : ATT_ROWS;
+    const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + arows - 1) / arows);
     int ns = att_splits(row_blocks, (keys + 63) / 64, false);
     const int slen = ((keys + ns - 1) / ns + 63) / 64 * 64;
     ns = (keys + slen - 1) / slen;
     for (int g = 0; g < c.n_kv_heads; ++g)
-        for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
-            const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
+        for (int r0 = 0; r0 < rows; r0 += arows) {
+            const int nr = std::min(arows, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
             for (int k = 0; k < ns && k * slen <= t_last; ++k)
                 blocks.push_back(AttnBlock{0, g, r0, nr, k * slen, std::min(keys, (k + 1) * slen), k, ns, 0, 0, 1, P0});
         }
@@ -783,6 +794,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
             a.part_o = part_o;
             a.part_ml = part_ml;
             a.n_tokens = n;
+            a.wide = wide;
             m->tbegin(PCD_KC_PREFILL_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);
@@ -834,12 +846,17 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
     const int grp = c.n_heads / c.n_kv_heads, hd = c.head_dim;
     std::vector<int32_t> t0(n_seqs + 1, 0);
     int max_len = 0;
-    int64_t row_blocks = 0;
+    int64_t wide_blocks = 0;
     for (int r = 0; r < n_seqs; ++r) {
         t0[r + 1] = t0[r] + lens[r];
         max_len = std::max(max_len, lens[r]);
-        row_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + ATT_ROWS - 1) / ATT_ROWS);
+        wide_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + ATT_WIDE_ROWS - 1) / ATT_WIDE_ROWS);
     }
+    const bool wide = c.dtype == PCD_DTYPE_BF16 && wide_blocks >= ATT_WIDE_MIN_BLOCKS;
+    const int arows = wide ? ATT_WIDE_ROWS : ATT_ROWS;
+    int64_t row_blocks = 0;
+    for (int r = 0; r < n_seqs; ++r)
+        row_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + arows - 1) / arows);
     const int n = t0[n_seqs];
     int ns = att_splits(row_blocks, (max_len + 63) / 64, false);
     const int slen = ((max_len + ns - 1) / ns + 63) / 64 * 64;
@@ -847,8 +864,8 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
     std::vector<AttnBlock> blocks;
     for (int r = 0; r < n_seqs; ++r)
         for (int g = 0; g < c.n_kv_heads; ++g)
-            for (int r0 = t0[r] * grp; r0 < t0[r + 1] * grp; r0 += ATT_ROWS) {
-                const int nr = std::min(ATT_ROWS, t0[r + 1] * grp - r0);
+            for (int r0 = t0[r] * grp; r0 < t0[r + 1] * grp; r0 += arows) {
+                const int nr = std::min(arows, t0[r + 1] * grp - r0);
                 const int p_last = (r0 + nr - 1) / grp - t0[r];  // position of the block's last token
                 for (int k = 0; k < ns && k * slen <= p_last; ++k)
                     blocks.push_back(AttnBlock{r, g, r0, nr, k * slen, std::min(lens[r], (k + 1) * slen), k, ns, 0, 0,
@@ -906,6 +923,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
             a.part_o = part_o;
             a.part_ml = part_ml;
             a.n_tokens = n;
+            a.wide = wide;
             m->tbegin(PCD_KC_PREFILL_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);
@@ -1171,15 +1189,29 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     // merged by a second kernel).  New tokens: causal over the extended
     // prefix.  Branch tokens: the prefix of their request, split; the last
     // split also covers the branch keys of the fields its rows belong to.
+    //
+    // With enough new tokens (bf16) their causal rows take 128-row blocks
+    // (as a prefill pass does) in a launch of their own after the branch
+    // blocks' launch; the branch rows then split their keys as in a pass of
+    // branch rows only.
     std::vector<int32_t> tok_splits(M, 1);
     std::vector<uint64_t> req_kv(n_req);
     std::vector<AttnBlock> blocks;
     bool any_split = false;
-    int64_t row_blocks = (int64_t)c.n_kv_heads * (((int64_t)n_new * grp + ATT_ROWS - 1) / ATT_ROWS);
+    const int64_t new_wide_blocks = (int64_t)c.n_kv_heads * (((int64_t)n_new * grp + ATT_WIDE_ROWS - 1) / ATT_WIDE_ROWS);
+    const bool wide_new = n_new > 0 && c.dtype == PCD_DTYPE_BF16 && new_wide_blocks >= ATT_WIDE_MIN_BLOCKS;
+    int64_t branch_row_blocks = 0;
     for (int r = 0; r < n_req; ++r)
-        row_blocks += (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
+        branch_row_blocks +=
+            (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
+    const int64_t row_blocks =
+        wide_new ? 0 : branch_row_blocks + (int64_t)c.n_kv_heads * (((int64_t)n_new * grp + ATT_ROWS - 1) / ATT_ROWS);
     auto split_keys = [&](int keys, bool causal, int &s, int &slen) {
-        s = att_splits(row_blocks, (keys + 63) / 64, !causal && n_new == 0);
+        if (wide_new)  // two launches: each group of blocks on its own
+            s = causal ? att_splits(new_wide_blocks, (keys + 63) / 64, false)
+                       : att_splits(branch_row_blocks, (keys + 63) / 64, true);
+        else
+            s = att_splits(row_blocks, (keys + 63) / 64, !causal && n_new == 0);
         if (keys == 0) {
             s = 1;
             slen = 0;
@@ -1215,10 +1247,10 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
         split_keys(P0 + n_new, true, s, slen);
         any_split |= s > 1;
         for (int t = 0; t < n_new; ++t) tok_splits[t] = (P0 + t) / slen + 1;
-        const int rows = n_new * grp;
+        const int rows = n_new * grp, arows = wide_new ? ATT_WIDE_ROWS : ATT_ROWS;
         for (int g = 0; g < c.n_kv_heads; ++g)
-            for (int r0 = 0; r0 < rows; r0 += ATT_ROWS) {
-                const int nr = std::min(ATT_ROWS, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
+            for (int r0 = 0; r0 < rows; r0 += arows) {
+                const int nr = std::min(arows, rows - r0), t_last = P0 + (r0 + nr - 1) / grp;
                 for (int k = 0; k < s && k * slen <= t_last; ++k)
                     blocks.push_back(
                         AttnBlock{0, g, r0, nr, k * slen, std::min(P0 + n_new, (k + 1) * slen), k, s, 0, 0, 1, P0});
@@ -1339,7 +1371,18 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
             a.par = d_par;
             a.chain = d_chain;
             m->tbegin(last ? PCD_KC_OTHER : n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_ATTN, st);
-            const bool ok = attention(a, st);
+            bool ok;
+            if (wide_new && !last) {
+                a.n_blocks = n_branch_blocks;
+                ok = attention(a, st);
+                AttnCall b = a;  // the new tokens' 128-row causal blocks
+                b.blocks = d_blk + n_branch_blocks;
+                b.n_blocks = (int)blocks.size() - n_branch_blocks;
+                b.wide = 1;
+                ok = ok && attention(b, st);
+            } else {
+                ok = attention(a, st);
+            }
             m->tend(st);
             if (!ok) return fail(PCD_E_ARG, "attention: unsupported head_dim/dtype");
             if (any_split) {

@@ -106,6 +106,7 @@ struct AttnCall {
     int32_t cap;
     const int32_t *fs, *nsc, *par;  // per branch token: field start, scaffold length, trie parent
     const int4 *chain;              // per branch token: 8 links of its trie chain (itself, parent, ...; -1 past the root)
+    int32_t wide;  // nonzero: blocks of up to 128 query rows, causal prefix keys only (bf16); else up to 64 rows
 };
 bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
 

@@ -1560,8 +1560,10 @@ constexpr float RESCALE_LOG2 = 8.0f;
 template <int HD> struct RingLds {
     static constexpr int KT = 64, RB = HD * 2, CPR = RB / 16, TILE = KT * RB;
     static constexpr int Q_BYTES = TILE;  // 64 query rows
-    // H key rings (one per half of the workgroup) behind the query rows
-    static int bytes(int S, int H = 1) { return Q_BYTES + H * S * 2 * TILE; }
+    // H key rings (one per half of the workgroup) behind the query rows.
+    // RW = 2 (128 query rows): the rows wait in the ring's second slot,
+    // which they fill exactly, until every wave holds its own in registers.
+    static int bytes(int S, int H = 1, int RW = 1) { return (RW == 2 ? 0 : Q_BYTES) + H * S * 2 * TILE; }
 };
 
 // H = 2: a workgroup of 8 waves, whose halves (waves 0-3 and 4-7) walk the
@@ -1571,7 +1573,14 @@ template <int HD> struct RingLds {
 // Each key chain is half as long, two waves share each SIMD, and no merge
 // kernel runs.  Used for launches of at most 256 blocks, where each block
 // has a compute unit to itself anyway (the two rings fill 144 KB of LDS).
-template <int HD, int S, int H = 1>
+//
+// RW = 2: 128 query rows, two 16-row groups per wave (rows 32 w .. 32 w +
+// 31).  Every K and V fragment a wave reads from LDS feeds both groups'
+// matrix instructions, which halves the LDS bytes per flop: with one group
+// per wave, the K and V reads of a tile take twice the LDS cycles of its
+// matrix work.  Causal prefix blocks only (no branch keys); the 64 KB ring
+// keeps two blocks on a compute unit.
+template <int HD, int S, int H = 1, int RW = 1>
 __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
     using T = bf16_t;
     using L = RingLds<HD>;
@@ -1582,14 +1591,16 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
     static_assert(INS >= 1 && INS * 4 * 1024 == TILE, "tile / DMA mapping");
     static_assert(S >= 2 && (S - 1) * LPS + INS < 64, "vmcnt range");
     static_assert(H == 1 || (H == 2 && S == 2), "two halves with two-stage rings");
+    static_assert(RW == 1 || (RW == 2 && H == 1 && S == 2), "128-row blocks: one 4-wave ring of two stages");
     extern __shared__ __attribute__((aligned(16))) char attn_lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)attn_lds;
-    const char *Qs = attn_lds;
+    constexpr int Q_OFF = RW == 2 ? STAGE : 0;  // the query rows: ring slot 1 (RW = 2) or ahead of the ring
+    const char *Qs = attn_lds + Q_OFF;
 
     const AttnBlock blk = c.blocks[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int half = (tid >> 6) / 4, w = (tid >> 6) % 4;  // w: the block's 16-row query group of this wave
-    const uint32_t ring_off = (uint32_t)(L::Q_BYTES + half * S * STAGE);  // this half's key ring
+    const int half = (tid >> 6) / 4, w = (tid >> 6) % 4;  // w: this wave's query rows 16 RW w .. 16 RW (w + 1) - 1
+    const uint32_t ring_off = (uint32_t)((RW == 2 ? 0 : L::Q_BYTES) + half * S * STAGE);  // this half's key ring
     const uint32_t ring_base = lds_base + ring_off;
     const int Hq = c.n_heads, Hkv = c.n_kv_heads, grp = Hq / Hkv;
     const int P = c.req_stride[blk.req];  // slab stride (the buffer's token capacity)
@@ -1600,11 +1611,16 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
     const char *Vb = reinterpret_cast<const char *>(c.vb) + (size_t)blk.g * c.cap * RB;
     const float qscale = LOG2E / sqrtf((float)HD);
 
-    // this lane's query row (B operand of S^T) and its token
-    const bool row_ok = (w * 16 + lr) < blk.nrows;
-    const int rr = row_ok ? blk.row0 + w * 16 + lr : blk.row0;
-    const int tq = rr / grp;
-    const int kend_row = blk.causal ? min(blk.qoff + tq + 1, blk.key1) : blk.key1;
+    // this lane's query rows (B operand of S^T), one per 16-row group, and their tokens
+    bool row_ok[RW];
+    int tq[RW], kend_row[RW];
+#pragma unroll
+    for (int rb = 0; rb < RW; ++rb) {
+        const int lrow = (w * RW + rb) * 16 + lr;
+        row_ok[rb] = lrow < blk.nrows;
+        tq[rb] = (row_ok[rb] ? blk.row0 + lrow : blk.row0) / grp;
+        kend_row[rb] = blk.causal ? min(blk.qoff + tq[rb] + 1, blk.key1) : blk.key1;
+    }
     // keys below kend_lo are visible to every row of the block (its first row's bound)
     const int kend_lo = blk.causal ? min(blk.qoff + blk.row0 / grp + 1, blk.key1) : blk.key1;
     int kmax = blk.key1;
@@ -1613,7 +1629,8 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
         kmax = last < kmax ? last : kmax;
     }
     const int n_pre = kmax > blk.key0 ? (kmax - blk.key0 + KT - 1) / KT : 0;
-    const int n_sfx = blk.sfx_hi > blk.sfx_lo ? (blk.sfx_hi - blk.sfx_lo + KT - 1) / KT : 0;
+    // branch keys: 64-row blocks only (the host never gives them to 128-row blocks)
+    const int n_sfx = (RW == 1 && blk.sfx_hi > blk.sfx_lo) ? (blk.sfx_hi - blk.sfx_lo + KT - 1) / KT : 0;
     const int n_tiles = n_pre + n_sfx;
     // this half's tiles: global indices [t_base, t_base + t_cnt); both halves
     // run n_iter loop steps, so they meet every barrier the same number of times
@@ -1621,7 +1638,7 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
     const int t_base = half * n_iter, t_cnt = half == 0 ? n_iter : n_tiles - n_iter;
     RowVis vis{};
     if (n_sfx > 0) {
-        row_vis_init(vis, c, tq - c.branch0);
+        row_vis_init(vis, c, tq[0] - c.branch0);
         vm_wait<0>();  // its loads must not sit in the counter behind the DMA below
     }
 
@@ -1636,15 +1653,19 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
         dcv[i] = pc ^ ((2 * drow[i]) & (CPR - 1));
     }
     // query rows: (token, head) pairs of this block; rows past nrows re-read row0
-    // (loaded by the first half; the second reads them after the first barrier)
+    // (loaded by the first half; the second reads them after the first barrier).
+    // Rows 64 h2 .. 64 h2 + 63 take the layout of one key tile, TILE bytes on.
     if (half == 0) {
         const char *Q = reinterpret_cast<const char *>(c.q);
 #pragma unroll
-        for (int i = 0; i < INS; ++i) {
-            const int qr = drow[i] < blk.nrows ? blk.row0 + drow[i] : blk.row0;
-            const size_t qrow = (size_t)(qr / grp) * Hq + blk.g * grp + qr % grp;
-            dma16(Q + qrow * RB + dck[i] * 16, lds_base + (uint32_t)((i * 4 + w) * 1024));
-        }
+        for (int h2 = 0; h2 < RW; ++h2)
+#pragma unroll
+            for (int i = 0; i < INS; ++i) {
+                const int qi = h2 * 64 + drow[i];
+                const int qr = qi < blk.nrows ? blk.row0 + qi : blk.row0;
+                const size_t qrow = (size_t)(qr / grp) * Hq + blk.g * grp + qr % grp;
+                dma16(Q + qrow * RB + dck[i] * 16, lds_base + (uint32_t)(Q_OFF + h2 * TILE + (i * 4 + w) * 1024));
+            }
     }
     auto issue = [&](int i, int it) {  // tile i into ring slot it % S
         const bool sfx = i >= n_pre;
@@ -1663,11 +1684,17 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
     for (int s = 0; s + 1 < S; ++s)
         if (s < t_cnt) issue(t_base + s, s);
 
-    float m_run = -INFINITY, l_run = 0.f;  // reference max of query row lr (replicated over lg); this lane's share of the sum
-    f32x4 o[CF];
+    // per 16-row group rb: reference max of query row lr (replicated over lg); this lane's share of the sum
+    float m_run[RW], l_run[RW];
+    f32x4 o[RW][CF];
+    Frag<T> qf[RW][HS];
 #pragma unroll
-    for (int j = 0; j < CF; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Frag<T> qf[HS];
+    for (int rb = 0; rb < RW; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+#pragma unroll
+        for (int j = 0; j < CF; ++j) o[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     auto frag16 = [&](const char *tile, int row, int lc) {  // 16 bytes: logical chunk lc of a K or Q row
         Frag<T> f;
         f.v = *reinterpret_cast<const bf16x8_t *>(tile + row * RB + ((lc ^ (row & (CPR - 1))) * 16));
@@ -1681,8 +1708,8 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
         const char *Kt = attn_lds + ring_off + (it % S) * STAGE, *Vt = Kt + TILE;
         const int k0 = SFX ? blk.sfx_lo + (i - n_pre) * KT : blk.key0 + i * KT;
 
-        // S^T tile: sc[kf][r] = score(query lr, key k0 + kf*16 + 4*lg + r)
-        f32x4 sc[KT / 16];
+        // S^T tile: sc[rb][kf][r] = score(query 16 rb + lr, key k0 + kf*16 + 4*lg + r)
+        f32x4 sc[RW][KT / 16];
         {
             Frag<T> kfr[KT / 16][HS];
 #pragma unroll
@@ -1691,58 +1718,65 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
                 for (int st = 0; st < HS; ++st) kfr[kf][st] = frag16(Kt, kf * 16 + lr, st * 4 + lg);
             __builtin_amdgcn_sched_barrier(0);  // every read ahead of the multiplies
 #pragma unroll
-            for (int kf = 0; kf < KT / 16; ++kf) sc[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rb = 0; rb < RW; ++rb)
+#pragma unroll
+                for (int kf = 0; kf < KT / 16; ++kf) sc[rb][kf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < HS; ++st)
 #pragma unroll
-                for (int kf = 0; kf < KT / 16; ++kf) mma(sc[kf], kfr[kf][st], qf[st]);
+                for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+                    for (int rb = 0; rb < RW; ++rb) mma(sc[rb][kf], kfr[kf][st], qf[rb][st]);
         }
-        // Row maximum of the raw scores (masked keys set to -inf), then scaled:
-        // the scale is positive, so this equals the maximum of the scaled
-        // scores.  A prefix tile below every row's causal bound needs no mask.
-        float mx = -INFINITY;
-        if (!SFX && k0 + KT <= kend_lo) {
+        float pr[RW][KT / 16][4];
 #pragma unroll
-            for (int kf = 0; kf < KT / 16; ++kf)
+        for (int rb = 0; rb < RW; ++rb) {
+            // Row maximum of the raw scores (masked keys set to -inf), then scaled:
+            // the scale is positive, so this equals the maximum of the scaled
+            // scores.  A prefix tile below every row's causal bound needs no mask.
+            float mx = -INFINITY;
+            if (!SFX && k0 + KT <= kend_lo) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kf][r]);
-        } else {
+                for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[rb][kf][r]);
+            } else {
+#pragma unroll
+                for (int kf = 0; kf < KT / 16; ++kf)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = k0 + kf * 16 + lg * 4 + r;
+                        bool see;
+                        if constexpr (SFX) see = row_ok[rb] && key < blk.sfx_hi && row_vis_sees(vis, c, key);
+                        else see = key < kend_row[rb];
+                        const float v = see ? sc[rb][kf][r] : -INFINITY;
+                        sc[rb][kf][r] = v;
+                        mx = fmaxf(mx, v);
+                    }
+            }
+            mx = rows_max(mx) * qscale;
+            if (__any(mx > m_run[rb] + RESCALE_LOG2)) {
+                const float m_new = fmaxf(m_run[rb], mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - (m_new == -INFINITY ? 0.f : m_new));
+                l_run[rb] *= alpha;
+                m_run[rb] = m_new;
+                // o holds this lane's own query row lr (columns 16 j + 4 lg + r)
+#pragma unroll
+                for (int j = 0; j < CF; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[rb][j][r] *= alpha;
+            }
+            const float m_neg = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+            float psum = 0.f;
 #pragma unroll
             for (int kf = 0; kf < KT / 16; ++kf)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int key = k0 + kf * 16 + lg * 4 + r;
-                    bool see;
-                    if constexpr (SFX) see = row_ok && key < blk.sfx_hi && row_vis_sees(vis, c, key);
-                    else see = key < kend_row;
-                    const float v = see ? sc[kf][r] : -INFINITY;
-                    sc[kf][r] = v;
-                    mx = fmaxf(mx, v);
+                    pr[rb][kf][r] = __builtin_amdgcn_exp2f(fmaf(sc[rb][kf][r], qscale, m_neg));
+                    psum += pr[rb][kf][r];
                 }
+            l_run[rb] += psum;
         }
-        mx = rows_max(mx) * qscale;
-        if (__any(mx > m_run + RESCALE_LOG2)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-            l_run *= alpha;
-            m_run = m_new;
-            // o holds this lane's own query row lr (columns 16 j + 4 lg + r)
-#pragma unroll
-            for (int j = 0; j < CF; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
-        }
-        const float m_neg = m_run == -INFINITY ? 0.f : -m_run;
-        float psum = 0.f;
-        float pr[KT / 16][4];
-#pragma unroll
-        for (int kf = 0; kf < KT / 16; ++kf)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[kf][r] = __builtin_amdgcn_exp2f(fmaf(sc[kf][r], qscale, m_neg));
-                psum += pr[kf][r];
-            }
-        l_run += psum;
 
         // O += P V over two 32-key steps; A = P (row lr, keys {4lg..4lg+3} and
         // {16+4lg..16+4lg+3}), B = V with the same key order: lane (lr, lg)
@@ -1761,18 +1795,20 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
             }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int st = 0; st < KT / 32; ++st) {
-            float pv[8];
+        for (int st = 0; st < KT / 32; ++st)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pv[r] = pr[2 * st][r];
-                pv[4 + r] = pr[2 * st + 1][r];
+            for (int rb = 0; rb < RW; ++rb) {
+                float pv[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pv[r] = pr[rb][2 * st][r];
+                    pv[4 + r] = pr[rb][2 * st + 1][r];
+                }
+                Frag<T> pa;
+                from8(pa, pv);
+#pragma unroll
+                for (int j = 0; j < CF; ++j) mma(o[rb][j], vfr[st][j], pa);  // V first: o[j] is O^T's layout
             }
-            Frag<T> pa;
-            from8(pa, pv);
-#pragma unroll
-            for (int j = 0; j < CF; ++j) mma(o[j], vfr[st][j], pa);  // V first: o[j] is O^T's layout
-        }
     };
 
     for (int it = 0; it < n_iter; ++it) {
@@ -1781,14 +1817,21 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
         barrier_keep_loads();
         if (it == 0) {
 #pragma unroll
-            for (int st = 0; st < HS; ++st) qf[st] = frag16(Qs, w * 16 + lr, st * 4 + lg);
+            for (int rb = 0; rb < RW; ++rb)
+#pragma unroll
+                for (int st = 0; st < HS; ++st) qf[rb][st] = frag16(Qs, (w * RW + rb) * 16 + lr, st * 4 + lg);
+            if constexpr (RW == 2) {
+                // the query rows sit in slot 1, which the next issue refills
+                lds_reads_done();
+                barrier_keep_loads();
+            }
         }
         // slot (it - 1) % S was read by every wave of this half before the barrier
         if (it + S - 1 < t_cnt) issue(t_base + it + S - 1, it + S - 1);
         if (it < t_cnt) {
             const int i = t_base + it;
             if (i < n_pre) tile(std::false_type{}, i, it);
-            else tile(std::true_type{}, i, it);
+            else if constexpr (RW == 1) tile(std::true_type{}, i, it);
         }
         lds_reads_done();
     }
@@ -1804,36 +1847,39 @@ __global__ __launch_bounds__(256 * H) void k_attn_ring(AttnCall c) {
 #pragma unroll
             for (int j = 0; j < CF; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) xs[(j * 4 + r) * 64] = o[j][r];
-            xs[4 * CF * 64] = m_run;
-            xs[(4 * CF + 1) * 64] = l_run;
+                for (int r = 0; r < 4; ++r) xs[(j * 4 + r) * 64] = o[0][j][r];
+            xs[4 * CF * 64] = m_run[0];
+            xs[(4 * CF + 1) * 64] = l_run[0];
         }
         __syncthreads();
         if (half == 1) return;
         // merge: the common reference is the larger maximum (log2 units)
         const float m1 = xs[4 * CF * 64], l1 = xs[(4 * CF + 1) * 64];
-        const float mm = fmaxf(m_run, m1);
-        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+        const float mm = fmaxf(m_run[0], m1);
+        const float a0 = m_run[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - mm);
         const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-        l_run = l_run * a0 + l1 * a1;
-        m_run = mm;
+        l_run[0] = l_run[0] * a0 + l1 * a1;
+        m_run[0] = mm;
 #pragma unroll
         for (int j = 0; j < CF; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[j][r] = o[j][r] * a0 + xs[(j * 4 + r) * 64] * a1;
+            for (int r = 0; r < 4; ++r) o[0][j][r] = o[0][j][r] * a0 + xs[(j * 4 + r) * 64] * a1;
     }
-    attn_write_rows<T, HD>(c, blk, o, m_run, rows_sum(l_run), w, lr, lg);
+#pragma unroll
+    for (int rb = 0; rb < RW; ++rb)
+        attn_write_rows<T, HD>(c, blk, o[rb], m_run[rb], rows_sum(l_run[rb]), w * RW + rb, lr, lg);
 }
 
-template <int HD, int S, int H> static void launch_attn_ring_h(const AttnCall &c, hipStream_t st) {
-    const int shmem = RingLds<HD>::bytes(S, H);
+
+template <int HD, int S, int H, int RW = 1> static void launch_attn_ring_h(const AttnCall &c, hipStream_t st) {
+    const int shmem = RingLds<HD>::bytes(S, H, RW);
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_attn_ring<HD, S, H>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_attn_ring<HD, S, H, RW>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_attn_ring<HD, S, H>), dim3(c.n_blocks), dim3(256 * H), shmem, st, c);
+    hipLaunchKernelGGL((k_attn_ring<HD, S, H, RW>), dim3(c.n_blocks), dim3(256 * H), shmem, st, c);
 }
 // Launches of at most one block per compute unit split each block's key
 // chain over two halves of one workgroup; larger ones keep 4-wave blocks,
@@ -1841,6 +1887,10 @@ template <int HD, int S, int H> static void launch_attn_ring_h(const AttnCall &c
 constexpr int ATT_HALVES_MAX_BLOCKS = 256;
 template <int HD, int S> static void launch_attn_ring(const AttnCall &c, hipStream_t st) {
     if constexpr (S == 2) {
+        if (c.wide) {
+            launch_attn_ring_h<HD, S, 1, 2>(c, st);
+            return;
+        }
         if (c.n_blocks <= ATT_HALVES_MAX_BLOCKS) {
             launch_attn_ring_h<HD, S, 2>(c, st);
             return;
@@ -1867,6 +1917,7 @@ template <typename T, int HD> static void launch_attn(const AttnCall &c, hipStre
 
 template <typename T> static bool attention_t(const AttnCall &c, hipStream_t st) {
     if (c.n_blocks <= 0) return true;
+    if (c.wide && (sizeof(T) != 2 || ATT_RING_STAGES != 2)) return false;  // 128-row blocks: the two-stage bf16 ring only
     if constexpr (sizeof(T) == 2) {
         switch (c.hd) {
             case 32: launch_attn_ring<32, ATT_RING_STAGES>(c, st); return true;

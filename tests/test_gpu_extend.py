@@ -293,6 +293,44 @@ def test_bf16_two_layer_fused_cold(q15_l2):
         m.close()
 
 
+@pytest.mark.parametrize("hd", [32, 64])
+def test_bf16_wide_fused_request(hd):
+    """Single-pass requests whose new tokens fill at least 512 attention
+    blocks of 128 rows: those causal rows run in a launch of their own,
+    after the branch rows' launch, whose keys are then split as in a pass
+    of branch rows only.  Head dim 32: an empty state and a 2,100-token
+    prompt; head dim 64: a 300-token head, forked, and 4,100 new tokens
+    (causal rows from position 300 on); then a decide on the state the pass
+    left."""
+    from test_gpu_parity import _wide_bf16_shape
+    sh = _wide_bf16_shape(hd)
+    w = pi.make_weights(sh, 1006)
+    dec = odec.Decoder(w, np.float64)
+    rng = np.random.default_rng(90 + hd)
+    V = sh.vocab_size
+    fields = pi.random_trie_fields(4400 + hd, V, 3, max_cands=6, max_len=3)
+    head = _tokens(rng, V, {32: 0, 64: 300}[hd])
+    inp = _tokens(rng, V, {32: 2100, 64: 4100}[hd])
+    grp = sh.n_heads // sh.n_kv_heads
+    assert sh.n_kv_heads * -(-len(inp) * grp // 128) >= 512
+    m = _fused_model(sh, w, len(head) + len(inp), fields)
+    if head:
+        hs = m.prefill(head)
+        st = hs.fork(capacity=len(head) + len(inp))
+    else:
+        hs, st = None, m.new_state(len(inp))
+    got = [m.extend_decide(st, inp, fields, debug=True)]
+    ref = opcd.decide(dec, [(head + inp, fields)])
+    _compare(f"bf16-wide-fused-hd{hd}", got, ref, ref.plan, "bf16")
+    # the state's KV, written by the pass, serves a later decide as prefill's would
+    again = [m.decide(st, fields, debug=True)]
+    _compare(f"bf16-wide-fused-hd{hd}-then-decide", again, ref, ref.plan, "bf16")
+    if hs is not None:
+        hs.close()
+    st.close()
+    m.close()
+
+
 def test_tiny_started_calls_match_extend_decide(tiny_w):
     """extend_decide_start + finish returns what extend_decide does, bit for
     bit, with MAX_PENDING calls in flight on as many states and finished in

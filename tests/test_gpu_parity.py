@@ -362,6 +362,47 @@ def test_bf16_small_head_dims(hd):
               dec=dec)
 
 
+def _wide_bf16_shape(hd):
+    """The tiny widths in bf16 with many heads in pairs (32 query / 16 KV
+    heads of 32, or 16 / 8 of 64): causal prefill launches reach 512 row
+    blocks of 128 rows at a few thousand tokens."""
+    heads = {32: (32, 16), 64: (16, 8)}[hd]
+    return dataclasses.replace(pi.SHAPES["tiny"], name=f"tiny-bf16-wide-hd{hd}", dtype="bf16", head_dim=hd,
+                               n_heads=heads[0], n_kv_heads=heads[1], max_seq=4608)
+
+
+@pytest.mark.parametrize("hd", [32, 64])
+def test_bf16_wide_prefill_attention_blocks(hd):
+    """Causal prefill whose launch has at least 512 blocks of 128 query rows:
+    those blocks give each wave two 16-row groups, the query rows wait in
+    the key ring's second slot, and the last block of each KV head is
+    ragged.  One long prompt (pcd_prefill), then two prompts in one
+    pcd_prefill_many pass, each decided against the oracle."""
+    sh = _wide_bf16_shape(hd)
+    grp, hkv = sh.n_heads // sh.n_kv_heads, sh.n_kv_heads
+    w = pi.make_weights(sh, 1005)
+    dec = odec.Decoder(w, np.float64)
+    V = sh.vocab_size
+    rng = np.random.default_rng(70 + hd)
+    P = {32: 2100, 64: 4100}[hd]
+    assert hkv * -(-P * grp // 128) >= 512 and (P * grp) % 128 != 0
+    prefix = [int(t) for t in rng.integers(0, V, size=P)]
+    _run_case(f"bf16-wide-hd{hd}-one", sh, w, [(prefix, pi.random_trie_fields(4200, V, 3, max_cands=6, max_len=3))],
+              dec=dec)
+    lens = {32: (1100, 1061), 64: (2050, 2029)}[hd]
+    assert hkv * sum(-(-n * grp // 128) for n in lens) >= 512
+    reqs = [([int(t) for t in rng.integers(0, V, size=n)], pi.random_trie_fields(4300 + k, V, 2, max_cands=5, max_len=2))
+            for k, n in enumerate(lens)]
+    m = _model(sh, w, reqs, max_prefill=sum(lens))
+    states = m.prefill_many([p for p, _ in reqs])
+    got = m.decide_many(states, [f for _, f in reqs], debug=True)
+    ref = opcd.decide(dec, reqs)
+    _compare(f"bf16-wide-hd{hd}-many", got, ref, ref.plan, "bf16")
+    for st in states:
+        st.close()
+    m.close()
+
+
 # ---------------------------------------------------------------------------
 # Qwen2.5-1.5B widths in bf16
 # ---------------------------------------------------------------------------
