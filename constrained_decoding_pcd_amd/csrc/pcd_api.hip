@@ -96,6 +96,95 @@ static int att_splits(int64_t row_blocks, int key_tiles, bool equal_chains) {
     return (int)std::max<int64_t>(1, std::min<int64_t>({std::max(want, want_long), (int64_t)MAX_SPLITS, (int64_t)by_len}));
 }
 
+// Causal launches with few blocks per compute unit: a block's keys end at
+// its last row, so the longest chains set the launch time (the 2,048-token
+// prompt at the 1.5B widths: 384 blocks of 1 to 32 key tiles in 42.7 us,
+// about the longest chain's time).  Where the longest chain reaches
+// ATT_CHAIN_MODEL_TILES and outlasts the launch's work spread over its
+// slots, the split count is the one of least estimated time: the larger of
+// the longest chain and the total work over the slots (two per compute
+// unit, or one per compute unit with chains walked as two halves when the
+// launch has at most ATT_HALVES_BLOCKS workgroups), each workgroup costing
+// ATT_BLOCK_FIXED plus its key tiles.  Split keys add the merge kernel:
+// ATT_MERGE_FIXED plus its fp32 partials (each token's splits x query heads
+// x head_dim x 4 bytes) at ATT_MERGE_MB_PER_TILE.  Times are in key tiles
+// (about 1.2 us per 64-key tile of a 64-row block).
+constexpr int ATT_CHAIN_MODEL_TILES = 16;
+constexpr int ATT_HALVES_BLOCKS = 256;  // the kernel's two-chain form (launches of at most this many)
+constexpr double ATT_BLOCK_FIXED = 2.4;  // entry to first DMA, output write: about 2.8 us
+constexpr double ATT_MERGE_FIXED = 1.7;  // the merge kernel's launch and ramp: about 2 us
+constexpr double ATT_MERGE_MB_PER_TILE = 3.6;  // partials it reads per key-tile time (about 3 TB/s)
+struct ChainSpec {
+    int kend;   // keys the block reaches (its last row's causal bound, or the whole prefix)
+    int extra;  // key tiles its last split adds (branch keys)
+};
+struct TokRange {
+    int kend0, count;  // count row tokens reaching kend0, kend0 + 1, ... (step) or all kend0
+    bool step;
+};
+struct SplitCost {
+    double chain, work;  // longest workgroup and total work over the slots, in key tiles
+};
+static SplitCost split_cost(const std::vector<ChainSpec> &blocks, int slen, int ns) {
+    int64_t n = 0, sum = 0, sum_half = 0;
+    int longest = 0;
+    for (const ChainSpec &b : blocks)
+        for (int k = 0; k < ns && k * slen < b.kend; ++k) {
+            const bool last = k == ns - 1 || (k + 1) * slen >= b.kend;
+            const int t = (std::min(b.kend, (k + 1) * slen) - k * slen + 63) / 64 + (last ? b.extra : 0);
+            ++n;
+            sum += t;
+            sum_half += (t + 1) / 2;
+            longest = std::max(longest, t);
+        }
+    if (n <= ATT_HALVES_BLOCKS)
+        return {ATT_BLOCK_FIXED + (longest + 1) / 2, (sum_half + ATT_BLOCK_FIXED * n) / ATT_HALVES_BLOCKS};
+    return {ATT_BLOCK_FIXED + longest, (sum + ATT_BLOCK_FIXED * n) / ATT_SLOTS};
+}
+static double merge_cost(const std::vector<TokRange> &toks, int slen, int ns, double tok_bytes) {
+    double mb = 0;  // partial bytes of the tokens with more than one split
+    for (const TokRange &r : toks) {
+        if (!r.step) {
+            const int t = std::min(ns, (r.kend0 + slen - 1) / slen);
+            if (t > 1) mb += (double)t * r.count * tok_bytes;
+            continue;
+        }
+        const int lo = r.kend0, hi = r.kend0 + r.count - 1;
+        for (int j = 2; j <= ns; ++j) {  // tokens with j splits reach keys in ((j-1) slen, j slen]
+            const int a = std::max(lo, (j - 1) * slen + 1), b = j == ns ? hi : std::min(hi, j * slen);
+            if (b >= a) mb += (double)j * (b - a + 1) * tok_bytes;
+        }
+    }
+    return ATT_MERGE_FIXED + mb / 1e6 / ATT_MERGE_MB_PER_TILE;
+}
+// The split count of least estimated time (a larger count must gain 3%), or
+// 0 when the longest chain is below ATT_CHAIN_MODEL_TILES.  toks: the row
+// tokens and the keys they reach; tok_bytes: one split's partials of one
+// token.
+static int model_splits(const std::vector<ChainSpec> &blocks, int keys, const std::vector<TokRange> &toks,
+                        double tok_bytes) {
+    int longest = 0;
+    for (const ChainSpec &b : blocks) longest = std::max(longest, (b.kend + 63) / 64 + b.extra);
+    if (longest < ATT_CHAIN_MODEL_TILES) return 0;
+    const SplitCost one = split_cost(blocks, keys, 1);
+    if (one.work >= one.chain) return 1;  // the slots are full: splitting only adds work
+    int best_s = 1;
+    double best = std::max(one.chain, one.work);
+    for (int s = 2; s <= MAX_SPLITS; ++s) {
+        const int slen = ((keys + s - 1) / s + 63) / 64 * 64;
+        if (slen / 64 < ATT_MIN_SPLIT_TILES) break;
+        const int ns = (keys + slen - 1) / slen;
+        if (ns != s) continue;  // the same split as a smaller count
+        const SplitCost c = split_cost(blocks, slen, ns);
+        const double t = std::max(c.chain, c.work) + merge_cost(toks, slen, ns, tok_bytes);
+        if (t < 0.97 * best) {
+            best = t;
+            best_s = s;
+        }
+    }
+    return best_s;
+}
+
 // Key tiles a block walks (prefix part up to its last row's causal bound,
 // plus its branch keys).
 static int block_tiles(const AttnBlock &b, int grp) {
@@ -733,6 +822,13 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     const int arows = wide ? ATT_WIDE_ROWS : ATT_ROWS;
     const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + arows - 1) / arows);
     int ns = att_splits(row_blocks, (keys + 63) / 64, false);
+    {
+        std::vector<ChainSpec> chains;
+        for (int g = 0; g < c.n_kv_heads; ++g)
+            for (int r0 = 0; r0 < rows; r0 += arows)
+                chains.push_back({P0 + (r0 + std::min(arows, rows - r0) - 1) / grp + 1, 0});
+        if (int ms = model_splits(chains, keys, {{P0 + 1, n, true}}, 4.0 * c.n_heads * hd)) ns = ms;
+    }
     const int slen = ((keys + ns - 1) / ns + 63) / 64 * 64;
     ns = (keys + slen - 1) / slen;
     for (int g = 0; g < c.n_kv_heads; ++g)
@@ -806,6 +902,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
                 t.n_heads = c.n_heads;
                 t.n_kv_heads = c.n_kv_heads;
                 t.n_tokens = n;
+                t.tok0 = std::max(0, std::min(n, slen - P0));  // earlier tokens have one split
                 t.part_o = part_o;
                 t.part_ml = part_ml;
                 t.tok_splits = d_tsp;
@@ -859,6 +956,17 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
         row_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + arows - 1) / arows);
     const int n = t0[n_seqs];
     int ns = att_splits(row_blocks, (max_len + 63) / 64, false);
+    {
+        std::vector<ChainSpec> chains;
+        std::vector<TokRange> toks;
+        for (int r = 0; r < n_seqs; ++r) {
+            toks.push_back({1, lens[r], true});
+            for (int g = 0; g < c.n_kv_heads; ++g)
+                for (int r0 = t0[r] * grp; r0 < t0[r + 1] * grp; r0 += arows)
+                    chains.push_back({(r0 + std::min(arows, t0[r + 1] * grp - r0) - 1) / grp - t0[r] + 1, 0});
+        }
+        if (int ms = model_splits(chains, max_len, toks, 4.0 * c.n_heads * hd)) ns = ms;
+    }
     const int slen = ((max_len + ns - 1) / ns + 63) / 64 * 64;
     ns = (max_len + slen - 1) / slen;
     std::vector<AttnBlock> blocks;
@@ -1206,12 +1314,36 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
             (int64_t)c.n_kv_heads * (((int64_t)(p.r_tok[r + 1] - p.r_tok[r]) * grp + ATT_ROWS - 1) / ATT_ROWS);
     const int64_t row_blocks =
         wide_new ? 0 : branch_row_blocks + (int64_t)c.n_kv_heads * (((int64_t)n_new * grp + ATT_ROWS - 1) / ATT_ROWS);
+    // A pass with new tokens serves one request, whose branch rows see the
+    // same extended prefix: where the longest chains bind, one split count
+    // for both groups of the launch (and for the causal launch of its own).
+    int model_s = 0;
+    if (n_new > 0) {
+        std::vector<ChainSpec> chains;
+        std::vector<TokRange> toks{{P0 + 1, n_new, true}};
+        const int keys = P0 + n_new;
+        const int rows = n_new * grp, arows = wide_new ? ATT_WIDE_ROWS : ATT_ROWS;
+        for (int g = 0; g < c.n_kv_heads; ++g)
+            for (int r0 = 0; r0 < rows; r0 += arows)
+                chains.push_back({P0 + (r0 + std::min(arows, rows - r0) - 1) / grp + 1, 0});
+        if (!wide_new) {  // the branch blocks share the launch; their tokens reach every key
+            toks.push_back({keys, p.r_tok[1], false});
+            const int row_beg = n_new * grp, row_end = (n_new + p.r_tok[1]) * grp;
+            for (int g = 0; g < c.n_kv_heads; ++g)
+                for (int r0 = row_beg; r0 < row_end; r0 += ATT_ROWS) {
+                    const int nr = std::min(ATT_ROWS, row_end - r0);
+                    const int b_first = r0 / grp - n_new, b_last = (r0 + nr - 1) / grp - n_new;
+                    chains.push_back({lens[0], (b_last + 1 - p.fs[b_first] + 63) / 64});
+                }
+        }
+        model_s = n_req == 1 && lens[0] == keys ? model_splits(chains, keys, toks, 4.0 * c.n_heads * hd) : 0;
+    }
     auto split_keys = [&](int keys, bool causal, int &s, int &slen) {
         if (wide_new)  // two launches: each group of blocks on its own
-            s = causal ? att_splits(new_wide_blocks, (keys + 63) / 64, false)
+            s = causal ? (model_s ? model_s : att_splits(new_wide_blocks, (keys + 63) / 64, false))
                        : att_splits(branch_row_blocks, (keys + 63) / 64, true);
         else
-            s = att_splits(row_blocks, (keys + 63) / 64, !causal && n_new == 0);
+            s = model_s ? model_s : att_splits(row_blocks, (keys + 63) / 64, !causal && n_new == 0);
         if (keys == 0) {
             s = 1;
             slen = 0;
@@ -1242,10 +1374,12 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     const int n_branch_blocks = (int)blocks.size();
     longest_first(blocks, 0, blocks.size(), grp);
     xcd_order(blocks, 0, blocks.size());
+    int merge_tok0 = n_new;  // the merge starts at the first token with more than one split
     if (n_new > 0) {
         int s, slen;
         split_keys(P0 + n_new, true, s, slen);
         any_split |= s > 1;
+        if (s > 1) merge_tok0 = std::max(0, std::min(n_new, slen - P0));
         for (int t = 0; t < n_new; ++t) tok_splits[t] = (P0 + t) / slen + 1;
         const int rows = n_new * grp, arows = wide_new ? ATT_WIDE_ROWS : ATT_ROWS;
         for (int g = 0; g < c.n_kv_heads; ++g)
@@ -1392,7 +1526,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
                 t.n_heads = c.n_heads;
                 t.n_kv_heads = c.n_kv_heads;
                 t.n_tokens = M;
-                t.tok0 = last ? n_new : 0;
+                t.tok0 = last ? n_new : merge_tok0;
                 t.part_o = part_o;
                 t.part_ml = part_ml;
                 t.tok_splits = d_tsp;
