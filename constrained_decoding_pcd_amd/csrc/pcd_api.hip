@@ -100,12 +100,12 @@ static int att_splits(int64_t row_blocks, int key_tiles, bool equal_chains) {
 // its last row, so the longest chains set the launch time (the 2,048-token
 // prompt at the 1.5B widths: 384 blocks of 1 to 32 key tiles in 42.7 us,
 // about the longest chain's time).  Where the longest chain reaches
-// ATT_CHAIN_MODEL_TILES and outlasts the launch's work spread over its
-// slots, the split count is the one of least estimated time: the larger of
-// the longest chain and the total work over the slots (two per compute
-// unit, or one per compute unit with chains walked as two halves when the
-// launch has at most ATT_HALVES_BLOCKS workgroups), each workgroup costing
-// ATT_BLOCK_FIXED plus its key tiles.  Split keys add the merge kernel:
+// ATT_CHAIN_MODEL_TILES, the split count and block form are the ones of
+// least estimated time: the larger of the longest chain and the total work
+// over the slots, each workgroup costing ATT_BLOCK_FIXED plus its key tiles.
+// 4-wave blocks take two slots per compute unit; 8-wave blocks walking two
+// key chains (the form launches of at most ATT_HALVES_BLOCKS take anyway)
+// one slot per compute unit, their chains halved.  Split keys add the merge kernel:
 // ATT_MERGE_FIXED plus its fp32 partials (each token's splits x query heads
 // x head_dim x 4 bytes) at ATT_MERGE_MB_PER_TILE.  Times are in key tiles
 // (about 1.2 us per 64-key tile of a 64-row block).
@@ -125,7 +125,7 @@ struct TokRange {
 struct SplitCost {
     double chain, work;  // longest workgroup and total work over the slots, in key tiles
 };
-static SplitCost split_cost(const std::vector<ChainSpec> &blocks, int slen, int ns) {
+static SplitCost split_cost(const std::vector<ChainSpec> &blocks, int slen, int ns, bool halves) {
     int64_t n = 0, sum = 0, sum_half = 0;
     int longest = 0;
     for (const ChainSpec &b : blocks)
@@ -137,7 +137,7 @@ static SplitCost split_cost(const std::vector<ChainSpec> &blocks, int slen, int 
             sum_half += (t + 1) / 2;
             longest = std::max(longest, t);
         }
-    if (n <= ATT_HALVES_BLOCKS)
+    if (halves || n <= ATT_HALVES_BLOCKS)
         return {ATT_BLOCK_FIXED + (longest + 1) / 2, (sum_half + ATT_BLOCK_FIXED * n) / ATT_HALVES_BLOCKS};
     return {ATT_BLOCK_FIXED + longest, (sum + ATT_BLOCK_FIXED * n) / ATT_SLOTS};
 }
@@ -157,32 +157,37 @@ static double merge_cost(const std::vector<TokRange> &toks, int slen, int ns, do
     }
     return ATT_MERGE_FIXED + mb / 1e6 / ATT_MERGE_MB_PER_TILE;
 }
-// The split count of least estimated time (a larger count must gain 3%), or
-// 0 when the longest chain is below ATT_CHAIN_MODEL_TILES.  toks: the row
-// tokens and the keys they reach; tok_bytes: one split's partials of one
-// token.
-static int model_splits(const std::vector<ChainSpec> &blocks, int keys, const std::vector<TokRange> &toks,
-                        double tok_bytes) {
+// The split count and block form of least estimated time (a larger count or
+// the two-chain form must gain 3%); s = 0 when the longest chain is below
+// ATT_CHAIN_MODEL_TILES.  toks: the row tokens and the keys they reach;
+// tok_bytes: one split's partials of one token; two_chains: the launch may
+// take the two-chain form (64-row blocks).
+struct SplitPlan {
+    int s;
+    bool halves;
+};
+static SplitPlan model_splits(const std::vector<ChainSpec> &blocks, int keys, const std::vector<TokRange> &toks,
+                              double tok_bytes, bool two_chains) {
     int longest = 0;
     for (const ChainSpec &b : blocks) longest = std::max(longest, (b.kend + 63) / 64 + b.extra);
-    if (longest < ATT_CHAIN_MODEL_TILES) return 0;
-    const SplitCost one = split_cost(blocks, keys, 1);
-    if (one.work >= one.chain) return 1;  // the slots are full: splitting only adds work
-    int best_s = 1;
-    double best = std::max(one.chain, one.work);
-    for (int s = 2; s <= MAX_SPLITS; ++s) {
-        const int slen = ((keys + s - 1) / s + 63) / 64 * 64;
-        if (slen / 64 < ATT_MIN_SPLIT_TILES) break;
-        const int ns = (keys + slen - 1) / slen;
-        if (ns != s) continue;  // the same split as a smaller count
-        const SplitCost c = split_cost(blocks, slen, ns);
-        const double t = std::max(c.chain, c.work) + merge_cost(toks, slen, ns, tok_bytes);
-        if (t < 0.97 * best) {
-            best = t;
-            best_s = s;
+    if (longest < ATT_CHAIN_MODEL_TILES) return {0, false};
+    SplitPlan best_p{1, false};
+    double best = 0;
+    for (int h = 0; h < (two_chains ? 2 : 1); ++h)
+        for (int s = 1; s <= MAX_SPLITS; ++s) {
+            const int slen = s == 1 ? keys : ((keys + s - 1) / s + 63) / 64 * 64;
+            if (s > 1 && slen / 64 < ATT_MIN_SPLIT_TILES) break;
+            const int ns = s == 1 ? 1 : (keys + slen - 1) / slen;
+            if (ns != s) continue;  // the same split as a smaller count
+            const SplitCost c = split_cost(blocks, slen, ns, h == 1);
+            const double t = std::max(c.chain, c.work) + (ns > 1 ? merge_cost(toks, slen, ns, tok_bytes) : 0.0);
+            if ((h == 0 && s == 1) || t < 0.97 * best) {
+                best = t;
+                best_p = {s, h == 1};
+            }
+            if (s == 1 && c.work >= c.chain) break;  // the slots are full: splitting only adds work
         }
-    }
-    return best_s;
+    return best_p;
 }
 
 // Key tiles a block walks (prefix part up to its last row's causal bound,
@@ -822,12 +827,15 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
     const int arows = wide ? ATT_WIDE_ROWS : ATT_ROWS;
     const int64_t row_blocks = (int64_t)c.n_kv_heads * ((rows + arows - 1) / arows);
     int ns = att_splits(row_blocks, (keys + 63) / 64, false);
+    bool halves = false;  // two key chains per 8-wave block whatever the block count
     {
         std::vector<ChainSpec> chains;
         for (int g = 0; g < c.n_kv_heads; ++g)
             for (int r0 = 0; r0 < rows; r0 += arows)
                 chains.push_back({P0 + (r0 + std::min(arows, rows - r0) - 1) / grp + 1, 0});
-        if (int ms = model_splits(chains, keys, {{P0 + 1, n, true}}, 4.0 * c.n_heads * hd)) ns = ms;
+        const SplitPlan sp = model_splits(chains, keys, {{P0 + 1, n, true}}, 4.0 * c.n_heads * hd, !wide);
+        if (sp.s) ns = sp.s;
+        halves = sp.halves;
     }
     const int slen = ((keys + ns - 1) / ns + 63) / 64 * 64;
     ns = (keys + slen - 1) / slen;
@@ -891,6 +899,7 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
             a.part_ml = part_ml;
             a.n_tokens = n;
             a.wide = wide;
+            a.halves = halves;
             m->tbegin(PCD_KC_PREFILL_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);
@@ -956,6 +965,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
         row_blocks += (int64_t)c.n_kv_heads * (((int64_t)lens[r] * grp + arows - 1) / arows);
     const int n = t0[n_seqs];
     int ns = att_splits(row_blocks, (max_len + 63) / 64, false);
+    bool halves = false;  // two key chains per 8-wave block whatever the block count
     {
         std::vector<ChainSpec> chains;
         std::vector<TokRange> toks;
@@ -965,7 +975,9 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
                 for (int r0 = t0[r] * grp; r0 < t0[r + 1] * grp; r0 += arows)
                     chains.push_back({(r0 + std::min(arows, t0[r + 1] * grp - r0) - 1) / grp - t0[r] + 1, 0});
         }
-        if (int ms = model_splits(chains, max_len, toks, 4.0 * c.n_heads * hd)) ns = ms;
+        const SplitPlan sp = model_splits(chains, max_len, toks, 4.0 * c.n_heads * hd, !wide);
+        if (sp.s) ns = sp.s;
+        halves = sp.halves;
     }
     const int slen = ((max_len + ns - 1) / ns + 63) / 64 * 64;
     ns = (max_len + slen - 1) / slen;
@@ -1032,6 +1044,7 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
             a.part_ml = part_ml;
             a.n_tokens = n;
             a.wide = wide;
+            a.halves = halves;
             m->tbegin(PCD_KC_PREFILL_ATTN, st);
             const bool ok = attention(a, st);
             m->tend(st);
@@ -1318,6 +1331,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
     // same extended prefix: where the longest chains bind, one split count
     // for both groups of the launch (and for the causal launch of its own).
     int model_s = 0;
+    bool halves = false;  // two key chains per 8-wave block (the one launch of a pass that is not wide)
     if (n_new > 0) {
         std::vector<ChainSpec> chains;
         std::vector<TokRange> toks{{P0 + 1, n_new, true}};
@@ -1336,7 +1350,11 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
                     chains.push_back({lens[0], (b_last + 1 - p.fs[b_first] + 63) / 64});
                 }
         }
-        model_s = n_req == 1 && lens[0] == keys ? model_splits(chains, keys, toks, 4.0 * c.n_heads * hd) : 0;
+        if (n_req == 1 && lens[0] == keys) {
+            const SplitPlan sp = model_splits(chains, keys, toks, 4.0 * c.n_heads * hd, !wide_new);
+            model_s = sp.s;
+            halves = sp.halves;
+        }
     }
     auto split_keys = [&](int keys, bool causal, int &s, int &slen) {
         if (wide_new)  // two launches: each group of blocks on its own
@@ -1504,6 +1522,7 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
             a.nsc = d_nsc;
             a.par = d_par;
             a.chain = d_chain;
+            a.halves = halves;
             m->tbegin(last ? PCD_KC_OTHER : n_new > 0 ? PCD_KC_FUSED_ATTN : PCD_KC_BRANCH_ATTN, st);
             bool ok;
             if (wide_new && !last) {

@@ -107,6 +107,8 @@ struct AttnCall {
     const int32_t *fs, *nsc, *par;  // per branch token: field start, scaffold length, trie parent
     const int4 *chain;              // per branch token: 8 links of its trie chain (itself, parent, ...; -1 past the root)
     int32_t wide;  // nonzero: blocks of up to 128 query rows, causal prefix keys only (bf16); else up to 64 rows
+    int32_t halves;  // nonzero (64-row bf16 blocks): 8-wave blocks walking two key chains each, whatever the block
+                     // count (else only launches of at most 256 blocks)
 };
 bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
 

@@ -1883,7 +1883,8 @@ template <int HD, int S, int H, int RW = 1> static void launch_attn_ring_h(const
 }
 // Launches of at most one block per compute unit split each block's key
 // chain over two halves of one workgroup; larger ones keep 4-wave blocks,
-// two of which share a compute unit.
+// two of which share a compute unit, unless the host asks for two chains
+// (a launch bound by its longest chains).
 constexpr int ATT_HALVES_MAX_BLOCKS = 256;
 template <int HD, int S> static void launch_attn_ring(const AttnCall &c, hipStream_t st) {
     if constexpr (S == 2) {
@@ -1891,7 +1892,7 @@ template <int HD, int S> static void launch_attn_ring(const AttnCall &c, hipStre
             launch_attn_ring_h<HD, S, 1, 2>(c, st);
             return;
         }
-        if (c.n_blocks <= ATT_HALVES_MAX_BLOCKS) {
+        if (c.n_blocks <= ATT_HALVES_MAX_BLOCKS || c.halves) {
             launch_attn_ring_h<HD, S, 2>(c, st);
             return;
         }
