@@ -104,13 +104,12 @@ static int att_splits(int64_t row_blocks, int key_tiles, bool equal_chains) {
 // least estimated time: the larger of the longest chain and the total work
 // over the slots, each workgroup costing ATT_BLOCK_FIXED plus its key tiles.
 // 4-wave blocks take two slots per compute unit; 8-wave blocks walking two
-// key chains (the form launches of at most ATT_HALVES_BLOCKS take anyway)
+// key chains (the form launches of at most ATT_HALVES_MAX_BLOCKS take anyway)
 // one slot per compute unit, their chains halved.  Split keys add the merge kernel:
 // ATT_MERGE_FIXED plus its fp32 partials (each token's splits x query heads
 // x head_dim x 4 bytes) at ATT_MERGE_MB_PER_TILE.  Times are in key tiles
 // (about 1.2 us per 64-key tile of a 64-row block).
 constexpr int ATT_CHAIN_MODEL_TILES = 16;
-constexpr int ATT_HALVES_BLOCKS = 256;  // the kernel's two-chain form (launches of at most this many)
 constexpr double ATT_BLOCK_FIXED = 2.4;  // entry to first DMA, output write: about 2.8 us
 constexpr double ATT_MERGE_FIXED = 1.7;  // the merge kernel's launch and ramp: about 2 us
 constexpr double ATT_MERGE_MB_PER_TILE = 3.6;  // partials it reads per key-tile time (about 3 TB/s)
@@ -137,8 +136,8 @@ static SplitCost split_cost(const std::vector<ChainSpec> &blocks, int slen, int 
             sum_half += (t + 1) / 2;
             longest = std::max(longest, t);
         }
-    if (halves || n <= ATT_HALVES_BLOCKS)
-        return {ATT_BLOCK_FIXED + (longest + 1) / 2, (sum_half + ATT_BLOCK_FIXED * n) / ATT_HALVES_BLOCKS};
+    if (halves || n <= ATT_HALVES_MAX_BLOCKS)
+        return {ATT_BLOCK_FIXED + (longest + 1) / 2, (sum_half + ATT_BLOCK_FIXED * n) / ATT_HALVES_MAX_BLOCKS};
     return {ATT_BLOCK_FIXED + longest, (sum + ATT_BLOCK_FIXED * n) / ATT_SLOTS};
 }
 static double merge_cost(const std::vector<TokRange> &toks, int slen, int ns, double tok_bytes) {

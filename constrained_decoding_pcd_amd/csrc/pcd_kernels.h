@@ -112,6 +112,10 @@ struct AttnCall {
 };
 bool attention(const AttnCall &c, hipStream_t st);  // false: unsupported head_dim/dtype
 
+// 64-row bf16 launches of at most this many blocks take the two-chain form
+// (8-wave blocks, one per compute unit) without being asked.
+constexpr int ATT_HALVES_MAX_BLOCKS = 256;
+
 // Key splits of one attention row block at most (the merge kernel holds
 // every split of a (token, head) in registers).
 constexpr int ATT_MAX_SPLITS = 8;

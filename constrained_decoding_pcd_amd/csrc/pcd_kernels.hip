@@ -1885,7 +1885,6 @@ template <int HD, int S, int H, int RW = 1> static void launch_attn_ring_h(const
 // chain over two halves of one workgroup; larger ones keep 4-wave blocks,
 // two of which share a compute unit, unless the host asks for two chains
 // (a launch bound by its longest chains).
-constexpr int ATT_HALVES_MAX_BLOCKS = 256;
 template <int HD, int S> static void launch_attn_ring(const AttnCall &c, hipStream_t st) {
     if constexpr (S == 2) {
         if (c.wide) {
