@@ -160,7 +160,7 @@ static double merge_cost(const std::vector<TokRange> &toks, int slen, int ns, do
 // the two-chain form must gain 3%); s = 0 when the longest chain is below
 // ATT_CHAIN_MODEL_TILES.  toks: the row tokens and the keys they reach;
 // tok_bytes: one split's partials of one token; two_chains: the launch may
-// take the two-chain form (64-row blocks).
+// take the two-chain form (64-row bf16 blocks; the fp32 kernel has one form).
 struct SplitPlan {
     int s;
     bool halves;
@@ -832,7 +832,8 @@ int causal_pass(pcd_model *m, void *kv_buf, int32_t cap, int32_t P0, const int32
         for (int g = 0; g < c.n_kv_heads; ++g)
             for (int r0 = 0; r0 < rows; r0 += arows)
                 chains.push_back({P0 + (r0 + std::min(arows, rows - r0) - 1) / grp + 1, 0});
-        const SplitPlan sp = model_splits(chains, keys, {{P0 + 1, n, true}}, 4.0 * c.n_heads * hd, !wide);
+        const SplitPlan sp = model_splits(chains, keys, {{P0 + 1, n, true}}, 4.0 * c.n_heads * hd,
+                                           !wide && c.dtype == PCD_DTYPE_BF16);
         if (sp.s) ns = sp.s;
         halves = sp.halves;
     }
@@ -974,7 +975,8 @@ int causal_many(pcd_model *m, int n_seqs, void *const *bufs, const int32_t *caps
                 for (int r0 = t0[r] * grp; r0 < t0[r + 1] * grp; r0 += arows)
                     chains.push_back({(r0 + std::min(arows, t0[r + 1] * grp - r0) - 1) / grp - t0[r] + 1, 0});
         }
-        const SplitPlan sp = model_splits(chains, max_len, toks, 4.0 * c.n_heads * hd, !wide);
+        const SplitPlan sp = model_splits(chains, max_len, toks, 4.0 * c.n_heads * hd,
+                                           !wide && c.dtype == PCD_DTYPE_BF16);
         if (sp.s) ns = sp.s;
         halves = sp.halves;
     }
@@ -1350,7 +1352,8 @@ int decide_start(pcd_state *const *states, const pcd_request *reqs, int32_t n_re
                 }
         }
         if (n_req == 1 && lens[0] == keys) {
-            const SplitPlan sp = model_splits(chains, keys, toks, 4.0 * c.n_heads * hd, !wide_new);
+            const SplitPlan sp = model_splits(chains, keys, toks, 4.0 * c.n_heads * hd,
+                                               !wide_new && c.dtype == PCD_DTYPE_BF16);
             model_s = sp.s;
             halves = sp.halves;
         }
